@@ -1,0 +1,123 @@
+"""Pins of the oracle's Lloyd-Max codebooks and gain-shape quantizer: the
+closed-form 1-bit quantizer, J. Max's 1960 table, the optimality conditions
+checked by numerical integration, the Panter-Dite high-rate constant, and the
+float32 decision rule."""
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import integrate
+from scipy.stats import norm
+
+from oracle import codebook_f32, dequantize, gains_f32, lloyd_max, quantize
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden",
+                    "gaussian_quantizer_max1960.txt")
+
+
+def _max1960():
+    rows = {}
+    for line in open(GOLD):
+        if line.startswith("#") or not line.strip():
+            continue
+        b, thr, lev, mse = (f.strip() for f in line.split("|"))
+        rows[int(b)] = ([float(t) for t in thr.split()],
+                        [float(t) for t in lev.split()], float(mse))
+    return rows
+
+
+def test_one_bit_closed_form():
+    levels, thr, mse = lloyd_max(1)
+    assert abs(levels[1] - math.sqrt(2 / math.pi)) < 1e-15
+    assert levels[0] == -levels[1] and thr.tolist() == [0.0]
+    assert abs(mse - (1 - 2 / math.pi)) < 1e-14
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3])
+def test_matches_max_1960_table(bits):
+    thr_ref, lev_ref, mse_ref = _max1960()[bits]
+    levels, thr, mse = lloyd_max(bits)
+    m = 2 ** (bits - 1)
+    np.testing.assert_allclose(levels[m:], lev_ref, rtol=6e-4)
+    np.testing.assert_allclose(thr[m:], thr_ref, rtol=6e-4)
+    assert abs(mse / mse_ref - 1) < 6e-4
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+def test_optimality_conditions_by_quadrature(bits):
+    levels, thr, mse = lloyd_max(bits)
+    n = levels.size
+    assert np.all(np.diff(levels) > 0) and np.all(np.diff(thr) > 0)
+    np.testing.assert_array_equal(levels, -levels[::-1])
+    # thresholds are midpoints of adjacent levels
+    assert np.max(np.abs(thr - 0.5 * (levels[:-1] + levels[1:]))) < 1e-14
+    # levels are centroids; checked with scipy quadrature on a few cells
+    edges = np.concatenate([[-np.inf], thr, [np.inf]])
+    for j in sorted({n // 2, n // 2 + 1, n - 2, n - 1} & set(range(n))):
+        a, b = edges[j], edges[j + 1]
+        mass = norm.cdf(b) - norm.cdf(a) if a < 0 else norm.sf(a) - norm.sf(b)
+        first = integrate.quad(lambda x: x * norm.pdf(x), a, b, epsabs=1e-15,
+                               epsrel=1e-13)[0]
+        assert abs(first / mass - levels[j]) < 1e-9 * max(1.0, abs(levels[j]))
+    # distortion by quadrature of (x - q(x))^2 over the positive half
+    tot = 0.0
+    for j in range(n // 2, n):
+        a, b = edges[j], edges[j + 1]
+        tot += integrate.quad(lambda x: (x - levels[j]) ** 2 * norm.pdf(x), a, b,
+                              epsabs=1e-16, epsrel=1e-12, limit=200)[0]
+    assert abs(2 * tot / mse - 1) < 1e-8
+
+
+def test_high_rate_constant_panter_dite():
+    c = [lloyd_max(b)[2] * 4.0 ** b for b in range(1, 9)]
+    assert all(x < y for x, y in zip(c, c[1:]))
+    pd = math.pi * math.sqrt(3) / 2
+    assert c[-1] < pd and pd - c[-1] < 0.03
+
+
+def test_float32_codebook():
+    for b in range(1, 9):
+        lv, th = codebook_f32(b)
+        assert lv.dtype == np.float32 and th.dtype == np.float32
+        assert th[th.size // 2] == 0.0
+
+
+def test_quantize_decision_rule_float32():
+    # two-bit table: thresholds -t, 0, t; exactly-on-threshold goes up
+    _, th = codebook_f32(2)
+    t = float(th[2])
+    g = np.array([1.0], dtype=np.float32)
+    c = np.array([[-10.0, -t, -1e-30, 0.0, 1e-30,
+                   np.nextafter(np.float32(t), np.float32(0)), t, 10.0]])
+    codes = quantize(c, g, np.array([2]))
+    assert codes.tolist() == [[0, 1, 1, 2, 2, 2, 3, 3]]
+
+
+def test_quantize_symmetry_and_zero_gain():
+    rng = np.random.default_rng(3)
+    c = rng.standard_normal((6, 64)).astype(np.float32)
+    g = gains_f32(np.mean(c.astype(np.float64) ** 2, axis=1))
+    for b in range(1, 9):
+        bits = np.full(6, b)
+        q1 = quantize(c, g, bits).astype(np.int64)
+        q2 = quantize(-c, g, bits).astype(np.int64)
+        assert np.array_equal(q1 + q2, np.full_like(q1, 2 ** b - 1))
+    # gain 0: reconstructs to exactly zero
+    z = np.zeros((1, 64))
+    q = quantize(z, np.zeros(1, np.float32), np.array([3]))
+    assert np.all(dequantize(q, np.zeros(1, np.float32), np.array([3])) == 0.0)
+    # zero-bit bins: code 0, reconstruct 0
+    q = quantize(c, g, np.zeros(6, np.int64))
+    assert np.all(q == 0)
+    assert np.all(dequantize(q, g, np.zeros(6, np.int64)) == 0.0)
+
+
+def test_eight_bit_roundtrip_distortion():
+    rng = np.random.default_rng(4)
+    c = rng.standard_normal((64, 4096)) * 3.0
+    g = gains_f32(np.mean(c ** 2, axis=1))
+    bits = np.full(64, 8)
+    r = dequantize(quantize(c, g, bits), g, bits)
+    rel = np.mean((r - c) ** 2) / np.mean(c ** 2)
+    assert abs(rel / lloyd_max(8)[2] - 1) < 0.05
