@@ -1,0 +1,167 @@
+#!/usr/bin/env python3
+"""Throughput of the TACT-KV codec on one MI355X.
+
+A step is one pass of the whole codec over one launch's worth of synthetic
+KV cache resident in HBM: tact_compress over every unit of the workload,
+then tact_decompress of every record.  Printed as ONE JSON line:
+
+  value     GB/s of bf16 KV compressed and decompressed: input bytes of all
+            units divided by (compress + decompress) time
+  roofline  HBM roofline of the codec call that dominates the step:
+            algorithmic bytes per call (what the call must read and write:
+            2 B in / B/8 + 5/d out for compress, the reverse for
+            decompress, per entry) over its average duration, timed with
+            HIP events on the stream the library launches on
+  cpu_baseline  the plain CPU oracle timed on a bounded sample (layer 0,
+            sequence 0, K and V) of the same workload on the host cores
+
+    python bench.py [--steps K] [--warmup W] [--workload ct32b] [--budget 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ct32b",
+                    choices=["tiny", "ct4b", "ct7b", "ct32b", "video"])
+    ap.add_argument("--budget", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-units", type=int, default=2,
+                    help="units in the oracle's timed sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, budget, n_units):
+    """Time the oracle (as it stands) on a bounded sample of the workload."""
+    import numpy as np
+
+    import oracle as O
+    from tact_inputs import generate_unit
+    keys = [(0, 0, 0), (0, 0, 1), (1, 0, 0), (1, 0, 1)][:n_units]
+    keys = [k for k in keys if k[0] < wl.layers]
+    xs = [generate_unit(wl, *k).float().numpy().astype(np.float64) for k in keys]
+    p = O.Params(*wl.unit_shape, budget_bits=budget, max_bits=wl.max_bits)
+    od = "bf16" if wl.dtype == torch.bfloat16 else "f32"
+    t0 = time.perf_counter()
+    for x in xs:
+        O.decompress(O.compress(x, p), p, od)
+    dt = time.perf_counter() - t0
+    nbytes = len(xs) * wl.unit_entries * (2 if wl.dtype == torch.bfloat16 else 4)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = 1
+    return {
+        "value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(xs)} units (layer 0/1, sequence 0, K and V) of {wl.name}, "
+                  f"compress+decompress in {dt:.2f} s; host has "
+                  f"{len(os.sched_getaffinity(0))} usable cores, BLAS threads {threads}",
+    }
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the codec is "
+              "per layer, per sequence and needs no exchange between GPUs; run one process "
+              "per GPU on its own share of the units.", file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import kv_cache_compression_tact_amd as tact
+    from tact_inputs import WORKLOADS, generate_units
+
+    wl = WORKLOADS[args.workload]
+    budget = args.budget if args.budget is not None else wl.budgets[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {wl.name}: {wl.n_units} units of {wl.unit_shape} "
+          f"{wl.dtype}", file=sys.stderr, flush=True)
+    x = generate_units(wl, device=dev)
+    g = tact.Geometry(*wl.unit_shape, budget_bits=budget, max_bits=wl.max_bits,
+                      dtype=wl.dtype)
+    U = wl.n_units
+    rec = torch.empty((U, g.record_bytes()), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x)
+    ws = tact.workspace(g, U, dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+          for _ in range(args.steps)]
+
+    def step(e=None):
+        if e is not None:
+            e[0].record(stream)
+        tact.compress(x, budget, wl.max_bits, records=rec, ws=ws)
+        if e is not None:
+            e[1].record(stream)
+        tact.decompress(rec, g, out=out, ws=ws)
+        if e is not None:
+            e[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    t_c = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    t_d = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    med = lambda v: v[len(v) // 2]
+    ms_c, ms_d = sum(t_c) / len(t_c), sum(t_d) / len(t_d)
+    es = 2 if wl.dtype == torch.bfloat16 else 4
+    in_bytes = U * wl.unit_entries * es
+    d = wl.head_dim
+    # algorithmic bytes per entry: compress reads the cache and writes the
+    # codes and side info; decompress reads those and writes the cache
+    side = (budget / 8.0 + 5.0 / d)
+    alg_c = U * wl.unit_entries * (es + side)
+    alg_d = U * wl.unit_entries * (side + es)
+    ms_step = elapsed * 1e3 / args.steps
+    value = in_bytes / (elapsed / args.steps) / 1e9
+    dom, alg, ms = ("tact_compress", alg_c, ms_c) if ms_c >= ms_d else \
+        ("tact_decompress", alg_d, ms_d)
+    achieved = alg / (ms * 1e-3) / 1e9
+    roofline_step = (alg_c + alg_d) / ((ms_c + ms_d) * 1e-3) / 1e9
+    line = {
+        "metric": "KV codec GB/s (compress+decompress, bf16 in) and % of HBM roofline at 1 GPU",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "units": U, "unit_shape": list(wl.unit_shape),
+                   "cache_dtype": str(wl.dtype).replace("torch.", ""),
+                   "budget_bits": budget, "max_bits": wl.max_bits,
+                   "input_bytes": in_bytes},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "step_frac": round(roofline_step / HBM_PEAK_GBS, 4)},
+        "ms_compress": round(ms_c, 4), "ms_decompress": round(ms_d, 4),
+        "ms_compress_median": round(med(t_c), 4), "ms_decompress_median": round(med(t_d), 4),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl, budget, args.cpu_units)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

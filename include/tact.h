@@ -1,0 +1,147 @@
+/*
+ * tact.h -- C ABI of the TACT-KV visual-KV-cache codec for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The codec follows the AI-summary page "TACT-KV: Tri-Axis Cosine Transform
+ * for Compressing Volumetric KV Caches in Medical VLMs", section
+ * "Methodology in Plain English" (stages 1-4 and the decoding paragraph).
+ * Per unit -- one layer, one sequence, the K or the V tensor -- it:
+ *   1. views the visual span of the cache as an (S, H, W, kv_heads, head_dim)
+ *      volume on the vision encoder's grid                       (stage 1);
+ *   2. applies a separable orthonormal DCT-II along S, H and W   (stage 2);
+ *   3. estimates each frequency bin's variance from the unit itself and
+ *      splits the unit's bit budget over the bins by reverse water-filling,
+ *      capped at max_bits per bin, hitting the budget exactly   (stage 3);
+ *   4. quantizes each bin with a gain (its RMS, stored as fp32) and a fixed
+ *      Gaussian Lloyd-Max codebook at the bin's bit width        (stage 4);
+ * and decoding reverses the steps (dequantize, inverse DCT, round).
+ *
+ * Definitions used throughout:
+ *   bin      one (ks, kh, kw, head) frequency of one head; flat bin index
+ *            ((ks*H + kh)*W + kw)*kv_heads + head.  n_bins = S*H*W*kv_heads.
+ *   variance (1/head_dim) * sum_j c_j^2 over the bin's head_dim coefficients.
+ *   budget   T = budget_bits * n_bins bit-planes per unit; bin i gets b_i
+ *            planes with sum_i b_i = T and 0 <= b_i <= max_bits.  The b_i are
+ *            the T largest marginal gains var_i * 4^-(k-1) (1 <= k <= max_bits)
+ *            ordered by (gain desc, bin asc, k asc) -- the result of
+ *            bisection for the water level plus the +-1 greedy correction.
+ *   code     u = fl32(c * fl32(1/g)) with g = fl32(sqrt(variance)) (u = 0 when
+ *            g == 0); code = number of fp32 Lloyd-Max thresholds <= u.
+ *
+ * Memory.  All buffer arguments are DEVICE pointers owned by the caller; the
+ * library never allocates, frees or synchronizes.  Work is enqueued on the
+ * given HIP stream and runs asynchronously; the return value reports only
+ * argument validation and launch errors.  Arguments are validated before any
+ * HIP call: an invalid call launches nothing.  Buffers must not overlap
+ * unless stated.  Inputs must be finite.
+ *
+ * Unit tensor layout: row-major (S, H, W, kv_heads, head_dim), element type
+ * given by tact_params.dtype; consecutive units are unit_stride elements
+ * apart (unit_stride >= S*H*W*kv_heads*head_dim, a multiple of 8).  Tensor
+ * pointers must be 16-byte aligned; records and workspace 256-byte aligned.
+ *
+ * Record layout (one per unit, tact_record_bytes() bytes, regions 256-byte
+ * aligned, in this order):
+ *   gains  float32[n_bins]               per-bin gain g
+ *   bits   uint8[n_bins]                 b_i
+ *   groups uint32[ceil(n_bins/64)]       sum_{k < 64*g} b_k (first plane of
+ *                                        every 64th bin)
+ *   codes  uint64[T*head_dim/64]         bin i's plane q (q = 0 is the least
+ *                                        significant code bit) starts at bit
+ *                                        (sum_{k<i} b_k + q) * head_dim; bit j
+ *                                        of a plane is bit q of code_j.
+ * The record is position independent: it can be copied or stored as is.
+ */
+#ifndef TACT_H_
+#define TACT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TACT_OK = 0,
+  TACT_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad alignment  */
+  TACT_ERR_UNSUPPORTED = 2,      /* valid C call, geometry not supported   */
+  TACT_ERR_WORKSPACE = 3,        /* workspace missing or too small         */
+  TACT_ERR_HIP = 4               /* the HIP runtime reported an error      */
+} tact_status;
+
+typedef enum { TACT_BF16 = 0, TACT_F32 = 1 } tact_dtype;
+
+/* Transform axes (bit mask); the method transforms all three.  Subsets are
+ * the transform ablation of the page's "Main Findings". */
+enum { TACT_AXIS_S = 1, TACT_AXIS_H = 2, TACT_AXIS_W = 4, TACT_AXES_ALL = 7 };
+
+/* Allocation mode: 0 = reverse water-filling (the method); 1 = uniform, every
+ * bin budget_bits planes (the page's "uniform allocation" ablation). */
+enum { TACT_ALLOC_WATERFILL = 0, TACT_ALLOC_UNIFORM = 1 };
+
+typedef struct {
+  int32_t S, H, W;      /* grid of the vision encoder, each 1..64            */
+  int32_t kv_heads;     /* 1..64                                             */
+  int32_t head_dim;     /* 64, 128 or 256                                    */
+  int32_t budget_bits;  /* average code bits per entry, 0..max_bits          */
+  int32_t max_bits;     /* per-bin cap, 1..8 (the page caps at 8)            */
+  int32_t dtype;        /* tact_dtype of the cache tensors (in == out)       */
+  int32_t axes;         /* TACT_AXES_ALL, or a non-empty subset              */
+  int32_t alloc_mode;   /* TACT_ALLOC_WATERFILL or TACT_ALLOC_UNIFORM        */
+} tact_params;
+
+/* Fills *p with the method's defaults for the given geometry and budget
+ * (dtype bf16, all axes, water-filling, cap 8). */
+void tact_params_init(tact_params* p, int32_t S, int32_t H, int32_t W,
+                      int32_t kv_heads, int32_t head_dim, int32_t budget_bits);
+
+/* Bytes of one unit's record; 0 if *p is invalid (see tact_last_error). */
+size_t tact_record_bytes(const tact_params* p);
+
+/* Workspace bytes that tact_compress / tact_decompress / tact_roundtrip need
+ * for a call over n_units units (a larger workspace is accepted); 0 if *p is
+ * invalid.  The stage entry points of tact_debug.h need none unless stated. */
+size_t tact_workspace_bytes(const tact_params* p, int64_t n_units);
+
+/* Compress n_units units: kv (device, unit_stride elements apart) ->
+ * records (device, n_units * tact_record_bytes(p) bytes, one after another).
+ * Stages 1-4 of the method.  n_units == 0 is a no-op. */
+tact_status tact_compress(const tact_params* p, int64_t n_units,
+                          const void* kv, int64_t kv_unit_stride,
+                          void* records, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* Decompress n_units records into kv_out (same layout rules as kv):
+ * unpack, dequantize, inverse DCT, round to bf16 (nearest even) or fp32. */
+tact_status tact_decompress(const tact_params* p, int64_t n_units,
+                            const void* records, void* kv_out,
+                            int64_t out_unit_stride, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* tact_compress followed by tact_decompress.  records may be NULL, in which
+ * case the records are kept in the workspace (tact_workspace_bytes then
+ * includes them).  kv_out may equal kv (in place). */
+tact_status tact_roundtrip(const tact_params* p, int64_t n_units,
+                           const void* kv, int64_t kv_unit_stride,
+                           void* kv_out, int64_t out_unit_stride,
+                           void* records, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* tact_status_string(tact_status s);
+
+/* Detail of the last failed call on this thread ("" if none). */
+const char* tact_last_error(void);
+
+/* Host-side copy of the library's fp32 Lloyd-Max table at `bits` (1..8):
+ * 2^bits levels and 2^bits - 1 thresholds, ascending.  Either pointer may be
+ * NULL.  Returns the number of levels, or 0 for an invalid bit width. */
+int32_t tact_codebook(int32_t bits, float* levels, float* thresholds);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TACT_H_ */

@@ -1,0 +1,296 @@
+"""Python binding of the TACT-KV codec library (libtact.so, gfx950).
+
+Argument marshalling only: every step of the codec runs in the library's
+HIP kernels.  PyTorch provides device memory and the current stream.  The
+functions take and return torch tensors on the GPU:
+
+    records = compress(kv, budget_bits)            # kv: (U, S, H, W, Hkv, d)
+    kv_hat  = decompress(records, geometry...)     # bf16 / fp32 like kv
+    kv_hat, records = roundtrip(kv, budget_bits)
+
+The library is loaded from this package's directory; importing this module
+without it raises ImportError (build it with
+``python -m kv_cache_compression_tact_amd.build``).  There is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtact.so")
+
+TACT_OK, TACT_ERR_INVALID_ARGUMENT, TACT_ERR_UNSUPPORTED, TACT_ERR_WORKSPACE, \
+    TACT_ERR_HIP = range(5)
+TACT_BF16, TACT_F32 = 0, 1
+AXIS_S, AXIS_H, AXIS_W, AXES_ALL = 1, 2, 4, 7
+ALLOC_WATERFILL, ALLOC_UNIFORM = 0, 1
+
+
+class TactParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("S", "H", "W", "kv_heads", "head_dim", "budget_bits", "max_bits",
+                 "dtype", "axes", "alloc_mode")]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m kv_cache_compression_tact_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(TactParams)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    sigs = {
+        "tact_params_init": (None, [P, i32, i32, i32, i32, i32, i32]),
+        "tact_record_bytes": (sz, [P]),
+        "tact_workspace_bytes": (sz, [P, i64]),
+        "tact_compress": (i32, [P, i64, vp, i64, vp, vp, sz, vp]),
+        "tact_decompress": (i32, [P, i64, vp, vp, i64, vp, sz, vp]),
+        "tact_roundtrip": (i32, [P, i64, vp, i64, vp, i64, vp, vp, sz, vp]),
+        "tact_status_string": (ctypes.c_char_p, [i32]),
+        "tact_last_error": (ctypes.c_char_p, []),
+        "tact_codebook": (i32, [i32, vp, vp]),
+        "tact_dbg_workspace_bytes": (sz, [P, i64]),
+        "tact_dbg_dct3": (i32, [P, i64, i32, vp, vp, vp, sz, vp]),
+        "tact_dbg_bin_variance": (i32, [P, i64, vp, vp, vp]),
+        "tact_dbg_allocate": (i32, [P, i64, vp, vp, vp]),
+        "tact_dbg_quantize": (i32, [P, i64, vp, vp, vp, vp, vp]),
+        "tact_dbg_unpack": (i32, [P, i64, vp, vp, vp]),
+        "tact_dbg_dequantize": (i32, [P, i64, vp, vp, vp]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("tact_params_init", "tact_record_bytes", "tact_workspace_bytes",
+            "tact_compress", "tact_decompress", "tact_roundtrip",
+            "tact_status_string", "tact_last_error", "tact_codebook",
+            "tact_dbg_workspace_bytes", "tact_dbg_dct3", "tact_dbg_bin_variance",
+            "tact_dbg_allocate", "tact_dbg_quantize", "tact_dbg_unpack",
+            "tact_dbg_dequantize")
+
+
+def lib():
+    """The loaded ctypes library (for tests of the raw C ABI)."""
+    return _lib
+
+
+class TactError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.tact_last_error().decode()
+        name = _lib.tact_status_string(status).decode()
+        super().__init__(f"{where}: {name} ({status}): {msg}")
+
+
+def _check(status: int, where: str):
+    if status != TACT_OK:
+        raise TactError(status, where)
+
+
+@dataclass(frozen=True)
+class Geometry:
+    S: int
+    H: int
+    W: int
+    kv_heads: int
+    head_dim: int
+    budget_bits: int
+    max_bits: int = 8
+    dtype: torch.dtype = torch.bfloat16
+    axes: int = AXES_ALL
+    alloc_mode: int = ALLOC_WATERFILL
+
+    def params(self) -> TactParams:
+        if self.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("cache dtype must be bfloat16 or float32")
+        return TactParams(self.S, self.H, self.W, self.kv_heads, self.head_dim,
+                          self.budget_bits, self.max_bits,
+                          TACT_BF16 if self.dtype == torch.bfloat16 else TACT_F32,
+                          self.axes, self.alloc_mode)
+
+    @property
+    def unit_shape(self):
+        return (self.S, self.H, self.W, self.kv_heads, self.head_dim)
+
+    @property
+    def n_bins(self) -> int:
+        return self.S * self.H * self.W * self.kv_heads
+
+    @property
+    def n_entries(self) -> int:
+        return self.n_bins * self.head_dim
+
+    def record_bytes(self) -> int:
+        p = self.params()
+        n = _lib.tact_record_bytes(ctypes.byref(p))
+        if n == 0:
+            raise TactError(TACT_ERR_INVALID_ARGUMENT, "tact_record_bytes")
+        return n
+
+    def workspace_bytes(self, n_units: int) -> int:
+        p = self.params()
+        return _lib.tact_workspace_bytes(ctypes.byref(p), n_units)
+
+    @staticmethod
+    def of(kv: torch.Tensor, budget_bits: int, **kw) -> "Geometry":
+        if kv.dim() != 6:
+            raise ValueError("kv must be (units, S, H, W, kv_heads, head_dim)")
+        _, S, H, W, hk, d = kv.shape
+        return Geometry(S, H, W, hk, d, budget_bits, dtype=kv.dtype, **kw)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _unit_stride(t: torch.Tensor) -> int:
+    """Elements between consecutive units; each unit must be contiguous."""
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if t.dim() != 6:
+        raise ValueError("expected a (units, S, H, W, kv_heads, head_dim) tensor")
+    unit = 1
+    for n in t.shape[1:]:
+        unit *= n
+    if t.shape[0] == 0:
+        return unit
+    if not t[0].is_contiguous():
+        raise ValueError("each unit must be a contiguous (S, H, W, kv_heads, head_dim) tensor")
+    return t.stride(0) if t.shape[0] > 1 else unit
+
+
+def workspace(geom: Geometry, n_units: int, device=None) -> torch.Tensor:
+    n = geom.workspace_bytes(n_units)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device or "cuda")
+
+
+def compress(kv: torch.Tensor, budget_bits: int, max_bits: int = 8, *,
+             records: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+             axes: int = AXES_ALL, alloc_mode: int = ALLOC_WATERFILL) -> torch.Tensor:
+    """kv (U, S, H, W, Hkv, d) bf16/fp32 on the GPU -> records uint8 (U, record_bytes)."""
+    g = Geometry.of(kv, budget_bits, max_bits=max_bits, axes=axes, alloc_mode=alloc_mode)
+    U = kv.shape[0]
+    if records is None:
+        records = torch.empty((U, g.record_bytes()), dtype=torch.uint8, device=kv.device)
+    if ws is None:
+        ws = workspace(g, U, kv.device)
+    p = g.params()
+    _check(_lib.tact_compress(ctypes.byref(p), U, _ptr(kv), _unit_stride(kv),
+                              _ptr(records), _ptr(ws), ws.numel(), _stream()),
+           "tact_compress")
+    return records
+
+
+def decompress(records: torch.Tensor, geom: Geometry, *, out: torch.Tensor | None = None,
+               ws: torch.Tensor | None = None) -> torch.Tensor:
+    """records uint8 (U, record_bytes) -> cache (U, S, H, W, Hkv, d) of geom.dtype."""
+    U = records.shape[0]
+    if out is None:
+        out = torch.empty((U,) + geom.unit_shape, dtype=geom.dtype, device=records.device)
+    if ws is None:
+        ws = workspace(geom, U, records.device)
+    p = geom.params()
+    _check(_lib.tact_decompress(ctypes.byref(p), U, _ptr(records), _ptr(out),
+                                _unit_stride(out), _ptr(ws), ws.numel(), _stream()),
+           "tact_decompress")
+    return out
+
+
+def roundtrip(kv: torch.Tensor, budget_bits: int, max_bits: int = 8, *,
+              out: torch.Tensor | None = None, records: torch.Tensor | None = None,
+              ws: torch.Tensor | None = None, keep_records: bool = True,
+              axes: int = AXES_ALL, alloc_mode: int = ALLOC_WATERFILL):
+    """Compress then decompress; returns (kv_hat, records or None)."""
+    g = Geometry.of(kv, budget_bits, max_bits=max_bits, axes=axes, alloc_mode=alloc_mode)
+    U = kv.shape[0]
+    if out is None:
+        out = torch.empty_like(kv)
+    if records is None and keep_records:
+        records = torch.empty((U, g.record_bytes()), dtype=torch.uint8, device=kv.device)
+    if ws is None:
+        ws = workspace(g, U, kv.device)
+    p = g.params()
+    _check(_lib.tact_roundtrip(ctypes.byref(p), U, _ptr(kv), _unit_stride(kv), _ptr(out),
+                               _unit_stride(out), _ptr(records), _ptr(ws), ws.numel(),
+                               _stream()), "tact_roundtrip")
+    return out, records
+
+
+def codebook(bits: int):
+    """The library's fp32 Lloyd-Max table (levels, thresholds) as CPU tensors."""
+    n = 1 << bits
+    lv = torch.empty(n, dtype=torch.float32)
+    th = torch.empty(n - 1, dtype=torch.float32)
+    got = _lib.tact_codebook(bits, _ptr(lv), _ptr(th))
+    if got != n:
+        raise ValueError("bits must be in 1..8")
+    return lv, th
+
+
+# ---- stage entry points ----------------------------------------------------
+def dbg_dct3(x: torch.Tensor, geom: Geometry, inverse: bool = False) -> torch.Tensor:
+    U = x.shape[0]
+    out = torch.empty((U,) + geom.unit_shape, dtype=torch.float32, device=x.device)
+    p = geom.params()
+    _check(_lib.tact_dbg_dct3(ctypes.byref(p), U, 1 if inverse else 0, _ptr(x), _ptr(out),
+                              None, 0, _stream()), "tact_dbg_dct3")
+    return out
+
+
+def dbg_bin_variance(coef: torch.Tensor, geom: Geometry) -> torch.Tensor:
+    U = coef.shape[0]
+    var = torch.empty((U,) + geom.unit_shape[:-1], dtype=torch.float32, device=coef.device)
+    p = geom.params()
+    _check(_lib.tact_dbg_bin_variance(ctypes.byref(p), U, _ptr(coef), _ptr(var), _stream()),
+           "tact_dbg_bin_variance")
+    return var
+
+
+def dbg_allocate(var: torch.Tensor, geom: Geometry) -> torch.Tensor:
+    U = var.shape[0]
+    bits = torch.empty((U,) + geom.unit_shape[:-1], dtype=torch.uint8, device=var.device)
+    p = geom.params()
+    _check(_lib.tact_dbg_allocate(ctypes.byref(p), U, _ptr(var.contiguous()), _ptr(bits),
+                                  _stream()), "tact_dbg_allocate")
+    return bits
+
+
+def dbg_quantize(coef: torch.Tensor, gains: torch.Tensor, bits: torch.Tensor,
+                 geom: Geometry) -> torch.Tensor:
+    U = coef.shape[0]
+    rec = torch.empty((U, geom.record_bytes()), dtype=torch.uint8, device=coef.device)
+    p = geom.params()
+    _check(_lib.tact_dbg_quantize(ctypes.byref(p), U, _ptr(coef.contiguous()),
+                                  _ptr(gains.contiguous()), _ptr(bits.contiguous()),
+                                  _ptr(rec), _stream()), "tact_dbg_quantize")
+    return rec
+
+
+def dbg_unpack(records: torch.Tensor, geom: Geometry) -> torch.Tensor:
+    U = records.shape[0]
+    codes = torch.empty((U,) + geom.unit_shape, dtype=torch.uint8, device=records.device)
+    p = geom.params()
+    _check(_lib.tact_dbg_unpack(ctypes.byref(p), U, _ptr(records), _ptr(codes), _stream()),
+           "tact_dbg_unpack")
+    return codes
+
+
+def dbg_dequantize(records: torch.Tensor, geom: Geometry) -> torch.Tensor:
+    U = records.shape[0]
+    coef = torch.empty((U,) + geom.unit_shape, dtype=torch.float32, device=records.device)
+    p = geom.params()
+    _check(_lib.tact_dbg_dequantize(ctypes.byref(p), U, _ptr(records), _ptr(coef),
+                                    _stream()), "tact_dbg_dequantize")
+    return coef

@@ -1,0 +1,79 @@
+// Internal interface between the C-ABI host layer (tact_api.cpp) and the
+// gfx950 kernels (tact_kernels.hip).  Not installed, not part of the ABI.
+#ifndef TACT_INTERNAL_H_
+#define TACT_INTERNAL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#include "tact.h"
+
+namespace tact {
+
+// Geometry of one unit and of its record, derived from validated params.
+struct Geometry {
+  int S, H, W, kv_heads, head_dim;
+  int max_bits, budget_bits, axes, alloc_mode;
+  int dtype;
+  int64_t n_bins;        // S*H*W*kv_heads
+  int64_t n_entries;     // n_bins * head_dim
+  int64_t total_bits;    // T = budget_bits * n_bins (bit-planes)
+  int64_t n_groups;      // ceil(n_bins / 64)
+  // record layout (bytes from the record start)
+  int64_t off_gains, off_bits, off_groups, off_codes, code_bytes, record_bytes;
+};
+
+// Locations of the record regions for a batch of units.
+struct RecordView {
+  uint8_t* base;         // record of unit 0
+  int64_t stride;        // bytes between records
+  int64_t off_gains, off_bits, off_groups, off_codes;
+};
+
+inline int64_t align256(int64_t n) { return (n + 255) / 256 * 256; }
+
+// ---- launchers (tact_kernels.hip); all asynchronous on `stream` -----------
+
+// Separable DCT-II (inverse: DCT-III) along the axes in `axes`, over
+// `n_units` unit tensors.  in: element type in_dtype, unit stride in_stride
+// (elements).  out: element type out_dtype, unit stride out_stride.  Passes
+// after the first run in place in `out`, so `out` must be able to hold fp32
+// intermediates unless exactly one axis is transformed; when out_dtype is
+// not fp32 and more than one axis is transformed, `scratch` (fp32, n_units
+// * n_entries) holds the intermediates.
+void launch_dct3(const Geometry& g, int64_t n_units, int inverse,
+                 const void* in, int in_dtype, int64_t in_stride,
+                 void* out, int out_dtype, int64_t out_stride,
+                 float* scratch, hipStream_t stream);
+
+// var[u*n_bins + i] = mean_j coef[(u*n_bins + i)*d + j]^2.
+void launch_bin_variance(const Geometry& g, int64_t n_units, const float* coef,
+                         float* var, hipStream_t stream);
+
+// Bit allocation of every unit from its variances; writes the bits into
+// `bits_out` (stride n_bins per unit) if non-null, and the record header
+// (gains, bits, group index, zeroed padding) into `rec` if rec.base != null.
+void launch_allocate(const Geometry& g, int64_t n_units, const float* var,
+                     uint8_t* bits_out, RecordView rec, hipStream_t stream);
+
+// Record header (gains, bits, group index, padding) from caller's gains/bits.
+void launch_header(const Geometry& g, int64_t n_units, const float* gains,
+                   const uint8_t* bits, RecordView rec, hipStream_t stream);
+
+// Quantize + bit-plane pack: reads coef and the record header, writes codes.
+void launch_quantize(const Geometry& g, int64_t n_units, const float* coef,
+                     RecordView rec, hipStream_t stream);
+
+// Unpack (+ dequantize): codes_out (uint8 per coefficient) and/or coef_out
+// (fp32 g * level) from records; either may be null.
+void launch_unpack(const Geometry& g, int64_t n_units, RecordView rec,
+                   uint8_t* codes_out, float* coef_out, hipStream_t stream);
+
+// Host copy of the fp32 codebooks.
+extern const float kHostLevels[];
+extern const float kHostThresholds[];
+
+}  // namespace tact
+
+#endif  // TACT_INTERNAL_H_

@@ -493,10 +493,11 @@ def pack_record(codes: np.ndarray, gains: np.ndarray, bits: np.ndarray,
     rec[lay["groups"]:lay["groups"] + 4 * lay["n_groups"]] = grp.view(np.uint8)
     c = np.asarray(codes).reshape(p.n_bins, d).astype(np.int64)
     bitstream = np.zeros(lay["code_bytes"] * 8, dtype=np.uint8)
-    for i in range(p.n_bins):
-        for q in range(b[i]):
-            base = (start[i] + q) * d
-            bitstream[base:base + d] = (c[i] >> q) & 1
+    j = np.arange(d, dtype=np.int64)
+    for q in range(int(b.max(initial=0))):
+        sel = np.nonzero(b > q)[0]                     # bins that own plane q
+        pos = ((start[sel] + q) * d)[:, None] + j[None, :]
+        bitstream[pos] = ((c[sel] >> q) & 1).astype(np.uint8)
     # bit n of the stream is bit (n mod 8) of byte n // 8 (little-endian words)
     packed = np.packbits(bitstream, bitorder="little")
     rec[lay["codes"]:lay["codes"] + lay["code_bytes"]] = packed
@@ -514,10 +515,11 @@ def unpack_record(rec: np.ndarray, p: Params):
     stream = np.unpackbits(rec[lay["codes"]:lay["codes"] + lay["code_bytes"]],
                            bitorder="little").astype(np.int64)
     codes = np.zeros((p.n_bins, d), dtype=np.int64)
-    for i in range(p.n_bins):
-        for q in range(b[i]):
-            base = (start[i] + q) * d
-            codes[i] |= stream[base:base + d] << q
+    j = np.arange(d, dtype=np.int64)
+    for q in range(int(b.max(initial=0))):
+        sel = np.nonzero(b > q)[0]
+        pos = ((start[sel] + q) * d)[:, None] + j[None, :]
+        codes[sel] |= stream[pos] << q
     shp = p.shape
     return (codes.astype(np.uint8).reshape(shp), gains.reshape(shp[:-1]),
             b.reshape(shp[:-1]))

@@ -1,0 +1,128 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/*.h declares, and rejects invalid calls before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import kv_cache_compression_tact_amd as tact
+from kv_cache_compression_tact_amd import TactParams, lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for h in ("tact.h", "tact_debug.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(tact_[a-z0-9_]+)\s*\(", src))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert {"tact_compress", "tact_decompress", "tact_roundtrip"} <= names
+    for n in sorted(names):
+        assert hasattr(lib(), n), n
+    assert names == set(tact.EXPORTED)
+
+
+def _params(**kw):
+    p = TactParams()
+    lib().tact_params_init(ctypes.byref(p), 4, 8, 8, 2, 64, 1)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_params_init_defaults():
+    p = _params()
+    assert (p.max_bits, p.dtype, p.axes, p.alloc_mode) == (8, 0, 7, 0)
+
+
+def test_record_bytes_matches_layout():
+    p = _params(max_bits=3, dtype=1)
+    # 512 bins: gains 2048, bits 512, groups 8*4 -> 256, codes 512*64/8 = 4096
+    assert lib().tact_record_bytes(ctypes.byref(p)) == 2048 + 512 + 256 + 4096
+    from oracle import Params, record_layout
+    for geo in [(64, 24, 24, 8, 128, 1), (32, 16, 16, 4, 256, 4), (3, 5, 7, 1, 64, 2)]:
+        q = _params(S=geo[0], H=geo[1], W=geo[2], kv_heads=geo[3], head_dim=geo[4],
+                    budget_bits=geo[5])
+        assert lib().tact_record_bytes(ctypes.byref(q)) == \
+            record_layout(Params(*geo, max_bits=8))["size"]
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("S", 0, 2), ("H", 65, 2), ("W", -1, 2), ("kv_heads", 0, 2), ("head_dim", 96, 2),
+    ("max_bits", 0, 1), ("max_bits", 9, 1), ("budget_bits", 9, 1), ("budget_bits", -1, 1),
+    ("dtype", 5, 1), ("axes", 0, 1), ("axes", 8, 1), ("alloc_mode", 2, 1),
+])
+def test_invalid_params_rejected(field, value, status):
+    p = _params(**{field: value})
+    assert lib().tact_record_bytes(ctypes.byref(p)) == 0
+    assert lib().tact_workspace_bytes(ctypes.byref(p), 4) == 0
+    fake = ctypes.c_void_p(1 << 20)
+    st = lib().tact_compress(ctypes.byref(p), 1, fake, 32768, fake, fake, 1 << 30, None)
+    assert st == status
+    assert len(lib().tact_last_error()) > 0
+
+
+def test_null_and_misaligned_pointers_rejected():
+    p = _params()
+    ws = lib().tact_workspace_bytes(ctypes.byref(p), 2)
+    assert ws > 0
+    fake = ctypes.c_void_p(1 << 20)
+    L = lib()
+    assert L.tact_compress(ctypes.byref(p), 2, None, 32768, fake, fake, ws, None) == 1
+    assert L.tact_compress(ctypes.byref(p), 2, ctypes.c_void_p((1 << 20) + 2), 32768, fake,
+                           fake, ws, None) == 1
+    assert L.tact_compress(ctypes.byref(p), 2, fake, 32768, None, fake, ws, None) == 1
+    assert L.tact_compress(ctypes.byref(p), 2, fake, 32768, ctypes.c_void_p((1 << 20) + 16),
+                           fake, ws, None) == 1
+    # unit stride below the unit size or not a multiple of 8
+    assert L.tact_compress(ctypes.byref(p), 2, fake, 32767, fake, fake, ws, None) == 1
+    assert L.tact_compress(ctypes.byref(p), 2, fake, 32772, fake, fake, ws, None) == 1
+    # workspace missing / too small
+    assert L.tact_compress(ctypes.byref(p), 2, fake, 32768, fake, None, ws, None) == 3
+    assert L.tact_compress(ctypes.byref(p), 2, fake, 32768, fake, fake, ws - 1, None) == 3
+    assert L.tact_decompress(ctypes.byref(p), 2, fake, fake, 32768, fake, ws - 1, None) == 3
+    assert L.tact_compress(ctypes.byref(p), -1, fake, 32768, fake, fake, ws, None) == 1
+    # overlapping but distinct in/out for the round trip
+    assert L.tact_roundtrip(ctypes.byref(p), 2, fake, 32768,
+                            ctypes.c_void_p((1 << 20) + 4096), 32768, None, fake, ws,
+                            None) == 1
+    assert L.tact_compress(None, 2, fake, 32768, fake, fake, ws, None) == 1
+
+
+def test_zero_units_is_a_noop():
+    p = _params()
+    assert lib().tact_compress(ctypes.byref(p), 0, None, 0, None, None, 0, None) == 0
+    assert lib().tact_decompress(ctypes.byref(p), 0, None, None, 0, None, 0, None) == 0
+
+
+def test_status_strings():
+    for s in range(5):
+        assert len(lib().tact_status_string(s)) > 0
+
+
+def test_library_codebook_equals_oracle_table():
+    from oracle import codebook_f32
+    for b in range(1, 9):
+        lv, th = tact.codebook(b)
+        olv, oth = codebook_f32(b)
+        assert torch.equal(lv, torch.from_numpy(olv)) and torch.equal(th, torch.from_numpy(oth))
+    assert lib().tact_codebook(0, None, None) == 0
+    assert lib().tact_codebook(9, None, None) == 0
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful without a GPU")
+def test_valid_call_without_device_reports_hip_error():
+    p = _params()
+    ws = lib().tact_workspace_bytes(ctypes.byref(p), 1)
+    fake = ctypes.c_void_p(1 << 20)
+    st = lib().tact_compress(ctypes.byref(p), 1, fake, 32768, fake, fake, ws, None)
+    assert st == 4
+    assert b"tact_compress" in lib().tact_last_error()

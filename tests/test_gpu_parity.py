@@ -1,0 +1,333 @@
+"""Parity of the HIP path with the CPU oracle, step by step and end to end.
+
+Every test calls the library through its C ABI (the ctypes binding) on
+seeded synthetic inputs and compares with the oracle on the same inputs:
+  * DCT coefficients:       ||c_gpu - c_ref|| / ||c_ref|| <= 1e-5 per unit
+  * variances:              <= 1e-6 relative per bin (fp32 sum of squares)
+  * bits:                   bit-exact given identical variances
+  * codes / records:        byte-exact given identical coefficients, gains
+                            and bits (both sides decide in fp32)
+  * unpack:                 byte-exact; dequantize within 1 fp32 rounding
+  * decompress:             bf16 outputs equal except 1-ulp differences on
+                            <= 0.1% of entries (rounding of a ~1e-6 error)
+  * end to end:             bits equal except at the cut, codes >= 99.99%
+                            equal with mismatches next to a threshold, and
+                            round-trip MSE within 1e-3 relative.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from tact_inputs import WORKLOADS, generate_unit, generate_units
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.device_count() > 0:
+    import kv_cache_compression_tact_amd as tact
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _geom(S, H, W, hk, d, budget, bmax=8, dtype=torch.bfloat16, **kw):
+    return tact.Geometry(S, H, W, hk, d, budget, max_bits=bmax, dtype=dtype, **kw)
+
+
+def _oparams(g):
+    return O.Params(g.S, g.H, g.W, g.kv_heads, g.head_dim, g.budget_bits, g.max_bits)
+
+
+def _units(g, n, seed=0, scale_spike=True):
+    """n random correlated units of geometry g (AR(1) field + spikes), on GPU."""
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    x = torch.randn((n,) + g.unit_shape, generator=gen, dtype=torch.float64)
+    for ax, rho in ((1, 0.9), (2, 0.85), (3, 0.8)):
+        for i in range(1, x.shape[ax]):
+            cur = x.select(ax, i)
+            cur.mul_(math.sqrt(1 - rho * rho)).add_(x.select(ax, i - 1), alpha=rho)
+    if scale_spike:
+        sc = torch.ones(g.kv_heads * g.head_dim, dtype=torch.float64)
+        sc[torch.randperm(sc.numel(), generator=gen)[:3]] = 8.0
+        x = x * sc.view(g.kv_heads, g.head_dim)
+    return x.to(g.dtype).cuda()
+
+
+GEOMS = [
+    # (S, H, W, kv_heads, head_dim, budget, bmax, dtype)
+    (4, 8, 8, 2, 64, 1, 3, torch.float32),          # the tiny workload shape
+    (5, 7, 9, 3, 64, 2, 8, torch.bfloat16),         # ragged everywhere
+    (3, 14, 14, 1, 128, 1, 8, torch.bfloat16),
+    (2, 5, 3, 2, 256, 4, 8, torch.bfloat16),
+    (33, 3, 2, 1, 128, 3, 5, torch.bfloat16),       # S beyond 32
+    (64, 2, 3, 1, 64, 1, 8, torch.float32),
+]
+
+
+def _rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+@pytest.mark.parametrize("geo", GEOMS)
+def test_dct_forward_and_inverse(geo):
+    g = _geom(*geo)
+    say("dct", geo)
+    x = _units(g, 2, seed=1)
+    c = tact.dbg_dct3(x, g).cpu().numpy()
+    xs = x.float().cpu().numpy().astype(np.float64)
+    for u in range(2):
+        assert _rel(c[u], O.dct3_forward(xs[u])) <= 1e-5
+    y = tact.dbg_dct3(torch.from_numpy(c).cuda(), g, inverse=True).cpu().numpy()
+    for u in range(2):
+        assert _rel(y[u], O.dct3_inverse(c[u].astype(np.float64))) <= 1e-5
+        assert _rel(y[u], xs[u]) <= 1e-5
+
+
+@pytest.mark.parametrize("axes", [1, 2, 4, 3, 6, 5])
+def test_dct_axis_subsets(axes):
+    g = _geom(5, 6, 7, 2, 64, 1, axes=axes)
+    say("dct axes", axes)
+    x = _units(g, 1, seed=2)
+    c = tact.dbg_dct3(x, g).cpu().numpy()[0]
+    ax = tuple(a for a in range(3) if axes & (1 << a))
+    ref = O.dct3_forward(x.float().cpu().numpy()[0].astype(np.float64), ax)
+    assert _rel(c, ref) <= 1e-5
+
+
+@pytest.mark.parametrize("geo", GEOMS[:4])
+def test_bin_variance(geo):
+    g = _geom(*geo)
+    say("variance", geo)
+    coef = torch.randn((2,) + g.unit_shape, dtype=torch.float32) * 3.0
+    var = tact.dbg_bin_variance(coef.cuda(), g).cpu().numpy()
+    ref = O.bin_variance(coef.numpy().astype(np.float64))
+    assert np.max(np.abs(var - ref) / ref) < 1e-6
+
+
+def _var_cases(rng, nb):
+    v = np.exp(rng.normal(0.0, 4.0, nb)).astype(np.float32)
+    out = [v.copy()]
+    w = v.copy()
+    w[::7] = w[0]                       # exact ties
+    w[1::11] = w[1] * np.float32(4.0)   # ties across bit levels
+    w[2::13] = 0.0                      # dead bins
+    out.append(w)
+    out.append(np.zeros(nb, np.float32))                       # all dead
+    q = np.full(nb, 2.0, np.float32)                           # all equal
+    out.append(q)
+    sub = v.copy()
+    sub[:nb // 3] = np.float32(1e-42)                          # fp32 subnormals
+    out.append(sub)
+    return out
+
+
+@pytest.mark.parametrize("geo,budget,bmax", [
+    ((4, 8, 8, 2, 64), 1, 3), ((5, 7, 9, 3, 64), 2, 8), ((3, 14, 14, 1, 128), 1, 8),
+    ((1, 1, 3, 1, 64), 1, 2), ((2, 5, 3, 2, 256), 4, 8), ((7, 3, 5, 1, 64), 0, 8),
+    ((7, 3, 5, 1, 64), 8, 8), ((6, 6, 6, 4, 64), 3, 4),
+])
+def test_allocation_bit_exact(geo, budget, bmax):
+    g = _geom(*geo, budget, bmax)
+    say("allocate", geo, budget, bmax)
+    rng = np.random.default_rng(sum(geo) + budget)
+    cases = _var_cases(rng, g.n_bins)
+    var = torch.from_numpy(np.stack(cases).reshape((len(cases),) + g.unit_shape[:-1]))
+    bits = tact.dbg_allocate(var.cuda(), g).cpu().numpy().reshape(len(cases), -1)
+    for u, v in enumerate(cases):
+        ref = O.allocate_bits(v.astype(np.float64), budget * g.n_bins, bmax)
+        assert np.array_equal(bits[u].astype(np.int64), ref), u
+
+
+def test_uniform_allocation():
+    g = _geom(3, 4, 5, 2, 64, 3, 8, alloc_mode=tact.ALLOC_UNIFORM)
+    var = torch.rand((2,) + g.unit_shape[:-1]).cuda()
+    bits = tact.dbg_allocate(var, g).cpu()
+    assert torch.all(bits == 3)
+
+
+@pytest.mark.parametrize("geo", GEOMS)
+def test_quantize_pack_byte_exact(geo):
+    g = _geom(*geo)
+    say("quantize", geo)
+    op = _oparams(g)
+    rng = np.random.default_rng(3)
+    U = 2
+    coef = (rng.standard_t(3, (U,) + g.unit_shape) *
+            np.exp(rng.normal(0, 2, (U,) + g.unit_shape[:-1]))[..., None]).astype(np.float32)
+    coef[0, 0, 0, 0, 0, :] = 0.0        # a zero-energy bin
+    gains, bits, recs = [], [], []
+    for u in range(U):
+        v = O.bin_variance(coef[u])
+        b = O.allocate_bits(v, O.total_bits(op), g.max_bits).reshape(v.shape)
+        gg = O.gains_f32(v)
+        gains.append(gg)
+        bits.append(b.astype(np.uint8))
+        recs.append(O.pack_record(O.quantize(coef[u], gg, b), gg, b, op))
+    rec = tact.dbg_quantize(torch.from_numpy(coef).cuda(), torch.from_numpy(np.stack(gains)).cuda(),
+                            torch.from_numpy(np.stack(bits)).cuda(), g).cpu().numpy()
+    for u in range(U):
+        assert np.array_equal(rec[u], recs[u]), u
+
+
+@pytest.mark.parametrize("geo", GEOMS)
+def test_unpack_and_dequantize(geo):
+    g = _geom(*geo)
+    say("unpack", geo)
+    op = _oparams(g)
+    x = _units(g, 2, seed=4).float().cpu().numpy().astype(np.float64)
+    recs = np.stack([O.compress(x[u], op) for u in range(2)])
+    rt = torch.from_numpy(recs).cuda()
+    codes = tact.dbg_unpack(rt, g).cpu().numpy()
+    deq = tact.dbg_dequantize(rt, g).cpu().numpy()
+    for u in range(2):
+        c, gg, b = O.unpack_record(recs[u], op)
+        assert np.array_equal(codes[u], c)
+        ref = O.dequantize(c, gg, b)
+        assert np.all(np.abs(deq[u] - ref) <= 2.0 ** -23 * np.abs(ref))
+
+
+@pytest.mark.parametrize("geo", GEOMS)
+def test_decompress_from_oracle_records(geo):
+    g = _geom(*geo)
+    say("decompress", geo)
+    op = _oparams(g)
+    x = _units(g, 2, seed=5).float().cpu().numpy().astype(np.float64)
+    recs = np.stack([O.compress(x[u], op) for u in range(2)])
+    out = tact.decompress(torch.from_numpy(recs).cuda(), g).float().cpu().numpy()
+    for u in range(2):
+        if g.dtype == torch.bfloat16:
+            ref = O.decompress(recs[u], op, "bf16")
+            a, b = O.bf16_bits(out[u]).astype(np.int64), O.bf16_bits(ref).astype(np.int64)
+            diff = a != b
+            assert diff.mean() <= 1e-3
+            assert np.all(np.abs(a[diff] - b[diff]) == 1)
+        else:
+            ref = O.decompress(recs[u], op, None)
+            assert _rel(out[u], ref) <= 1e-5
+
+
+def _compare_records(rec_gpu, rec_ref, op, coef_ref):
+    """End-to-end record comparison; returns stats."""
+    c1, g1, b1 = O.unpack_record(rec_gpu, op)
+    c2, g2, b2 = O.unpack_record(rec_ref, op)
+    assert b1.sum() == b2.sum() == O.total_bits(op)
+    # bits may differ only where the bin's marginal gain sits at the cut
+    var_ref = O.bin_variance(coef_ref)
+    differ = b1 != b2
+    if differ.any():
+        gains = np.sort(np.ldexp(np.repeat(var_ref.ravel(), op.max_bits),
+                                 -2 * np.tile(np.arange(op.max_bits), var_ref.size)))[::-1]
+        cut = gains[O.total_bits(op) - 1]
+        for idx in zip(*np.nonzero(differ)):
+            k = min(b1[idx], b2[idx])          # the contested bit
+            gk = np.ldexp(var_ref[idx], -2 * int(k))
+            assert abs(gk - cut) <= 1e-5 * cut, (idx, gk, cut)
+    assert differ.mean() <= 1e-3
+    np.testing.assert_allclose(g1, g2, rtol=1e-5)
+    same = (b1 == b2) & (b1 > 0)
+    eq = c1[same] == c2[same]
+    assert eq.mean() >= 0.9999
+    # every mismatching code sits next to a decision threshold
+    if (~eq).any():
+        u = coef_ref[same][~eq] / g2[same][:, None].repeat(op.head_dim, 1)[~eq]
+        bb = b1[same][:, None].repeat(op.head_dim, 1)[~eq]
+        for ui, bi in zip(u, bb):
+            _, thr = O.codebook_f32(int(bi))
+            t = thr[np.argmin(np.abs(thr - ui))]
+            assert abs(ui - t) <= 1e-5 * max(abs(float(t)), 1e-2), (ui, t)
+    return differ.mean(), 1 - eq.mean()
+
+
+@pytest.mark.parametrize("geo", GEOMS)
+def test_compress_end_to_end(geo):
+    g = _geom(*geo)
+    say("compress", geo)
+    op = _oparams(g)
+    x = _units(g, 2, seed=6)
+    rec = tact.compress(x, g.budget_bits, g.max_bits).cpu().numpy()
+    xs = x.float().cpu().numpy().astype(np.float64)
+    for u in range(2):
+        ref = O.compress(xs[u], op)
+        _compare_records(rec[u], ref, op, O.dct3_forward(xs[u]))
+
+
+def _roundtrip_check(x_gpu, g, units=None):
+    op = _oparams(g)
+    out, rec = tact.roundtrip(x_gpu, g.budget_bits, g.max_bits)
+    units = range(x_gpu.shape[0]) if units is None else units
+    for u in units:
+        xs = x_gpu[u].float().cpu().numpy().astype(np.float64)
+        od = "bf16" if g.dtype == torch.bfloat16 else "f32"
+        ref_out, ref_rec = O.roundtrip(xs, op, od)
+        m_gpu = O.mse(out[u].float().cpu().numpy(), xs)
+        m_ref = O.mse(ref_out, xs)
+        say(f"  unit {u}: mse gpu {m_gpu:.6e} oracle {m_ref:.6e}")
+        assert abs(m_gpu / m_ref - 1) <= 1e-3
+        _compare_records(rec[u].cpu().numpy(), ref_rec, op, O.dct3_forward(xs))
+
+
+@pytest.mark.parametrize("geo", GEOMS)
+def test_roundtrip_small(geo):
+    g = _geom(*geo)
+    say("roundtrip", geo)
+    _roundtrip_check(_units(g, 3, seed=7), g)
+
+
+def test_tiny_workload_all_units():
+    wl = WORKLOADS["tiny"]
+    say("tiny workload")
+    x = generate_units(wl, device="cuda")
+    g = tact.Geometry(*wl.unit_shape, budget_bits=1, max_bits=3, dtype=torch.float32)
+    _roundtrip_check(x, g)
+
+
+def test_in_place_roundtrip_and_separate_calls_agree():
+    g = _geom(5, 7, 9, 3, 64, 2)
+    x = _units(g, 3, seed=8)
+    out1, rec1 = tact.roundtrip(x, 2)
+    rec2 = tact.compress(x, 2)
+    out2 = tact.decompress(rec2, g)
+    assert torch.equal(rec1, rec2) and torch.equal(out1, out2)
+    y = x.clone()
+    tact.roundtrip(y, 2, out=y, keep_records=False)
+    assert torch.equal(y, out1)
+
+
+def test_deterministic():
+    g = _geom(6, 6, 6, 4, 64, 2)
+    x = _units(g, 4, seed=9)
+    a = tact.compress(x, 2)
+    b = tact.compress(x, 2)
+    assert torch.equal(a, b)
+
+
+def test_strided_units_and_empty_batch():
+    g = _geom(3, 5, 4, 2, 64, 1)
+    big = _units(g, 4, seed=10)
+    view = big[::2]                          # unit stride = 2 units
+    rec = tact.compress(view, 1)
+    ref = tact.compress(view.contiguous(), 1)
+    assert torch.equal(rec, ref)
+    empty = big[:0]
+    assert tact.compress(empty, 1).shape[0] == 0
+
+
+FULL = [("ct4b", 1), ("ct4b", 4), ("ct7b", 1), ("ct32b", 1), ("video", 1), ("video", 2)]
+
+
+@pytest.mark.parametrize("name,budget", FULL)
+def test_full_size_sampled_units(name, budget):
+    """Whole launch at the workload's full size (as the benchmark runs it);
+    the first and last unit are checked against the oracle."""
+    wl = WORKLOADS[name]
+    say("full size", name, budget, "units", wl.n_units)
+    x = generate_units(wl, device="cuda")
+    g = tact.Geometry(*wl.unit_shape, budget_bits=budget, max_bits=wl.max_bits, dtype=wl.dtype)
+    _roundtrip_check(x, g, units=[0, wl.n_units - 1])
+    del x
+    torch.cuda.empty_cache()
