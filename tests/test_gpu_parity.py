@@ -201,11 +201,18 @@ def test_decompress_from_oracle_records(geo):
     out = tact.decompress(torch.from_numpy(recs).cuda(), g).float().cpu().numpy()
     for u in range(2):
         if g.dtype == torch.bfloat16:
-            ref = O.decompress(recs[u], op, "bf16")
-            a, b = O.bf16_bits(out[u]).astype(np.int64), O.bf16_bits(ref).astype(np.int64)
+            exact = O.decompress(recs[u], op, None)
+            ref = O.round_to_bf16(exact)
+            a, b = O.bf16_bits(out[u]), O.bf16_bits(ref)
             diff = a != b
             assert diff.mean() <= 1e-3
-            assert np.all(np.abs(a[diff] - b[diff]) == 1)
+            # a mismatch is a rounding-boundary case: the GPU value is within
+            # half a bf16 ulp of the exact value, up to the fp32 transform's
+            # error (~1e-6 of the unit's RMS, which dominates near zero)
+            mag = np.maximum(np.abs(exact[diff]), np.abs(out[u][diff]))
+            ulp = np.ldexp(1.0, (np.floor(np.log2(mag)) - 7).astype(int))
+            rms = math.sqrt(np.mean(exact ** 2))
+            assert np.all(np.abs(out[u][diff] - exact[diff]) <= 0.5 * ulp + 1e-6 * rms)
         else:
             ref = O.decompress(recs[u], op, None)
             assert _rel(out[u], ref) <= 1e-5
@@ -239,7 +246,8 @@ def _compare_records(rec_gpu, rec_ref, op, coef_ref):
         for ui, bi in zip(u, bb):
             _, thr = O.codebook_f32(int(bi))
             t = thr[np.argmin(np.abs(thr - ui))]
-            assert abs(ui - t) <= 1e-5 * max(abs(float(t)), 1e-2), (ui, t)
+            # distance to the boundary in units of the bin gain
+            assert abs(ui - t) <= 1e-5 * max(abs(float(t)), 1.0), (ui, t)
     return differ.mean(), 1 - eq.mean()
 
 
