@@ -244,8 +244,10 @@ def dbg_dct3(x: torch.Tensor, geom: Geometry, inverse: bool = False) -> torch.Te
     U = x.shape[0]
     out = torch.empty((U,) + geom.unit_shape, dtype=torch.float32, device=x.device)
     p = geom.params()
+    nws = _lib.tact_dbg_workspace_bytes(ctypes.byref(p), U)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=x.device)
     _check(_lib.tact_dbg_dct3(ctypes.byref(p), U, 1 if inverse else 0, _ptr(x), _ptr(out),
-                              None, 0, _stream()), "tact_dbg_dct3")
+                              _ptr(ws), ws.numel(), _stream()), "tact_dbg_dct3")
     return out
 
 

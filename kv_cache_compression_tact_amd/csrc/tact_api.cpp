@@ -32,8 +32,10 @@ tact_status ok() {
 }
 
 // Upper bound on the workspace one chunk of units may use; batches larger
-// than a chunk are processed chunk by chunk on the same stream.
-constexpr int64_t kChunkWorkspaceBytes = int64_t(2) << 30;
+// than a chunk are processed chunk by chunk on the same stream.  Sized for
+// the 288 GB of HBM of an MI355X: whole launches of the large workloads fit
+// in one chunk, so every kernel runs once over all units.
+constexpr int64_t kChunkWorkspaceBytes = int64_t(24) << 30;
 
 tact_status make_geometry(const tact_params* p, Geometry* g) {
   if (!p) return fail(TACT_ERR_INVALID_ARGUMENT, "params is NULL");
@@ -83,31 +85,51 @@ tact_status make_geometry(const tact_params* p, Geometry* g) {
 
 int64_t elem_size(int dtype) { return dtype == TACT_F32 ? 4 : 2; }
 
-// Per-unit workspace of the codec calls: fp32 coefficients, fp32
-// variances, one record.
+// Workspace of the codec calls: DCT tables once, then per unit of a chunk an
+// fp32 intermediate volume, fp32 variances, fp32 reciprocal gains, uint32
+// per-bin first planes and one record (used by tact_roundtrip when
+// records == NULL).
 int64_t unit_ws_bytes(const Geometry& g) {
-  return align256(4 * g.n_entries) + align256(4 * g.n_bins) + g.record_bytes;
+  return align256(4 * g.n_entries) + 3 * align256(4 * g.n_bins) + g.record_bytes;
 }
+
+// floats between the variances of consecutive units in the workspace
+int64_t var_stride(const Geometry& g) { return align256(4 * g.n_bins) / 4; }
+
+constexpr int64_t kTableBytes = align256(4 * kDctTableFloats);
 
 int64_t chunk_units(const Geometry& g, int64_t n_units) {
   int64_t c = kChunkWorkspaceBytes / unit_ws_bytes(g);
   if (c < 1) c = 1;
-  if (c > 65535) c = 65535;  // grid.y limit of the transform kernels
+  if (c > 65535) c = 65535;
   return n_units < c ? n_units : c;
 }
 
+int64_t ws_bytes(const Geometry& g, int64_t n_units) {
+  return kTableBytes + chunk_units(g, n_units) * unit_ws_bytes(g);
+}
+
 struct Workspace {
+  float* tab;
   float* coef;
   float* var;
+  float* invg;
+  uint32_t* poff;
   uint8_t* recs;
 };
 
 Workspace carve(const Geometry& g, int64_t chunk, void* ws) {
   uint8_t* b = static_cast<uint8_t*>(ws);
   Workspace w;
+  w.tab = reinterpret_cast<float*>(b);
+  b += kTableBytes;
   w.coef = reinterpret_cast<float*>(b);
   b += chunk * align256(4 * g.n_entries);
   w.var = reinterpret_cast<float*>(b);
+  b += chunk * align256(4 * g.n_bins);
+  w.invg = reinterpret_cast<float*>(b);
+  b += chunk * align256(4 * g.n_bins);
+  w.poff = reinterpret_cast<uint32_t*>(b);
   b += chunk * align256(4 * g.n_bins);
   w.recs = b;
   return w;
@@ -142,7 +164,7 @@ tact_status check_buffer(const void* ptr, const char* name, uintptr_t align) {
 }
 
 tact_status check_workspace(const Geometry& g, int64_t n_units, const void* ws, size_t bytes) {
-  const int64_t need = chunk_units(g, n_units) * unit_ws_bytes(g);
+  const int64_t need = ws_bytes(g, n_units);
   if (!ws) return fail(TACT_ERR_WORKSPACE, "workspace is NULL (%lld bytes needed)", (long long)need);
   if (!aligned(ws, 256)) return fail(TACT_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
   if (static_cast<int64_t>(bytes) < need)
@@ -168,19 +190,63 @@ RecordView view(const Geometry& g, void* base) {
   return r;
 }
 
-// compress `cn` units: kv chunk -> records chunk, workspace w
-void compress_chunk(const Geometry& g, int64_t cn, const void* kv, int64_t kv_stride,
-                    uint8_t* recs, const Workspace& w, hipStream_t s) {
-  launch_dct3(g, cn, 0, kv, g.dtype, kv_stride, w.coef, TACT_F32, g.n_entries, nullptr, s);
-  launch_bin_variance(g, cn, w.coef, w.var, s);
-  launch_allocate(g, cn, w.var, nullptr, view(g, recs), s);
-  launch_quantize(g, cn, w.coef, view(g, recs), s);
+// Transform axes in forward order (S, H, W) restricted to the mask.
+int forward_axes(const Geometry& g, int* ax) {
+  int m = 0;
+  for (int a = 0; a < 3; ++a)
+    if (g.axes & (1 << a)) ax[m++] = a;
+  return m;
 }
 
+// compress `cn` units: kv chunk -> records chunk.  All axes but the last run
+// forward into the fp32 volume; the last axis runs twice, first producing
+// the per-bin variances, then (after the allocation) the codes.
+void compress_chunk(const Geometry& g, int64_t cn, const void* kv, int64_t kv_stride,
+                    uint8_t* recs, const Workspace& w, hipStream_t s) {
+  int ax[3];
+  const int m = forward_axes(g, ax);
+  const RecordView none{};
+  const int in_pro = g.dtype == TACT_BF16 ? AX_PRO_BF16 : AX_PRO_F32;
+  for (int j = 0; j + 1 < m; ++j) {
+    if (j == 0)
+      launch_axis(g, cn, ax[j], 0, in_pro, AX_EPI_F32, kv, kv_stride, w.coef, g.n_entries,
+                  w.tab, nullptr, nullptr, 0, none, nullptr, s);
+    else
+      launch_axis(g, cn, ax[j], 0, AX_PRO_F32, AX_EPI_F32, w.coef, g.n_entries, w.coef,
+                  g.n_entries, w.tab, nullptr, nullptr, 0, none, nullptr, s);
+  }
+  const void* last_in = (m == 1) ? kv : static_cast<const void*>(w.coef);
+  const int64_t last_stride = (m == 1) ? kv_stride : g.n_entries;
+  const int last_pro = (m == 1) ? in_pro : AX_PRO_F32;
+  const int64_t vs = var_stride(g);
+  launch_axis(g, cn, ax[m - 1], 0, last_pro, AX_EPI_STATS, last_in, last_stride, nullptr, 0,
+              w.tab, w.var, nullptr, vs, none, nullptr, s);
+  // the variances are consumed by the allocation; their slots then hold
+  // the reciprocal gains for the coding pass
+  launch_allocate2(g, cn, w.var, vs, nullptr, view(g, recs), w.poff, w.invg, s);
+  launch_axis(g, cn, ax[m - 1], 0, last_pro, AX_EPI_QUANT, last_in, last_stride, nullptr, 0,
+              w.tab, nullptr, w.invg, vs, view(g, recs), w.poff, s);
+}
+
+// decompress `cn` records: the last forward axis runs first, reading and
+// dequantizing the codes; the remaining axes run in reverse order, the last
+// one writing the cache.
 void decompress_chunk(const Geometry& g, int64_t cn, const uint8_t* recs, void* out,
                       int64_t out_stride, const Workspace& w, hipStream_t s) {
-  launch_unpack(g, cn, view(g, const_cast<uint8_t*>(recs)), nullptr, w.coef, s);
-  launch_dct3(g, cn, 1, w.coef, TACT_F32, g.n_entries, out, g.dtype, out_stride, w.coef, s);
+  int ax[3];
+  const int m = forward_axes(g, ax);
+  const RecordView rv = view(g, const_cast<uint8_t*>(recs));
+  const int out_epi = g.dtype == TACT_BF16 ? AX_EPI_BF16 : AX_EPI_F32;
+  launch_plane_offsets(g, cn, rv, w.poff, s);
+  for (int j = m - 1; j >= 0; --j) {
+    const bool first = (j == m - 1), last = (j == 0);
+    const int pro = first ? AX_PRO_DEQUANT : AX_PRO_F32;
+    const int epi = last ? out_epi : AX_EPI_F32;
+    void* o = last ? out : static_cast<void*>(w.coef);
+    const int64_t os = last ? out_stride : g.n_entries;
+    launch_axis(g, cn, ax[j], 1, pro, epi, w.coef, g.n_entries, o, os, w.tab, nullptr, nullptr, 0,
+                rv, w.poff, s);
+  }
 }
 
 }  // namespace
@@ -215,7 +281,7 @@ size_t tact_workspace_bytes(const tact_params* p, int64_t n_units) {
   Geometry g;
   if (make_geometry(p, &g) != TACT_OK) return 0;
   if (n_units <= 0) return 0;
-  return static_cast<size_t>(chunk_units(g, n_units) * unit_ws_bytes(g));
+  return static_cast<size_t>(ws_bytes(g, n_units));
 }
 
 tact_status tact_compress(const tact_params* p, int64_t n_units, const void* kv,
@@ -232,6 +298,7 @@ tact_status tact_compress(const tact_params* p, int64_t n_units, const void* kv,
   const int64_t chunk = chunk_units(g, n_units);
   const Workspace w = carve(g, chunk, workspace);
   const int64_t es = elem_size(g.dtype);
+  launch_dct_tables(g, w.tab, stream);
   for (int64_t u0 = 0; u0 < n_units; u0 += chunk) {
     const int64_t cn = (n_units - u0 < chunk) ? n_units - u0 : chunk;
     compress_chunk(g, cn, static_cast<const uint8_t*>(kv) + u0 * kv_unit_stride * es,
@@ -255,6 +322,7 @@ tact_status tact_decompress(const tact_params* p, int64_t n_units, const void* r
   const int64_t chunk = chunk_units(g, n_units);
   const Workspace w = carve(g, chunk, workspace);
   const int64_t es = elem_size(g.dtype);
+  launch_dct_tables(g, w.tab, stream);
   for (int64_t u0 = 0; u0 < n_units; u0 += chunk) {
     const int64_t cn = (n_units - u0 < chunk) ? n_units - u0 : chunk;
     decompress_chunk(g, cn, static_cast<const uint8_t*>(records) + u0 * g.record_bytes,
@@ -287,6 +355,7 @@ tact_status tact_roundtrip(const tact_params* p, int64_t n_units, const void* kv
   const int64_t chunk = chunk_units(g, n_units);
   const Workspace w = carve(g, chunk, workspace);
   const int64_t es = elem_size(g.dtype);
+  launch_dct_tables(g, w.tab, stream);
   for (int64_t u0 = 0; u0 < n_units; u0 += chunk) {
     const int64_t cn = (n_units - u0 < chunk) ? n_units - u0 : chunk;
     uint8_t* recs = records ? static_cast<uint8_t*>(records) + u0 * g.record_bytes : w.recs;
@@ -326,14 +395,12 @@ size_t tact_dbg_workspace_bytes(const tact_params* p, int64_t n_units) {
   Geometry g;
   if (make_geometry(p, &g) != TACT_OK) return 0;
   (void)n_units;
-  return 0;
+  return static_cast<size_t>(kTableBytes);
 }
 
 tact_status tact_dbg_dct3(const tact_params* p, int64_t n_units, int32_t inverse,
                           const void* in, float* out, void* workspace,
                           size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   Geometry g;
   tact_status st;
   if ((st = make_geometry(p, &g)) != TACT_OK) return st;
@@ -341,9 +408,23 @@ tact_status tact_dbg_dct3(const tact_params* p, int64_t n_units, int32_t inverse
   if (n_units == 0) return ok();
   if ((st = check_buffer(in, "in", 16)) != TACT_OK) return st;
   if ((st = check_buffer(out, "out", 16)) != TACT_OK) return st;
-  const int in_dtype = inverse ? TACT_F32 : g.dtype;
-  launch_dct3(g, n_units, inverse ? 1 : 0, in, in_dtype, g.n_entries, out, TACT_F32,
-              g.n_entries, nullptr, stream);
+  if (!workspace) return fail(TACT_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(TACT_ERR_INVALID_ARGUMENT, "workspace not 256-byte aligned");
+  if (static_cast<int64_t>(workspace_bytes) < kTableBytes)
+    return fail(TACT_ERR_WORKSPACE, "workspace of %zu bytes, %lld needed", workspace_bytes,
+                (long long)kTableBytes);
+  float* tab = static_cast<float*>(workspace);
+  launch_dct_tables(g, tab, stream);
+  int ax[3];
+  const int m = forward_axes(g, ax);
+  const RecordView none{};
+  for (int j = 0; j < m; ++j) {
+    const int a = inverse ? ax[m - 1 - j] : ax[j];
+    const int pro = (j == 0 && !inverse && g.dtype == TACT_BF16) ? AX_PRO_BF16 : AX_PRO_F32;
+    const void* src = (j == 0) ? in : static_cast<const void*>(out);
+    launch_axis(g, n_units, a, inverse ? 1 : 0, pro, AX_EPI_F32, src, g.n_entries, out,
+                g.n_entries, tab, nullptr, nullptr, 0, none, nullptr, stream);
+  }
   return after_launch("tact_dbg_dct3");
 }
 
@@ -370,7 +451,7 @@ tact_status tact_dbg_allocate(const tact_params* p, int64_t n_units, const float
   if ((st = check_buffer(var, "var", 4)) != TACT_OK) return st;
   if ((st = check_buffer(bits, "bits", 1)) != TACT_OK) return st;
   RecordView none{};
-  launch_allocate(g, n_units, var, bits, none, stream);
+  launch_allocate2(g, n_units, var, g.n_bins, bits, none, nullptr, nullptr, stream);
   return after_launch("tact_dbg_allocate");
 }
 

@@ -31,7 +31,7 @@ struct RecordView {
   int64_t off_gains, off_bits, off_groups, off_codes;
 };
 
-inline int64_t align256(int64_t n) { return (n + 255) / 256 * 256; }
+constexpr int64_t align256(int64_t n) { return (n + 255) / 256 * 256; }
 
 // ---- launchers (tact_kernels.hip); all asynchronous on `stream` -----------
 
@@ -69,6 +69,32 @@ void launch_quantize(const Geometry& g, int64_t n_units, const float* coef,
 // (fp32 g * level) from records; either may be null.
 void launch_unpack(const Geometry& g, int64_t n_units, RecordView rec,
                    uint8_t* codes_out, float* coef_out, hipStream_t stream);
+
+// ---- MFMA path (tact_mfma.hip) ---------------------------------------------
+// Prologue / epilogue selectors of launch_axis.
+enum { AX_PRO_BF16 = 0, AX_PRO_F32 = 1, AX_PRO_DEQUANT = 2 };
+enum { AX_EPI_F32 = 0, AX_EPI_BF16 = 1, AX_EPI_STATS = 2, AX_EPI_QUANT = 3 };
+constexpr int64_t kDctTableFloats = 3 * 64 * 64;
+
+// DCT-II matrices of the three axes into tab[3][64][64] (fp32, zero padded).
+void launch_dct_tables(const Geometry& g, float* tab, hipStream_t stream);
+
+// One axis (0 = S, 1 = H, 2 = W) of the transform on the matrix cores over
+// n_units units; see tact_mfma.hip for the prologue / epilogue contracts.
+void launch_axis(const Geometry& g, int64_t n_units, int axis, int inverse, int pro, int epi,
+                 const void* in, int64_t in_stride, void* out, int64_t out_stride,
+                 const float* tab, float* var, const float* inv_gain, int64_t var_stride,
+                 RecordView rec, const uint32_t* plane_off, hipStream_t stream);
+
+// Allocation by exact radix selection; writes bits_out and/or the record
+// header, and per-bin first planes into plane_off (each may be null).
+void launch_allocate2(const Geometry& g, int64_t n_units, const float* var, int64_t var_stride,
+                      uint8_t* bits_out, RecordView rec, uint32_t* plane_off, float* inv_gain,
+                      hipStream_t stream);
+
+// Per-bin first planes from the bits stored in records.
+void launch_plane_offsets(const Geometry& g, int64_t n_units, RecordView rec,
+                          uint32_t* plane_off, hipStream_t stream);
 
 // Host copy of the fp32 codebooks.
 extern const float kHostLevels[];

@@ -20,10 +20,8 @@
 
 namespace tact {
 
-#include "generated/codebooks.inc"
+#include "codebook_device.h"
 
-__constant__ float c_levels[TACT_CODEBOOK_LEVELS] = {TACT_CODEBOOK_LEVEL_VALUES};
-__constant__ float c_thresholds[TACT_CODEBOOK_THRESHOLDS] = {TACT_CODEBOOK_THRESHOLD_VALUES};
 const float kHostLevels[TACT_CODEBOOK_LEVELS] = {TACT_CODEBOOK_LEVEL_VALUES};
 const float kHostThresholds[TACT_CODEBOOK_THRESHOLDS] = {TACT_CODEBOOK_THRESHOLD_VALUES};
 

@@ -1,0 +1,893 @@
+// MFMA path of the TACT-KV codec for gfx950 (page "TACT-KV: Tri-Axis Cosine
+// Transform for Compressing Volumetric KV Caches in Medical VLMs", section
+// "Methodology in Plain English", stages 2-4 and the decoding paragraph).
+//
+// k_axis: one axis of the separable DCT as dense matrix products on the
+// matrix cores.  The axis of length N is the contraction (K) dimension,
+// padded to 16/32/64; the columns are 16 consecutive elements of the
+// contiguous trailing dimensions (one 64-byte run per 16 lanes).  Products
+// keep fp32 accuracy with split fp16 operands: the DCT matrix, scaled by
+// 2^12, is C_hi + C_lo; every column is scaled by a power of two that puts
+// its largest magnitude in [2^13, 2^14) and split x_hi + x_lo, so each
+// operand carries ~22 significant bits (|x - x_hi - x_lo| <= 2^-22 |x| plus
+// a floor 2^-38 below the column maximum).  bf16 inputs are exact in fp16
+// and need C_hi*x + C_lo*x; fp32 inputs add C_hi*x_lo.  Accumulation is fp32
+// inside the MFMA; the power-of-two scales are undone exactly on output.
+//   prologues:  bf16 / fp32 loads, or dequantization straight from a record
+//               (first inverse axis);
+//   epilogues:  fp32 / bf16 stores, per-bin variance (last forward axis,
+//               statistics pass), or quantization + bit-plane packing (last
+//               forward axis, coding pass).
+//
+// k_allocate2: reverse water-filling as an exact radix selection of the
+// T-th largest marginal gain (3 histogram sweeps instead of a long
+// bisection), then the index-ordered tie rule, record header and per-bin
+// plane offsets.
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "tact_internal.h"
+
+namespace tact {
+
+#include "codebook_device.h"
+
+namespace {
+
+constexpr int kWave = 64;
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// scale of the DCT matrix before splitting (keeps C_lo out of fp16
+// subnormals); undone on output
+constexpr float kMatScale = 4096.0f;
+
+// ---------------------------------------------------------------------------
+// DCT-II matrices of the three axes, fp32, zero padded to 64 x 64:
+// tab[a][k][n] = a_k cos(pi (2n+1) k / 2N_a), a_0 = sqrt(1/N), a_k = sqrt(2/N).
+// ---------------------------------------------------------------------------
+__global__ void k_dct_tables(float* __restrict__ tab, int n0, int n1, int n2) {
+  const int a = blockIdx.x;
+  const int N = a == 0 ? n0 : (a == 1 ? n1 : n2);
+  for (int e = threadIdx.x; e < 64 * 64; e += blockDim.x) {
+    const int k = e / 64, n = e % 64;
+    float v = 0.f;
+    if (k < N && n < N) {
+      const double al = (k == 0) ? sqrt(1.0 / N) : sqrt(2.0 / N);
+      v = static_cast<float>(al * cospi((2.0 * n + 1.0) * k / (2.0 * N)));
+    }
+    tab[a * 4096 + e] = v;
+  }
+}
+
+// fp32 -> (hi, lo) fp16 pair with hi = RNE(x), lo = RNE(x - hi); x must be
+// below 2^15 in magnitude (callers scale first).
+__device__ __forceinline__ void split2(float x, _Float16& hi, _Float16& lo) {
+  hi = static_cast<_Float16>(x);
+  lo = static_cast<_Float16>(x - static_cast<float>(hi));
+}
+
+// max over the 4 lane groups that hold the K ranges of one column
+__device__ __forceinline__ float column_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+
+__device__ __forceinline__ uint16_t bf16_rne_bits(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Number of the 2^b - 1 ascending thresholds (LDS copy) that are <= u.
+__device__ __forceinline__ int cell_index_lds(const float* thr, float u, int b) {
+  const float* t = thr + ((1 << b) - b - 1);
+  int pos = 0;
+  for (int step = 1 << (b - 1); step >= 1; step >>= 1)
+    if (t[pos + step - 1] <= u) pos += step;
+  return pos;
+}
+
+enum Pro { PRO_BF16 = 0, PRO_F32 = 1, PRO_DEQUANT = 2 };
+enum Epi { EPI_F32 = 0, EPI_BF16 = 1, EPI_STATS = 2, EPI_QUANT = 3 };
+
+struct AxisArgs {
+  const void* in;
+  int64_t in_ustride;        // elements between units
+  void* out;
+  int64_t out_ustride;
+  const float* tab;          // 64 x 64 matrix of this axis
+  int inverse;               // multiply by C^T instead of C
+  int N;                     // axis length
+  int64_t outer, inner;      // columns: outer x inner, inner contiguous
+  int64_t n_units;
+  // bins (epilogues / dequant prologue)
+  int head_dim, kv_heads;
+  int64_t C;                 // kv_heads * head_dim
+  int64_t n_bins;
+  int64_t total_bits;
+  int max_bits;
+  float* var;                // EPI_STATS: var[u * var_stride + bin]
+  const float* inv_gain;     // EPI_QUANT: fp32 1/gain per bin (0 for gain 0), same stride
+  int64_t var_stride;
+  RecordView rec;            // EPI_QUANT, PRO_DEQUANT
+  const uint32_t* plane_off; // per-bin first plane, u * n_bins + bin
+};
+
+template <int NP>
+struct Frag {
+  // K elements per lane per MFMA and number of K steps
+  static constexpr int KV = (NP == 16) ? 4 : 8;
+  static constexpr int KSTEPS = (NP == 64) ? 2 : 1;
+  static constexpr int KPER = (NP == 16) ? 16 : 32;
+  static constexpr int MT = NP / 16;
+  typedef typename std::conditional<NP == 16, f16x4, f16x8>::type vec;
+};
+
+template <int NP>
+__device__ __forceinline__ f32x4 mfma(typename Frag<NP>::vec a, typename Frag<NP>::vec b, f32x4 c) {
+  if constexpr (NP == 16)
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Column layout of one wave: TPW tiles of 16 columns.
+//   interleaved (plain passes): tile i holds columns c0 + TPW*t + i, so each
+//     lane loads and stores TPW consecutive elements as one vector;
+//   contiguous (variance / quantize passes): tile i holds c0 + 16*i + t, so
+//     a tile is 16 consecutive channels of one head.
+template <int TPW, bool INTL>
+__device__ __forceinline__ int64_t col_of(int64_t c0, int i, int t) {
+  return INTL ? c0 + TPW * t + i : c0 + 16 * i + t;
+}
+
+// Grid: x = groups of 4 waves along the columns (each wave loops over
+// column groups), y = outer index o, z = unit.  One wave: TPW tiles.
+template <int NP, int PRO, int EPI, int TPW>
+__global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
+  static_assert(PRO != PRO_DEQUANT || TPW == 4, "dequant reads one 64-channel word per plane");
+  constexpr bool INTL = (EPI == EPI_F32 || EPI == EPI_BF16);
+  static_assert(!INTL || TPW == 4 || TPW == 8, "vector width");
+  static_assert(!INTL || PRO != PRO_F32 || TPW == 4, "fp32 rows load 4 floats");
+  using F = Frag<NP>;
+  using vec = typename F::vec;
+  const int lane = threadIdx.x % kWave;
+  const int t = lane % 16, g = lane / 16;
+  const int64_t u = blockIdx.z;
+  const int64_t o = blockIdx.y;
+  const int64_t groups = a.inner / (16 * TPW);
+  __shared__ float s_levels[(PRO == PRO_DEQUANT) ? TACT_CODEBOOK_LEVELS : 1];
+  __shared__ float s_thr[(EPI == EPI_QUANT) ? TACT_CODEBOOK_THRESHOLDS : 1];
+  // bin-major staging of one wave's coefficients: quantize (rows = output
+  // frequencies, 16 * TPW channels) or dequantize (rows = input frequencies,
+  // 64 channels); rows padded by 4 floats to spread LDS banks
+  constexpr int ZROW = 16 * TPW + 4;
+  // rows staged at once: at most 32 for the widest heads (LDS budget)
+  constexpr int ZROWS = (TPW == 16 && NP > 32) ? 32 : NP;
+  __shared__ float s_z[(EPI == EPI_QUANT) ? 4 * ZROWS * ZROW : 1];
+  __shared__ float s_d[(PRO == PRO_DEQUANT) ? 4 * NP * 68 : 1];
+  if constexpr (PRO == PRO_DEQUANT || EPI == EPI_QUANT) {
+    if constexpr (PRO == PRO_DEQUANT)
+      for (int j = threadIdx.x; j < TACT_CODEBOOK_LEVELS; j += blockDim.x) s_levels[j] = c_levels[j];
+    if constexpr (EPI == EPI_QUANT)
+      for (int j = threadIdx.x; j < TACT_CODEBOOK_THRESHOLDS; j += blockDim.x) s_thr[j] = c_thresholds[j];
+    __syncthreads();
+  }
+  const int N = a.N;
+
+  // A fragments (the DCT matrix scaled by 2^12, or its transpose), hi / lo
+  vec ahi[F::MT][F::KSTEPS], alo[F::MT][F::KSTEPS];
+#pragma unroll
+  for (int m = 0; m < F::MT; ++m)
+#pragma unroll
+    for (int ks = 0; ks < F::KSTEPS; ++ks)
+#pragma unroll
+      for (int v = 0; v < F::KV; ++v) {
+        const int row = 16 * m + t;
+        const int col = ks * F::KPER + F::KV * g + v;
+        const float c = kMatScale * (a.inverse ? a.tab[col * 64 + row] : a.tab[row * 64 + col]);
+        _Float16 h, l;
+        split2(c, h, l);
+        ahi[m][ks][v] = h;
+        alo[m][ks][v] = l;
+      }
+
+  const int64_t col_stride = a.inner;                 // element step along the axis
+  const int64_t obase = o * static_cast<int64_t>(N) * a.inner;
+  const int64_t bins_per_k = (a.inner / a.C) * a.kv_heads;   // bin step per frequency
+
+  for (int64_t grp = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave; grp < groups;
+       grp += static_cast<int64_t>(gridDim.x) * 4) {
+    const int64_t c0 = grp * (16 * TPW);
+    // bin of frequency k at this column start: bin0 + k * bins_per_k
+    const int64_t bin0 =
+        (o * N * (a.inner / a.C) + c0 / a.C) * a.kv_heads + (c0 % a.C) / a.head_dim;
+
+    f32x4 acc[TPW][F::MT];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int m = 0; m < F::MT; ++m) acc[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    float xv[TPW][F::KSTEPS][F::KV];
+    if constexpr (PRO == PRO_DEQUANT) {
+      // first inverse axis: coefficients come from the record
+      const uint8_t* r = a.rec.base + u * a.rec.stride;
+      const uint8_t* bits = r + a.rec.off_bits;
+      const float* gains = reinterpret_cast<const float*>(r + a.rec.off_gains);
+      const uint64_t* words = reinterpret_cast<const uint64_t*>(r + a.rec.off_codes);
+      const uint32_t* poff = a.plane_off + u * a.n_bins;
+      const int wpp = a.head_dim / 64;
+      const int ch0 = static_cast<int>(c0 % a.head_dim);   // multiple of 64
+      // decode one bin at a time (its bit width is uniform over the wave):
+      // lane j is channel ch0 + j of the bin's 64-bit code words
+      float* dt = s_d + (threadIdx.x / kWave) * NP * 68;
+      // lane j fetches bin j's bits, gain, first plane and code words (all
+      // loads in flight together); the decode loop broadcasts them
+      int bj = 0;
+      float gj = 0.f;
+      uint32_t wlo[8], whi[8];
+      {
+        int64_t pj = 0;
+        if (lane < N) {
+          const int64_t bin = bin0 + lane * bins_per_k;
+          bj = bits[bin];
+          pj = poff[bin];
+          gj = gains[bin];
+          if (bj > a.max_bits || pj + bj > a.total_bits) bj = 0;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          uint64_t w = 0;
+          if (q < bj) w = words[(pj + q) * wpp + ch0 / 64];
+          wlo[q] = static_cast<uint32_t>(w);
+          whi[q] = static_cast<uint32_t>(w >> 32);
+        }
+      }
+      for (int n = 0; n < N; ++n) {
+        const int b = __builtin_amdgcn_readlane(bj, n);
+        float x = 0.f;
+        if (b > 0) {
+          int code = 0;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            if (q < b) {
+              const uint32_t lo = __builtin_amdgcn_readlane(wlo[q], n);
+              const uint32_t hi = __builtin_amdgcn_readlane(whi[q], n);
+              const uint32_t wd = lane < 32 ? lo : hi;
+              code |= static_cast<int>((wd >> (lane & 31)) & 1u) << q;
+            }
+          }
+          x = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gj), n)) *
+              s_levels[(1 << b) - 2 + code];
+        }
+        dt[n * 68 + lane] = x;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int ks = 0; ks < F::KSTEPS; ++ks)
+#pragma unroll
+        for (int v = 0; v < F::KV; ++v) {
+          const int n = ks * F::KPER + F::KV * g + v;
+          float4 q = float4{0.f, 0.f, 0.f, 0.f};
+          if (n < N) q = *reinterpret_cast<const float4*>(dt + n * 68 + TPW * t);
+          xv[0][ks][v] = q.x;
+          xv[1][ks][v] = q.y;
+          xv[2][ks][v] = q.z;
+          xv[3][ks][v] = q.w;
+        }
+    } else if constexpr (INTL) {
+      // TPW consecutive elements per lane: one 16-byte vector per row
+#pragma unroll
+      for (int ks = 0; ks < F::KSTEPS; ++ks)
+#pragma unroll
+        for (int v = 0; v < F::KV; ++v) {
+          const int n = ks * F::KPER + F::KV * g + v;
+          if (n < N) {
+            const int64_t idx = u * a.in_ustride + obase + n * col_stride + c0 + TPW * t;
+            if constexpr (PRO == PRO_BF16) {
+              uint32_t w4[4];
+              if constexpr (TPW == 8) {
+                const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.in) + idx);
+                w4[0] = q.x; w4[1] = q.y; w4[2] = q.z; w4[3] = q.w;
+              } else {
+                const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.in) + idx);
+                w4[0] = q.x; w4[1] = q.y; w4[2] = 0; w4[3] = 0;
+              }
+#pragma unroll
+              for (int i = 0; i < TPW; ++i)
+                xv[i][ks][v] = __uint_as_float((i & 1) ? (w4[i / 2] & 0xFFFF0000u) : (w4[i / 2] << 16));
+            } else {
+              const float4 q = *reinterpret_cast<const float4*>(static_cast<const float*>(a.in) + idx);
+              xv[0][ks][v] = q.x;
+              xv[1][ks][v] = q.y;
+              xv[2][ks][v] = q.z;
+              xv[3][ks][v] = q.w;
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) xv[i][ks][v] = 0.f;
+          }
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int64_t c = c0 + 16 * i + t;
+#pragma unroll
+        for (int ks = 0; ks < F::KSTEPS; ++ks)
+#pragma unroll
+          for (int v = 0; v < F::KV; ++v) {
+            const int n = ks * F::KPER + F::KV * g + v;
+            float x = 0.f;
+            if (n < N) {
+              const int64_t idx = u * a.in_ustride + obase + n * col_stride + c;
+              if constexpr (PRO == PRO_BF16)
+                x = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.in)[idx]) << 16);
+              else
+                x = static_cast<const float*>(a.in)[idx];
+            }
+            xv[i][ks][v] = x;
+          }
+      }
+    }
+
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      float mx = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < F::KSTEPS; ++ks)
+#pragma unroll
+        for (int v = 0; v < F::KV; ++v) mx = fmaxf(mx, fabsf(xv[i][ks][v]));
+      mx = column_max(mx);
+      // scale 2^(14 - e) puts the column maximum m = f 2^e in [2^13, 2^14);
+      // output scale: 2^-12 (matrix) * 2^(e - 14) (column)
+      int e = 0;
+      if (mx > 0.f) frexpf(mx, &e);
+      const float sc = ldexpf(1.0f, 14 - e);
+      const float unscale = ldexpf(1.0f, e - 26);
+#pragma unroll
+      for (int ks = 0; ks < F::KSTEPS; ++ks) {
+        vec bhi, blo;
+#pragma unroll
+        for (int v = 0; v < F::KV; ++v) {
+          _Float16 h, l;
+          split2(xv[i][ks][v] * sc, h, l);
+          bhi[v] = h;
+          blo[v] = l;
+        }
+#pragma unroll
+        for (int m = 0; m < F::MT; ++m) {
+          acc[i][m] = mfma<NP>(ahi[m][ks], bhi, acc[i][m]);
+          acc[i][m] = mfma<NP>(alo[m][ks], bhi, acc[i][m]);
+          // a scaled bf16 input is exact in fp16 down to 2^-14, 2^27 below
+          // the column maximum: its x_lo term is negligible and skipped
+          if constexpr (PRO != PRO_BF16) acc[i][m] = mfma<NP>(ahi[m][ks], blo, acc[i][m]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < F::MT; ++m) acc[i][m] *= unscale;
+    }
+
+    // ---- epilogues ---------------------------------------------------------
+    if constexpr (EPI == EPI_F32 || EPI == EPI_BF16) {
+#pragma unroll
+      for (int m = 0; m < F::MT; ++m)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int k = 16 * m + 4 * g + rr;
+          if (k < N) {
+            const int64_t idx = u * a.out_ustride + obase + k * col_stride + c0 + TPW * t;
+            if constexpr (EPI == EPI_F32) {
+              float* dst = static_cast<float*>(a.out) + idx;
+#pragma unroll
+              for (int i = 0; i < TPW; i += 4)
+                *reinterpret_cast<float4*>(dst + i) =
+                    float4{acc[i][m][rr], acc[i + 1][m][rr], acc[i + 2][m][rr], acc[i + 3][m][rr]};
+            } else {
+              uint16_t* dst = static_cast<uint16_t*>(a.out) + idx;
+#pragma unroll
+              for (int i = 0; i < TPW; i += 4) {
+                const uint32_t lo = bf16_rne_bits(acc[i][m][rr]) |
+                                    (static_cast<uint32_t>(bf16_rne_bits(acc[i + 1][m][rr])) << 16);
+                const uint32_t hi = bf16_rne_bits(acc[i + 2][m][rr]) |
+                                    (static_cast<uint32_t>(bf16_rne_bits(acc[i + 3][m][rr])) << 16);
+                *reinterpret_cast<uint2*>(dst + i) = uint2{lo, hi};
+              }
+            }
+          }
+        }
+    } else if constexpr (EPI == EPI_STATS) {
+      // one wave covers the head_dim channels of one head: TPW == head_dim / 16
+      const float inv_d = 1.0f / static_cast<float>(a.head_dim);
+#pragma unroll
+      for (int m = 0; m < F::MT; ++m)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          float sq = 0.f;
+#pragma unroll
+          for (int i = 0; i < TPW; ++i) sq = fmaf(acc[i][m][rr], acc[i][m][rr], sq);
+#pragma unroll
+          for (int off = 8; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, kWave);
+          const int k = 16 * m + 4 * g + rr;
+          if (t == 0 && k < N) a.var[u * a.var_stride + bin0 + k * bins_per_k] = sq * inv_d;
+        }
+    } else {  // EPI_QUANT
+      uint8_t* r = a.rec.base + u * a.rec.stride;
+      const uint8_t* bits = r + a.rec.off_bits;
+      uint64_t* words = reinterpret_cast<uint64_t*>(r + a.rec.off_codes);
+      const uint32_t* poff = a.plane_off + u * a.n_bins;
+      const float* invg = a.inv_gain + u * a.var_stride;
+      constexpr int HALVES = TPW / 4;                  // 64-channel words per plane
+      float* zt = s_z + (threadIdx.x / kWave) * ZROWS * ZROW;
+#pragma unroll
+      for (int s0 = 0; s0 < NP; s0 += ZROWS) {
+        // bin-major staging: row k - s0 holds the head's 16 * TPW coefficients
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+          for (int m = s0 / 16; m < (s0 + ZROWS) / 16; ++m)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              zt[(16 * m + 4 * g + rr - s0) * ZROW + 16 * i + t] = acc[i][m][rr];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // one bin at a time: uniform bit width, lane j = channel j of a word;
+        // lane j prefetches the bits / first plane / reciprocal gain of bin j
+        const int kend = (s0 + ZROWS < N) ? s0 + ZROWS : N;
+        int bj = 0;
+        int pjlo = 0;
+        float ij = 0.f;
+        if (s0 + lane < kend) {
+          const int64_t bin = bin0 + (s0 + lane) * bins_per_k;
+          bj = bits[bin];
+          const int64_t pj = poff[bin];
+          if (bj > a.max_bits || pj + bj > a.total_bits) bj = 0;
+          pjlo = static_cast<int>(pj);
+          ij = invg[bin];
+        }
+        for (int k = s0; k < kend; ++k) {
+          const int b = __builtin_amdgcn_readlane(bj, k - s0);
+          if (b == 0) continue;
+          const int64_t p0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(pjlo, k - s0));
+          const float inv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ij), k - s0));
+#pragma unroll
+          for (int h = 0; h < HALVES; ++h) {
+            const int code = cell_index_lds(s_thr, zt[(k - s0) * ZROW + 64 * h + lane] * inv, b);
+            for (int q = 0; q < b; ++q) {
+              const uint64_t word = __ballot((code >> q) & 1);
+              if (lane == 0) words[(p0 + q) * HALVES + h] = word;
+            }
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Allocation by exact radix selection.
+// Gains of bin i are key_i - (k-1) * 2^53 (k = 1..bmax) in the bit pattern of
+// the fp64 value var_i * 4^-(k-1); key_i = pattern of (double)var_i, or 0 for
+// var_i == 0.  As (exponent e, mantissa) pairs a gain is (E_i - 2(k-1), M_i).
+// Sweep 1 finds the exponent of the T-th largest gain from a histogram of
+// E_i, sweeps 2-3 find its mantissa (only the top 23 mantissa bits can be
+// non-zero: the values come from fp32), then the final sweep assigns bits,
+// breaking ties at the cut by bin index, and writes the record header and
+// per-bin plane offsets.
+// ---------------------------------------------------------------------------
+constexpr int kAllocThreads = 1024;
+
+__device__ __forceinline__ uint64_t gain_key(float v) {
+  return v > 0.f ? static_cast<uint64_t>(__double_as_longlong(static_cast<double>(v))) : 0ull;
+}
+
+__device__ __forceinline__ int count_ge(uint64_t key, uint64_t tau, int bmax) {
+  if (key == 0) return tau == 0 ? bmax : 0;
+  if (key < tau) return 0;
+  const uint64_t q = ((key - tau) >> 53) + 1;
+  return q > static_cast<uint64_t>(bmax) ? bmax : static_cast<int>(q);
+}
+
+// exclusive scan over the block (thread order), returns total via *total
+__device__ int block_exscan(int v, int* sh, int* total) {
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) sh[w] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int i = 0; i < static_cast<int>(blockDim.x) / kWave; ++i) {
+    if (i < w) before += sh[i];
+    all += sh[i];
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+__device__ int64_t block_sum64(int64_t v, long long* sh) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) sh[threadIdx.x / kWave] = v;
+  __syncthreads();
+  int64_t t = 0;
+  for (int i = 0; i < static_cast<int>(blockDim.x) / kWave; ++i) t += sh[i];
+  return t;
+}
+
+// Largest bucket b of hist[0..nb) with sum_{y >= b} hist[y] >= need; the
+// count strictly above it goes to *above.  nb <= 4 * blockDim.x.
+__device__ void select_bucket(const uint32_t* hist, int nb, int64_t need, int* sh,
+                              int* out_bucket, int64_t* out_above) {
+  const int per = (nb + blockDim.x - 1) / blockDim.x;
+  const int hi = nb - 1 - static_cast<int>(threadIdx.x) * per;
+  int mine = 0;
+  for (int j = 0; j < per; ++j)
+    if (hi - j >= 0) mine += hist[hi - j];
+  int tot;
+  const int before = block_exscan(mine, sh, &tot);
+  __shared__ int s_bucket;
+  __shared__ long long s_above;
+  if (threadIdx.x == 0) {
+    s_bucket = -1;
+    s_above = 0;
+  }
+  __syncthreads();
+  int64_t run = before;
+  for (int j = 0; j < per; ++j) {
+    const int b = hi - j;
+    if (b < 0) break;
+    const int64_t after = run + hist[b];
+    if (run < need && after >= need) {
+      s_bucket = b;
+      s_above = run;
+    }
+    run = after;
+  }
+  __syncthreads();
+  *out_bucket = s_bucket;
+  *out_above = s_above;
+  __syncthreads();
+}
+
+// Calls f(i, v_i) for the bins of one unit, 4 consecutive bins per thread
+// per step (vector loads when the unit's variances are 16-byte aligned).
+template <typename Fn>
+__device__ __forceinline__ void for_bins4(const float* v, int64_t nb, Fn f) {
+  const bool vec = (reinterpret_cast<uintptr_t>(v) & 15) == 0;
+  for (int64_t i0 = 4 * static_cast<int64_t>(threadIdx.x); i0 < nb; i0 += 4 * blockDim.x) {
+    if (vec && i0 + 3 < nb) {
+      const float4 q = *reinterpret_cast<const float4*>(v + i0);
+      f(i0, q.x);
+      f(i0 + 1, q.y);
+      f(i0 + 2, q.z);
+      f(i0 + 3, q.w);
+    } else {
+      for (int j = 0; j < 4; ++j)
+        if (i0 + j < nb) f(i0 + j, v[i0 + j]);
+    }
+  }
+}
+
+// gains of exponent e for a bin with var exponent E (> 0): E = e + 2(k-1)
+__device__ __forceinline__ bool has_gain_at(int E, int e, int bmax) {
+  const int d = E - e;
+  return E > 0 && d >= 0 && (d & 1) == 0 && d / 2 < bmax;
+}
+
+__global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const float* __restrict__ var,
+                                                             int64_t var_stride,
+                                                             uint8_t* __restrict__ bits_out,
+                                                             RecordView rec,
+                                                             uint32_t* __restrict__ plane_off,
+                                                             float* __restrict__ inv_gain) {
+  __shared__ uint32_t hist[4096];
+  __shared__ int sh[kAllocThreads / kWave];
+  __shared__ long long sh64[kAllocThreads / kWave];
+  const int64_t u = blockIdx.x;
+  const float* v = var + u * var_stride;
+  const int bmax = g.max_bits;
+  const int64_t T = g.total_bits;
+  const int64_t nb = g.n_bins;
+
+  uint64_t tau = 0;
+  int64_t need = 0;        // tied gains (== tau) to hand out in bin order
+  int64_t eq_total = 0;    // all gains == tau
+  const bool wf = g.alloc_mode == TACT_ALLOC_WATERFILL && T > 0;
+  if (wf) {
+    // ---- sweep 1: exponent of the T-th largest gain --------------------
+    for (int j = threadIdx.x; j < 4096; j += blockDim.x) hist[j] = 0;
+    __syncthreads();
+    for_bins4(v, nb, [&](int64_t, float x) { atomicAdd(&hist[gain_key(x) >> 52], 1u); });
+    __syncthreads();
+    // gains per exponent e: bins with E in {e, e+2, ..., e+2(bmax-1)} (E > 0);
+    // all bmax gains of zero bins sit at e = 0
+    for (int e = threadIdx.x; e < 2048; e += blockDim.x) {
+      uint32_t c = 0;
+      if (e == 0) {
+        c = hist[0] * static_cast<uint32_t>(bmax);
+      } else {
+        for (int k = 0; k < bmax; ++k) {
+          const int E = e + 2 * k;
+          if (E < 2048) c += hist[E];
+        }
+      }
+      hist[2048 + e] = c;
+    }
+    __syncthreads();
+    int ebin;
+    int64_t above;
+    select_bucket(hist + 2048, 2048, T, sh, &ebin, &above);
+    if (ebin == 0) {
+      tau = 0;
+    } else {
+      // ---- sweep 2: top 12 mantissa bits among gains with exponent ebin --
+      for (int j = threadIdx.x; j < 4096; j += blockDim.x) hist[j] = 0;
+      __syncthreads();
+      for_bins4(v, nb, [&](int64_t, float x) {
+        const uint64_t key = gain_key(x);
+        if (has_gain_at(static_cast<int>(key >> 52), ebin, bmax))
+          atomicAdd(&hist[(key >> 40) & 0xFFF], 1u);
+      });
+      __syncthreads();
+      int b2;
+      int64_t above2;
+      select_bucket(hist, 4096, T - above, sh, &b2, &above2);
+      // ---- sweep 3: next 11 mantissa bits ---------------------------------
+      for (int j = threadIdx.x; j < 4096; j += blockDim.x) hist[j] = 0;
+      __syncthreads();
+      for_bins4(v, nb, [&](int64_t, float x) {
+        const uint64_t key = gain_key(x);
+        if (has_gain_at(static_cast<int>(key >> 52), ebin, bmax) &&
+            static_cast<int>((key >> 40) & 0xFFF) == b2)
+          atomicAdd(&hist[(key >> 29) & 0x7FF], 1u);
+      });
+      __syncthreads();
+      int b3;
+      int64_t above3;
+      select_bucket(hist, 2048, T - above - above2, sh, &b3, &above3);
+      tau = (static_cast<uint64_t>(ebin) << 52) | (static_cast<uint64_t>(b2) << 40) |
+            (static_cast<uint64_t>(b3) << 29);
+    }
+    int64_t gt = 0, eq = 0;
+    for_bins4(v, nb, [&](int64_t, float x) {
+      const uint64_t key = gain_key(x);
+      const int a1 = count_ge(key, tau + 1, bmax);
+      gt += a1;
+      eq += count_ge(key, tau, bmax) - a1;
+    });
+    const int64_t gt_total = block_sum64(gt, sh64);
+    eq_total = block_sum64(eq, sh64);
+    need = T - gt_total;
+  }
+  // ties at the cut need the bin-ordered prefix only when some are left out
+  const bool all_ties = (need == eq_total);
+
+  // ---- final sweep: bits, ties by bin index, header, plane offsets --------
+  uint8_t* bo = bits_out ? bits_out + u * nb : nullptr;
+  uint8_t* r = rec.base ? rec.base + u * rec.stride : nullptr;
+  uint32_t* po = plane_off ? plane_off + u * nb : nullptr;
+  const bool vec = (reinterpret_cast<uintptr_t>(v) & 15) == 0;
+  int64_t tie_carry = 0, plane_carry = 0;
+  for (int64_t base = 0; base < nb; base += 4 * blockDim.x) {
+    const int64_t i0 = base + 4 * static_cast<int64_t>(threadIdx.x);
+    float vi[4] = {0.f, 0.f, 0.f, 0.f};
+    if (vec && i0 + 3 < nb) {
+      const float4 q = *reinterpret_cast<const float4*>(v + i0);
+      vi[0] = q.x; vi[1] = q.y; vi[2] = q.z; vi[3] = q.w;
+    } else {
+      for (int j = 0; j < 4; ++j)
+        if (i0 + j < nb) vi[j] = v[i0 + j];
+    }
+    int b[4] = {0, 0, 0, 0}, eqv[4] = {0, 0, 0, 0};
+    int eq_sum = 0;
+    for (int j = 0; j < 4; ++j) {
+      if (i0 + j >= nb) continue;
+      if (g.alloc_mode == TACT_ALLOC_UNIFORM) {
+        b[j] = g.budget_bits;
+      } else if (wf) {
+        const uint64_t key = gain_key(vi[j]);
+        b[j] = count_ge(key, tau + 1, bmax);
+        eqv[j] = count_ge(key, tau, bmax) - b[j];
+        eq_sum += eqv[j];
+      }
+    }
+    if (wf) {
+      if (all_ties) {
+        for (int j = 0; j < 4; ++j) b[j] += eqv[j];
+      } else {
+        int tot;
+        const int ex = block_exscan(eq_sum, sh, &tot);
+        int64_t before = tie_carry + ex;
+        for (int j = 0; j < 4; ++j) {
+          int64_t avail = need - before;
+          avail = avail < 0 ? 0 : avail;
+          const int take = static_cast<int>(avail < eqv[j] ? avail : eqv[j]);
+          b[j] += take;
+          before += eqv[j];
+        }
+        tie_carry += tot;
+      }
+    }
+    const int bsum = b[0] + b[1] + b[2] + b[3];
+    int ptot;
+    const int pex = block_exscan(bsum, sh, &ptot);
+    int64_t p = plane_carry + pex;
+    for (int j = 0; j < 4; ++j) {
+      const int64_t i = i0 + j;
+      if (i < nb) {
+        if (bo) bo[i] = static_cast<uint8_t>(b[j]);
+        if (po) po[i] = static_cast<uint32_t>(p);
+        const float gn = sqrtf(vi[j]);
+        if (inv_gain) inv_gain[u * var_stride + i] = gn > 0.f ? 1.0f / gn : 0.f;
+        if (r) {
+          reinterpret_cast<float*>(r + g.off_gains)[i] = gn;
+          r[g.off_bits + i] = static_cast<uint8_t>(b[j]);
+          if ((i & 63) == 0) reinterpret_cast<uint32_t*>(r + g.off_groups)[i >> 6] = static_cast<uint32_t>(p);
+        }
+      }
+      p += b[j];
+    }
+    plane_carry += ptot;
+  }
+  if (r) {
+    for (int64_t k = g.off_gains + 4 * nb + threadIdx.x; k < g.off_bits; k += blockDim.x) r[k] = 0;
+    for (int64_t k = g.off_bits + nb + threadIdx.x; k < g.off_groups; k += blockDim.x) r[k] = 0;
+    for (int64_t k = g.off_groups + 4 * g.n_groups + threadIdx.x; k < g.off_codes; k += blockDim.x)
+      r[k] = 0;
+    for (int64_t k = g.off_codes + g.code_bytes + threadIdx.x; k < g.record_bytes; k += blockDim.x)
+      r[k] = 0;
+  }
+}
+
+// Per-bin first plane from a record's bits (decoding side): one block per
+// unit, block scan over the bins.
+__global__ __launch_bounds__(1024) void k_plane_offsets(Geometry g, RecordView rec,
+                                                        uint32_t* __restrict__ plane_off) {
+  __shared__ int sh[1024 / kWave];
+  const int64_t u = blockIdx.x;
+  const uint8_t* bits = rec.base + u * rec.stride + rec.off_bits;
+  uint32_t* po = plane_off + u * g.n_bins;
+  int64_t carry = 0;
+  for (int64_t base = 0; base < g.n_bins; base += 4 * blockDim.x) {
+    const int64_t i0 = base + 4 * static_cast<int64_t>(threadIdx.x);
+    int b[4];
+    for (int j = 0; j < 4; ++j) b[j] = (i0 + j < g.n_bins) ? bits[i0 + j] : 0;
+    int tot;
+    int64_t p = carry + block_exscan(b[0] + b[1] + b[2] + b[3], sh, &tot);
+    for (int j = 0; j < 4; ++j) {
+      if (i0 + j < g.n_bins) po[i0 + j] = static_cast<uint32_t>(p);
+      p += b[j];
+    }
+    carry += tot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch helpers
+// ---------------------------------------------------------------------------
+template <int NP, int PRO, int EPI, int TPW>
+void launch_axis_t(const AxisArgs& a, hipStream_t s) {
+  const int64_t groups = a.inner / (16 * TPW);
+  // about 2048 blocks (8 per CU): each wave walks several column groups so
+  // that the matrix fragments are built once per wave
+  const int64_t rows = a.outer * a.n_units;
+  int64_t gx = (2048 + rows - 1) / rows;
+  const int64_t gmax = (groups + 3) / 4;
+  if (gx > gmax) gx = gmax;
+  if (gx < 1) gx = 1;
+  hipLaunchKernelGGL((k_axis<NP, PRO, EPI, TPW>),
+                     dim3(static_cast<unsigned>(gx), static_cast<unsigned>(a.outer),
+                          static_cast<unsigned>(a.n_units)),
+                     dim3(256), 0, s, a);
+}
+
+template <int NP, int PRO, int EPI>
+void launch_axis_tpw(const AxisArgs& a, int tpw, hipStream_t s) {
+  if (tpw == 4) launch_axis_t<NP, PRO, EPI, 4>(a, s);
+  else if (tpw == 8) launch_axis_t<NP, PRO, EPI, 8>(a, s);
+  else launch_axis_t<NP, PRO, EPI, 16>(a, s);
+}
+
+template <int NP>
+void launch_axis_np(const AxisArgs& a, int pro, int epi, int tpw, hipStream_t s) {
+  if (epi == EPI_STATS) {
+    if (pro == PRO_BF16) launch_axis_tpw<NP, PRO_BF16, EPI_STATS>(a, tpw, s);
+    else launch_axis_tpw<NP, PRO_F32, EPI_STATS>(a, tpw, s);
+  } else if (epi == EPI_QUANT) {
+    if (pro == PRO_BF16) launch_axis_tpw<NP, PRO_BF16, EPI_QUANT>(a, tpw, s);
+    else launch_axis_tpw<NP, PRO_F32, EPI_QUANT>(a, tpw, s);
+  } else if (epi == EPI_F32) {
+    // bf16 rows: 8 elements (16 bytes) per lane when the row holds whole
+    // 128-column groups, else 4
+    if (pro == PRO_BF16 && a.inner % 128 == 0) launch_axis_t<NP, PRO_BF16, EPI_F32, 8>(a, s);
+    else if (pro == PRO_BF16) launch_axis_t<NP, PRO_BF16, EPI_F32, 4>(a, s);
+    else if (pro == PRO_F32) launch_axis_t<NP, PRO_F32, EPI_F32, 4>(a, s);
+    else launch_axis_t<NP, PRO_DEQUANT, EPI_F32, 4>(a, s);
+  } else {
+    if (pro == PRO_F32) launch_axis_t<NP, PRO_F32, EPI_BF16, 4>(a, s);
+    else if (pro == PRO_BF16 && a.inner % 128 == 0) launch_axis_t<NP, PRO_BF16, EPI_BF16, 8>(a, s);
+    else if (pro == PRO_BF16) launch_axis_t<NP, PRO_BF16, EPI_BF16, 4>(a, s);
+    else launch_axis_t<NP, PRO_DEQUANT, EPI_BF16, 4>(a, s);
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// host-facing launchers (declared in tact_internal.h)
+// ---------------------------------------------------------------------------
+void launch_dct_tables(const Geometry& g, float* tab, hipStream_t s) {
+  hipLaunchKernelGGL(k_dct_tables, dim3(3), dim3(256), 0, s, tab, g.S, g.H, g.W);
+}
+
+// axis: 0 = S, 1 = H, 2 = W
+static void axis_shape(const Geometry& g, int axis, int* N, int64_t* outer, int64_t* inner) {
+  const int64_t C = static_cast<int64_t>(g.kv_heads) * g.head_dim;
+  if (axis == 0) {
+    *N = g.S; *outer = 1; *inner = static_cast<int64_t>(g.H) * g.W * C;
+  } else if (axis == 1) {
+    *N = g.H; *outer = g.S; *inner = static_cast<int64_t>(g.W) * C;
+  } else {
+    *N = g.W; *outer = static_cast<int64_t>(g.S) * g.H; *inner = C;
+  }
+}
+
+void launch_axis(const Geometry& g, int64_t n_units, int axis, int inverse, int pro, int epi,
+                 const void* in, int64_t in_stride, void* out, int64_t out_stride,
+                 const float* tab, float* var, const float* inv_gain, int64_t var_stride,
+                 RecordView rec, const uint32_t* plane_off, hipStream_t s) {
+  AxisArgs a;
+  a.in = in;
+  a.in_ustride = in_stride;
+  a.out = out;
+  a.out_ustride = out_stride;
+  a.tab = tab + axis * 4096;
+  a.inverse = inverse;
+  axis_shape(g, axis, &a.N, &a.outer, &a.inner);
+  a.n_units = n_units;
+  a.head_dim = g.head_dim;
+  a.kv_heads = g.kv_heads;
+  a.C = static_cast<int64_t>(g.kv_heads) * g.head_dim;
+  a.n_bins = g.n_bins;
+  a.total_bits = g.total_bits;
+  a.max_bits = g.max_bits;
+  a.var = var;
+  a.inv_gain = inv_gain;
+  a.var_stride = var_stride;
+  a.rec = rec;
+  a.plane_off = plane_off;
+  const int tpw = (epi == EPI_STATS || epi == EPI_QUANT) ? g.head_dim / 16 : 4;
+  if (a.N <= 16) launch_axis_np<16>(a, pro, epi, tpw, s);
+  else if (a.N <= 32) launch_axis_np<32>(a, pro, epi, tpw, s);
+  else launch_axis_np<64>(a, pro, epi, tpw, s);
+}
+
+void launch_allocate2(const Geometry& g, int64_t n_units, const float* var, int64_t var_stride,
+                      uint8_t* bits_out, RecordView rec, uint32_t* plane_off, float* inv_gain,
+                      hipStream_t s) {
+  hipLaunchKernelGGL(k_allocate2, dim3(static_cast<unsigned>(n_units)), dim3(kAllocThreads), 0, s,
+                     g, var, var_stride, bits_out, rec, plane_off, inv_gain);
+}
+
+void launch_plane_offsets(const Geometry& g, int64_t n_units, RecordView rec, uint32_t* plane_off,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(k_plane_offsets, dim3(static_cast<unsigned>(n_units)), dim3(1024), 0, s, g,
+                     rec, plane_off);
+}
+
+}  // namespace tact
