@@ -89,12 +89,16 @@ int64_t elem_size(int dtype) { return dtype == TACT_F32 ? 4 : 2; }
 // fp32 intermediate volume, fp32 variances, fp32 reciprocal gains, uint32
 // per-bin first planes and one record (used by tact_roundtrip when
 // records == NULL).
-int64_t unit_ws_bytes(const Geometry& g) {
-  return align256(4 * g.n_entries) + 3 * align256(4 * g.n_bins) + g.record_bytes;
-}
+// per-bin partial sums of squares: one per 64-channel slab of a head
+int64_t var_parts(const Geometry& g) { return g.head_dim / 64; }
 
-// floats between the variances of consecutive units in the workspace
-int64_t var_stride(const Geometry& g) { return align256(4 * g.n_bins) / 4; }
+// floats between the variances (and reciprocal gains) of consecutive units
+int64_t var_stride(const Geometry& g) { return align256(4 * g.n_bins * var_parts(g)) / 4; }
+
+int64_t unit_ws_bytes(const Geometry& g) {
+  return align256(4 * g.n_entries) + 4 * 2 * var_stride(g) + align256(4 * g.n_bins) +
+         g.record_bytes;
+}
 
 constexpr int64_t kTableBytes = align256(4 * kDctTableFloats);
 
@@ -126,9 +130,9 @@ Workspace carve(const Geometry& g, int64_t chunk, void* ws) {
   w.coef = reinterpret_cast<float*>(b);
   b += chunk * align256(4 * g.n_entries);
   w.var = reinterpret_cast<float*>(b);
-  b += chunk * align256(4 * g.n_bins);
+  b += chunk * 4 * var_stride(g);
   w.invg = reinterpret_cast<float*>(b);
-  b += chunk * align256(4 * g.n_bins);
+  b += chunk * 4 * var_stride(g);
   w.poff = reinterpret_cast<uint32_t*>(b);
   b += chunk * align256(4 * g.n_bins);
   w.recs = b;
@@ -203,10 +207,24 @@ int forward_axes(const Geometry& g, int* ax) {
 // the per-bin variances, then (after the allocation) the codes.
 void compress_chunk(const Geometry& g, int64_t cn, const void* kv, int64_t kv_stride,
                     uint8_t* recs, const Workspace& w, hipStream_t s) {
-  int ax[3];
-  const int m = forward_axes(g, ax);
   const RecordView none{};
   const int in_pro = g.dtype == TACT_BF16 ? AX_PRO_BF16 : AX_PRO_F32;
+  const int64_t vs = var_stride(g);
+  const float inv_d = 1.0f / static_cast<float>(g.head_dim);
+  if (g.axes == TACT_AXES_ALL && plane_supported(g)) {
+    // S on the matrix cores into the fp32 volume, then H and W fused in LDS
+    launch_axis(g, cn, 0, 0, in_pro, AX_EPI_F32, kv, kv_stride, w.coef, g.n_entries, w.tab,
+                nullptr, nullptr, 0, none, nullptr, s);
+    launch_plane(g, cn, 0, w.coef, nullptr, g.n_entries, w.tab, w.var, vs, nullptr, none,
+                 nullptr, s);
+    launch_allocate2(g, cn, w.var, vs, static_cast<int>(var_parts(g)), inv_d, nullptr,
+                     view(g, recs), w.poff, w.invg, s);
+    launch_plane(g, cn, 1, w.coef, nullptr, g.n_entries, w.tab, nullptr, vs, w.invg,
+                 view(g, recs), w.poff, s);
+    return;
+  }
+  int ax[3];
+  const int m = forward_axes(g, ax);
   for (int j = 0; j + 1 < m; ++j) {
     if (j == 0)
       launch_axis(g, cn, ax[j], 0, in_pro, AX_EPI_F32, kv, kv_stride, w.coef, g.n_entries,
@@ -218,12 +236,11 @@ void compress_chunk(const Geometry& g, int64_t cn, const void* kv, int64_t kv_st
   const void* last_in = (m == 1) ? kv : static_cast<const void*>(w.coef);
   const int64_t last_stride = (m == 1) ? kv_stride : g.n_entries;
   const int last_pro = (m == 1) ? in_pro : AX_PRO_F32;
-  const int64_t vs = var_stride(g);
   launch_axis(g, cn, ax[m - 1], 0, last_pro, AX_EPI_STATS, last_in, last_stride, nullptr, 0,
               w.tab, w.var, nullptr, vs, none, nullptr, s);
-  // the variances are consumed by the allocation; their slots then hold
-  // the reciprocal gains for the coding pass
-  launch_allocate2(g, cn, w.var, vs, nullptr, view(g, recs), w.poff, w.invg, s);
+  // the variances are consumed by the allocation, which also leaves the
+  // reciprocal gains for the coding pass
+  launch_allocate2(g, cn, w.var, vs, 1, inv_d, nullptr, view(g, recs), w.poff, w.invg, s);
   launch_axis(g, cn, ax[m - 1], 0, last_pro, AX_EPI_QUANT, last_in, last_stride, nullptr, 0,
               w.tab, nullptr, w.invg, vs, view(g, recs), w.poff, s);
 }
@@ -233,11 +250,18 @@ void compress_chunk(const Geometry& g, int64_t cn, const void* kv, int64_t kv_st
 // one writing the cache.
 void decompress_chunk(const Geometry& g, int64_t cn, const uint8_t* recs, void* out,
                       int64_t out_stride, const Workspace& w, hipStream_t s) {
-  int ax[3];
-  const int m = forward_axes(g, ax);
   const RecordView rv = view(g, const_cast<uint8_t*>(recs));
   const int out_epi = g.dtype == TACT_BF16 ? AX_EPI_BF16 : AX_EPI_F32;
   launch_plane_offsets(g, cn, rv, w.poff, s);
+  if (g.axes == TACT_AXES_ALL && plane_supported(g)) {
+    launch_plane(g, cn, 2, nullptr, w.coef, g.n_entries, w.tab, nullptr, 0, nullptr, rv,
+                 w.poff, s);
+    launch_axis(g, cn, 0, 1, AX_PRO_F32, out_epi, w.coef, g.n_entries, out, out_stride, w.tab,
+                nullptr, nullptr, 0, rv, w.poff, s);
+    return;
+  }
+  int ax[3];
+  const int m = forward_axes(g, ax);
   for (int j = m - 1; j >= 0; --j) {
     const bool first = (j == m - 1), last = (j == 0);
     const int pro = first ? AX_PRO_DEQUANT : AX_PRO_F32;
@@ -451,7 +475,7 @@ tact_status tact_dbg_allocate(const tact_params* p, int64_t n_units, const float
   if ((st = check_buffer(var, "var", 4)) != TACT_OK) return st;
   if ((st = check_buffer(bits, "bits", 1)) != TACT_OK) return st;
   RecordView none{};
-  launch_allocate2(g, n_units, var, g.n_bins, bits, none, nullptr, nullptr, stream);
+  launch_allocate2(g, n_units, var, g.n_bins, 1, 1.0f, bits, none, nullptr, nullptr, stream);
   return after_launch("tact_dbg_allocate");
 }
 

@@ -88,9 +88,18 @@ void launch_axis(const Geometry& g, int64_t n_units, int axis, int inverse, int 
 
 // Allocation by exact radix selection; writes bits_out and/or the record
 // header, and per-bin first planes into plane_off (each may be null).
+// var holds `parts` partial sums per bin (consecutive), scaled by var_scale.
 void launch_allocate2(const Geometry& g, int64_t n_units, const float* var, int64_t var_stride,
-                      uint8_t* bits_out, RecordView rec, uint32_t* plane_off, float* inv_gain,
-                      hipStream_t stream);
+                      int parts, float var_scale, uint8_t* bits_out, RecordView rec,
+                      uint32_t* plane_off, float* inv_gain, hipStream_t stream);
+
+// Fused H and W axes (see tact_mfma.hip); mode 0 = variance partial sums,
+// 1 = quantize + pack, 2 = decode + inverse.
+bool plane_supported(const Geometry& g);
+void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in, float* out,
+                  int64_t ustride, const float* tab, float* var_part, int64_t var_stride,
+                  const float* inv_gain, RecordView rec, const uint32_t* plane_off,
+                  hipStream_t stream);
 
 // Per-bin first planes from the bits stored in records.
 void launch_plane_offsets(const Geometry& g, int64_t n_units, RecordView rec,

@@ -403,8 +403,8 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
           }
         }
     } else if constexpr (EPI == EPI_STATS) {
-      // one wave covers the head_dim channels of one head: TPW == head_dim / 16
-      const float inv_d = 1.0f / static_cast<float>(a.head_dim);
+      // one wave covers the head_dim channels of one head: TPW == head_dim / 16;
+      // raw sum of squares (the allocation applies 1/head_dim)
 #pragma unroll
       for (int m = 0; m < F::MT; ++m)
 #pragma unroll
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
 #pragma unroll
           for (int off = 8; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, kWave);
           const int k = 16 * m + 4 * g + rr;
-          if (t == 0 && k < N) a.var[u * a.var_stride + bin0 + k * bins_per_k] = sq * inv_d;
+          if (t == 0 && k < N) a.var[u * a.var_stride + bin0 + k * bins_per_k] = sq;
         }
     } else {  // EPI_QUANT
       uint8_t* r = a.rec.base + u * a.rec.stride;
@@ -469,6 +469,347 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_plane: the H and W axes of one (unit, slice s, 64-channel slab) in one
+// block.  The H x W x 64 plane lives in LDS between the two contractions,
+// so the fp32 volume crosses HBM once per direction instead of twice.
+//   forward (MODE_STATS / MODE_QUANT): H from global memory into LDS, then
+//     W from LDS with the variance epilogue (per-slab partial sums of
+//     squares) or the quantize + pack epilogue (one 64-bit code word per
+//     plane per bin: the slab is one word wide);
+//   inverse (MODE_DEQUANT): decode + inverse W into LDS, then inverse H
+//     to global memory.
+// 8 waves; a wave owns whole rows of the plane (one w in the first
+// contraction, one kh in the second), so its LDS rows need no barrier
+// beyond the one between the two contractions.
+// ---------------------------------------------------------------------------
+enum PlaneMode { MODE_STATS = 0, MODE_QUANT = 1, MODE_DEQUANT = 2 };
+
+struct PlaneArgs {
+  const float* in;           // forward: the volume after the S axis; unused inverse
+  float* out;                // inverse: the volume before the inverse S axis
+  int64_t ustride;           // elements between units of in / out
+  const float* tab;          // tab[3][64][64]
+  int S, H, W;
+  int64_t C;                 // kv_heads * head_dim
+  int head_dim, kv_heads;
+  int64_t n_bins, total_bits;
+  int max_bits;
+  float* var_part;           // MODE_STATS: raw sums of squares, [u][bin][part]
+  int parts;                 // head_dim / 64
+  int64_t var_stride;        // floats per unit in var_part / inv_gain
+  const float* inv_gain;     // MODE_QUANT
+  RecordView rec;
+  const uint32_t* plane_off;
+};
+
+template <int NP>
+__device__ __forceinline__ void load_afrag(const float* tab, int inverse, int t, int g,
+                                           typename Frag<NP>::vec (&ahi)[Frag<NP>::MT][Frag<NP>::KSTEPS],
+                                           typename Frag<NP>::vec (&alo)[Frag<NP>::MT][Frag<NP>::KSTEPS]) {
+  using F = Frag<NP>;
+#pragma unroll
+  for (int m = 0; m < F::MT; ++m)
+#pragma unroll
+    for (int ks = 0; ks < F::KSTEPS; ++ks)
+#pragma unroll
+      for (int v = 0; v < F::KV; ++v) {
+        const int row = 16 * m + t;
+        const int col = ks * F::KPER + F::KV * g + v;
+        const float c = kMatScale * (inverse ? tab[col * 64 + row] : tab[row * 64 + col]);
+        _Float16 h, l;
+        split2(c, h, l);
+        ahi[m][ks][v] = h;
+        alo[m][ks][v] = l;
+      }
+}
+
+// acc[i][m] += A * B for 4 interleaved column tiles whose K values are
+// xv[i][ks][v]; per-column power-of-two scaling, 3-term split products.
+template <int NP>
+__device__ __forceinline__ void contract4(const typename Frag<NP>::vec (&ahi)[Frag<NP>::MT][Frag<NP>::KSTEPS],
+                                          const typename Frag<NP>::vec (&alo)[Frag<NP>::MT][Frag<NP>::KSTEPS],
+                                          float (&xv)[4][Frag<NP>::KSTEPS][Frag<NP>::KV],
+                                          f32x4 (&acc)[4][Frag<NP>::MT]) {
+  using F = Frag<NP>;
+  using vec = typename F::vec;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int m = 0; m < F::MT; ++m) acc[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float mx = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < F::KSTEPS; ++ks)
+#pragma unroll
+      for (int v = 0; v < F::KV; ++v) mx = fmaxf(mx, fabsf(xv[i][ks][v]));
+    mx = column_max(mx);
+    int e = 0;
+    if (mx > 0.f) frexpf(mx, &e);
+    const float sc = ldexpf(1.0f, 14 - e);
+    const float unscale = ldexpf(1.0f, e - 26);
+#pragma unroll
+    for (int ks = 0; ks < F::KSTEPS; ++ks) {
+      vec bhi, blo;
+#pragma unroll
+      for (int v = 0; v < F::KV; ++v) {
+        _Float16 h, l;
+        split2(xv[i][ks][v] * sc, h, l);
+        bhi[v] = h;
+        blo[v] = l;
+      }
+#pragma unroll
+      for (int m = 0; m < F::MT; ++m) {
+        acc[i][m] = mfma<NP>(ahi[m][ks], bhi, acc[i][m]);
+        acc[i][m] = mfma<NP>(alo[m][ks], bhi, acc[i][m]);
+        acc[i][m] = mfma<NP>(ahi[m][ks], blo, acc[i][m]);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < F::MT; ++m) acc[i][m] *= unscale;
+  }
+}
+
+constexpr int kPlaneWaves = 8;
+
+template <int NPH, int NPW, int MODE>
+__global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
+  using FH = Frag<NPH>;
+  using FW = Frag<NPW>;
+  extern __shared__ float plane[];          // [H][W][64] fp32
+  __shared__ float s_cb[(MODE == MODE_QUANT) ? TACT_CODEBOOK_THRESHOLDS
+                                             : (MODE == MODE_DEQUANT ? TACT_CODEBOOK_LEVELS : 1)];
+  const int lane = threadIdx.x % kWave;
+  const int wv = threadIdx.x / kWave;
+  const int t = lane % 16, g = lane / 16;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int s = blockIdx.y;
+  const int64_t u = blockIdx.z;
+  const int H = a.H, W = a.W;
+  const int64_t head = c0 / a.head_dim;
+  const int half = static_cast<int>((c0 % a.head_dim) / 64);
+  if constexpr (MODE == MODE_QUANT)
+    for (int j = threadIdx.x; j < TACT_CODEBOOK_THRESHOLDS; j += blockDim.x) s_cb[j] = c_thresholds[j];
+  if constexpr (MODE == MODE_DEQUANT)
+    for (int j = threadIdx.x; j < TACT_CODEBOOK_LEVELS; j += blockDim.x) s_cb[j] = c_levels[j];
+  // bin of (s, kh, kw) for this slab's head
+  auto bin_of3 = [&](int kh, int kw) -> int64_t {
+    return ((static_cast<int64_t>(s) * H + kh) * W + kw) * a.kv_heads + head;
+  };
+  const int64_t vol = u * a.ustride + static_cast<int64_t>(s) * H * W * a.C;   // (s, 0, 0, 0)
+
+  if constexpr (MODE != MODE_DEQUANT) {
+    // ---- H axis: global -> LDS; a wave owns the columns of one w --------
+    typename FH::vec ahi[FH::MT][FH::KSTEPS], alo[FH::MT][FH::KSTEPS];
+    load_afrag<NPH>(a.tab + 1 * 4096, 0, t, g, ahi, alo);
+    for (int w = wv; w < W; w += kPlaneWaves) {
+      float xv[4][FH::KSTEPS][FH::KV];
+#pragma unroll
+      for (int ks = 0; ks < FH::KSTEPS; ++ks)
+#pragma unroll
+        for (int v = 0; v < FH::KV; ++v) {
+          const int h = ks * FH::KPER + FH::KV * g + v;
+          float4 q = float4{0.f, 0.f, 0.f, 0.f};
+          if (h < H) q = *reinterpret_cast<const float4*>(a.in + vol + (static_cast<int64_t>(h) * W + w) * a.C + c0 + 4 * t);
+          xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
+        }
+      f32x4 acc[4][FH::MT];
+      contract4<NPH>(ahi, alo, xv, acc);
+#pragma unroll
+      for (int m = 0; m < FH::MT; ++m)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int kh = 16 * m + 4 * g + rr;
+          if (kh < H)
+            *reinterpret_cast<float4*>(plane + (kh * W + w) * 64 + 4 * t) =
+                float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]};
+        }
+    }
+    __syncthreads();
+    // ---- W axis: LDS -> epilogue; a wave owns the columns of one kh ------
+    typename FW::vec bhi_w[FW::MT][FW::KSTEPS], blo_w[FW::MT][FW::KSTEPS];
+    load_afrag<NPW>(a.tab + 2 * 4096, 0, t, g, bhi_w, blo_w);
+    for (int kh = wv; kh < H; kh += kPlaneWaves) {
+      float xv[4][FW::KSTEPS][FW::KV];
+#pragma unroll
+      for (int ks = 0; ks < FW::KSTEPS; ++ks)
+#pragma unroll
+        for (int v = 0; v < FW::KV; ++v) {
+          const int w = ks * FW::KPER + FW::KV * g + v;
+          float4 q = float4{0.f, 0.f, 0.f, 0.f};
+          if (w < W) q = *reinterpret_cast<const float4*>(plane + (kh * W + w) * 64 + 4 * t);
+          xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
+        }
+      f32x4 acc[4][FW::MT];
+      contract4<NPW>(bhi_w, blo_w, xv, acc);
+      if constexpr (MODE == MODE_STATS) {
+#pragma unroll
+        for (int m = 0; m < FW::MT; ++m)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            float sq = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sq = fmaf(acc[i][m][rr], acc[i][m][rr], sq);
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, kWave);
+            const int kw = 16 * m + 4 * g + rr;
+            if (t == 0 && kw < W)
+              a.var_part[u * a.var_stride + bin_of3(kh, kw) * a.parts + half] = sq;
+          }
+      } else {
+        // stage the coefficients bin-major in this wave's own plane row
+        // (row kh is read only by this wave), then one bin at a time
+        float* zt = plane + static_cast<int64_t>(kh) * W * 64;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int m = 0; m < FW::MT; ++m)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int kw = 16 * m + 4 * g + rr;
+            if (kw < W)
+              *reinterpret_cast<float4*>(zt + kw * 64 + 4 * t) =
+                  float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]};
+          }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        uint8_t* r = a.rec.base + u * a.rec.stride;
+        const uint8_t* bits = r + a.rec.off_bits;
+        uint64_t* words = reinterpret_cast<uint64_t*>(r + a.rec.off_codes);
+        const uint32_t* poff = a.plane_off + u * a.n_bins;
+        const float* invg = a.inv_gain + u * a.var_stride;
+        const int wpp = a.head_dim / 64;
+        int bj = 0, pjlo = 0;
+        float ij = 0.f;
+        if (lane < W) {
+          const int64_t bin = bin_of3(kh, lane);
+          bj = bits[bin];
+          const int64_t pj = poff[bin];
+          if (bj > a.max_bits || pj + bj > a.total_bits) bj = 0;
+          pjlo = static_cast<int>(pj);
+          ij = invg[bin];
+        }
+        for (int kw = 0; kw < W; ++kw) {
+          const int b = __builtin_amdgcn_readlane(bj, kw);
+          if (b == 0) continue;
+          const int64_t p0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(pjlo, kw));
+          const float inv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ij), kw));
+          const int code = cell_index_lds(s_cb, zt[kw * 64 + lane] * inv, b);
+          for (int q = 0; q < b; ++q) {
+            const uint64_t word = __ballot((code >> q) & 1);
+            if (lane == 0) words[(p0 + q) * wpp + half] = word;
+          }
+        }
+      }
+    }
+  } else {
+    // ---- inverse W: decode bins into LDS, contract; a wave owns one kh ----
+    __syncthreads();                         // codebook in LDS
+    typename FW::vec ahi_w[FW::MT][FW::KSTEPS], alo_w[FW::MT][FW::KSTEPS];
+    load_afrag<NPW>(a.tab + 2 * 4096, 1, t, g, ahi_w, alo_w);
+    const uint8_t* r = a.rec.base + u * a.rec.stride;
+    const uint8_t* bits = r + a.rec.off_bits;
+    const float* gains = reinterpret_cast<const float*>(r + a.rec.off_gains);
+    const uint64_t* words = reinterpret_cast<const uint64_t*>(r + a.rec.off_codes);
+    const uint32_t* poff = a.plane_off + u * a.n_bins;
+    const int wpp = a.head_dim / 64;
+    for (int kh = wv; kh < H; kh += kPlaneWaves) {
+      float* row = plane + static_cast<int64_t>(kh) * W * 64;
+      int bj = 0;
+      float gj = 0.f;
+      uint32_t wlo[8], whi[8];
+      {
+        int64_t pj = 0;
+        if (lane < W) {
+          const int64_t bin = bin_of3(kh, lane);
+          bj = bits[bin];
+          pj = poff[bin];
+          gj = gains[bin];
+          if (bj > a.max_bits || pj + bj > a.total_bits) bj = 0;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          uint64_t w = 0;
+          if (q < bj) w = words[(pj + q) * wpp + half];
+          wlo[q] = static_cast<uint32_t>(w);
+          whi[q] = static_cast<uint32_t>(w >> 32);
+        }
+      }
+      for (int kw = 0; kw < W; ++kw) {
+        const int b = __builtin_amdgcn_readlane(bj, kw);
+        float x = 0.f;
+        if (b > 0) {
+          int code = 0;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            if (q < b) {
+              const uint32_t lo = __builtin_amdgcn_readlane(wlo[q], kw);
+              const uint32_t hi = __builtin_amdgcn_readlane(whi[q], kw);
+              code |= static_cast<int>(((lane < 32 ? lo : hi) >> (lane & 31)) & 1u) << q;
+            }
+          }
+          x = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gj), kw)) *
+              s_cb[(1 << b) - 2 + code];
+        }
+        row[kw * 64 + lane] = x;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float xv[4][FW::KSTEPS][FW::KV];
+#pragma unroll
+      for (int ks = 0; ks < FW::KSTEPS; ++ks)
+#pragma unroll
+        for (int v = 0; v < FW::KV; ++v) {
+          const int kw = ks * FW::KPER + FW::KV * g + v;
+          float4 q = float4{0.f, 0.f, 0.f, 0.f};
+          if (kw < W) q = *reinterpret_cast<const float4*>(row + kw * 64 + 4 * t);
+          xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
+        }
+      f32x4 acc[4][FW::MT];
+      contract4<NPW>(ahi_w, alo_w, xv, acc);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int m = 0; m < FW::MT; ++m)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int w = 16 * m + 4 * g + rr;
+          if (w < W)
+            *reinterpret_cast<float4*>(row + w * 64 + 4 * t) =
+                float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]};
+        }
+    }
+    __syncthreads();
+    // ---- inverse H: LDS -> global; a wave owns the columns of one w -------
+    typename FH::vec ahi_h[FH::MT][FH::KSTEPS], alo_h[FH::MT][FH::KSTEPS];
+    load_afrag<NPH>(a.tab + 1 * 4096, 1, t, g, ahi_h, alo_h);
+    for (int w = wv; w < W; w += kPlaneWaves) {
+      float xv[4][FH::KSTEPS][FH::KV];
+#pragma unroll
+      for (int ks = 0; ks < FH::KSTEPS; ++ks)
+#pragma unroll
+        for (int v = 0; v < FH::KV; ++v) {
+          const int kh = ks * FH::KPER + FH::KV * g + v;
+          float4 q = float4{0.f, 0.f, 0.f, 0.f};
+          if (kh < H) q = *reinterpret_cast<const float4*>(plane + (kh * W + w) * 64 + 4 * t);
+          xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
+        }
+      f32x4 acc[4][FH::MT];
+      contract4<NPH>(ahi_h, alo_h, xv, acc);
+#pragma unroll
+      for (int m = 0; m < FH::MT; ++m)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int h = 16 * m + 4 * g + rr;
+          if (h < H)
+            *reinterpret_cast<float4*>(a.out + vol + (static_cast<int64_t>(h) * W + w) * a.C + c0 + 4 * t) =
+                float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]};
+        }
     }
   }
 }
@@ -564,22 +905,50 @@ __device__ void select_bucket(const uint32_t* hist, int nb, int64_t need, int* s
   __syncthreads();
 }
 
+// The variance of bins i0..i0+3: (sum of the `parts` partial sums, added in
+// part order) * scale.  Partials of a bin are consecutive.
+__device__ __forceinline__ void var4(const float* v, int64_t nb, int parts, float scale,
+                                     bool vec, int64_t i0, float (&out)[4]) {
+  if (vec && i0 + 3 < nb) {
+    if (parts == 1) {
+      const float4 q = *reinterpret_cast<const float4*>(v + i0);
+      out[0] = q.x; out[1] = q.y; out[2] = q.z; out[3] = q.w;
+    } else if (parts == 2) {
+      const float4 q0 = *reinterpret_cast<const float4*>(v + 2 * i0);
+      const float4 q1 = *reinterpret_cast<const float4*>(v + 2 * i0 + 4);
+      out[0] = q0.x + q0.y; out[1] = q0.z + q0.w; out[2] = q1.x + q1.y; out[3] = q1.z + q1.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 q = *reinterpret_cast<const float4*>(v + 4 * (i0 + j));
+        out[j] = ((q.x + q.y) + q.z) + q.w;
+      }
+    }
+  } else {
+    for (int j = 0; j < 4; ++j) {
+      float acc = 0.f;
+      if (i0 + j < nb) {
+        acc = v[(i0 + j) * parts];
+        for (int p = 1; p < parts; ++p) acc += v[(i0 + j) * parts + p];
+      }
+      out[j] = acc;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[j] *= scale;
+}
+
 // Calls f(i, v_i) for the bins of one unit, 4 consecutive bins per thread
-// per step (vector loads when the unit's variances are 16-byte aligned).
+// per step.
 template <typename Fn>
-__device__ __forceinline__ void for_bins4(const float* v, int64_t nb, Fn f) {
+__device__ __forceinline__ void for_bins4(const float* v, int64_t nb, int parts, float scale,
+                                          Fn f) {
   const bool vec = (reinterpret_cast<uintptr_t>(v) & 15) == 0;
   for (int64_t i0 = 4 * static_cast<int64_t>(threadIdx.x); i0 < nb; i0 += 4 * blockDim.x) {
-    if (vec && i0 + 3 < nb) {
-      const float4 q = *reinterpret_cast<const float4*>(v + i0);
-      f(i0, q.x);
-      f(i0 + 1, q.y);
-      f(i0 + 2, q.z);
-      f(i0 + 3, q.w);
-    } else {
-      for (int j = 0; j < 4; ++j)
-        if (i0 + j < nb) f(i0 + j, v[i0 + j]);
-    }
+    float q[4];
+    var4(v, nb, parts, scale, vec, i0, q);
+    for (int j = 0; j < 4; ++j)
+      if (i0 + j < nb) f(i0 + j, q[j]);
   }
 }
 
@@ -594,7 +963,8 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
                                                              uint8_t* __restrict__ bits_out,
                                                              RecordView rec,
                                                              uint32_t* __restrict__ plane_off,
-                                                             float* __restrict__ inv_gain) {
+                                                             float* __restrict__ inv_gain,
+                                                             int parts, float var_scale) {
   __shared__ uint32_t hist[4096];
   __shared__ int sh[kAllocThreads / kWave];
   __shared__ long long sh64[kAllocThreads / kWave];
@@ -612,7 +982,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
     // ---- sweep 1: exponent of the T-th largest gain --------------------
     for (int j = threadIdx.x; j < 4096; j += blockDim.x) hist[j] = 0;
     __syncthreads();
-    for_bins4(v, nb, [&](int64_t, float x) { atomicAdd(&hist[gain_key(x) >> 52], 1u); });
+    for_bins4(v, nb, parts, var_scale, [&](int64_t, float x) { atomicAdd(&hist[gain_key(x) >> 52], 1u); });
     __syncthreads();
     // gains per exponent e: bins with E in {e, e+2, ..., e+2(bmax-1)} (E > 0);
     // all bmax gains of zero bins sit at e = 0
@@ -638,7 +1008,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
       // ---- sweep 2: top 12 mantissa bits among gains with exponent ebin --
       for (int j = threadIdx.x; j < 4096; j += blockDim.x) hist[j] = 0;
       __syncthreads();
-      for_bins4(v, nb, [&](int64_t, float x) {
+      for_bins4(v, nb, parts, var_scale, [&](int64_t, float x) {
         const uint64_t key = gain_key(x);
         if (has_gain_at(static_cast<int>(key >> 52), ebin, bmax))
           atomicAdd(&hist[(key >> 40) & 0xFFF], 1u);
@@ -650,7 +1020,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
       // ---- sweep 3: next 11 mantissa bits ---------------------------------
       for (int j = threadIdx.x; j < 4096; j += blockDim.x) hist[j] = 0;
       __syncthreads();
-      for_bins4(v, nb, [&](int64_t, float x) {
+      for_bins4(v, nb, parts, var_scale, [&](int64_t, float x) {
         const uint64_t key = gain_key(x);
         if (has_gain_at(static_cast<int>(key >> 52), ebin, bmax) &&
             static_cast<int>((key >> 40) & 0xFFF) == b2)
@@ -664,7 +1034,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
             (static_cast<uint64_t>(b3) << 29);
     }
     int64_t gt = 0, eq = 0;
-    for_bins4(v, nb, [&](int64_t, float x) {
+    for_bins4(v, nb, parts, var_scale, [&](int64_t, float x) {
       const uint64_t key = gain_key(x);
       const int a1 = count_ge(key, tau + 1, bmax);
       gt += a1;
@@ -685,14 +1055,8 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
   int64_t tie_carry = 0, plane_carry = 0;
   for (int64_t base = 0; base < nb; base += 4 * blockDim.x) {
     const int64_t i0 = base + 4 * static_cast<int64_t>(threadIdx.x);
-    float vi[4] = {0.f, 0.f, 0.f, 0.f};
-    if (vec && i0 + 3 < nb) {
-      const float4 q = *reinterpret_cast<const float4*>(v + i0);
-      vi[0] = q.x; vi[1] = q.y; vi[2] = q.z; vi[3] = q.w;
-    } else {
-      for (int j = 0; j < 4; ++j)
-        if (i0 + j < nb) vi[j] = v[i0 + j];
-    }
+    float vi[4];
+    var4(v, nb, parts, var_scale, vec, i0, vi);
     int b[4] = {0, 0, 0, 0}, eqv[4] = {0, 0, 0, 0};
     int eq_sum = 0;
     for (int j = 0; j < 4; ++j) {
@@ -877,11 +1241,66 @@ void launch_axis(const Geometry& g, int64_t n_units, int axis, int inverse, int 
   else launch_axis_np<64>(a, pro, epi, tpw, s);
 }
 
+
+bool plane_supported(const Geometry& g) {
+  return (g.axes & 6) == 6 && g.H <= 32 && g.W <= 32 &&
+         static_cast<int64_t>(g.H) * g.W * 64 * 4 <= 150 * 1024;
+}
+
+void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in, float* out,
+                  int64_t ustride, const float* tab, float* var_part, int64_t var_stride,
+                  const float* inv_gain, RecordView rec, const uint32_t* plane_off, hipStream_t s) {
+  PlaneArgs a;
+  a.in = in;
+  a.out = out;
+  a.ustride = ustride;
+  a.tab = tab;
+  a.S = g.S;
+  a.H = g.H;
+  a.W = g.W;
+  a.C = static_cast<int64_t>(g.kv_heads) * g.head_dim;
+  a.head_dim = g.head_dim;
+  a.kv_heads = g.kv_heads;
+  a.n_bins = g.n_bins;
+  a.total_bits = g.total_bits;
+  a.max_bits = g.max_bits;
+  a.var_part = var_part;
+  a.parts = g.head_dim / 64;
+  a.var_stride = var_stride;
+  a.inv_gain = inv_gain;
+  a.rec = rec;
+  a.plane_off = plane_off;
+  const dim3 grid(static_cast<unsigned>(a.C / 64), static_cast<unsigned>(g.S),
+                  static_cast<unsigned>(n_units));
+  const dim3 block(64 * kPlaneWaves);
+  const size_t lds = static_cast<size_t>(g.H) * g.W * 64 * sizeof(float);
+  const bool h16 = g.H <= 16, w16 = g.W <= 16;
+  // the plane needs more dynamic LDS than the default limit
+#define TACT_PLANE_ONE(NH, NW, M)                                                               \
+  do {                                                                                          \
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_plane<NH, NW, M>),                \
+                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));     \
+    hipLaunchKernelGGL((k_plane<NH, NW, M>), grid, block, lds, s, a);                           \
+  } while (0)
+#define TACT_PLANE(NH, NW)                                                                      \
+  do {                                                                                          \
+    if (mode == MODE_STATS) TACT_PLANE_ONE(NH, NW, MODE_STATS);                                 \
+    else if (mode == MODE_QUANT) TACT_PLANE_ONE(NH, NW, MODE_QUANT);                            \
+    else TACT_PLANE_ONE(NH, NW, MODE_DEQUANT);                                                  \
+  } while (0)
+  if (h16 && w16) TACT_PLANE(16, 16);
+  else if (h16) TACT_PLANE(16, 32);
+  else if (w16) TACT_PLANE(32, 16);
+  else TACT_PLANE(32, 32);
+#undef TACT_PLANE
+#undef TACT_PLANE_ONE
+}
+
 void launch_allocate2(const Geometry& g, int64_t n_units, const float* var, int64_t var_stride,
-                      uint8_t* bits_out, RecordView rec, uint32_t* plane_off, float* inv_gain,
-                      hipStream_t s) {
+                      int parts, float var_scale, uint8_t* bits_out, RecordView rec,
+                      uint32_t* plane_off, float* inv_gain, hipStream_t s) {
   hipLaunchKernelGGL(k_allocate2, dim3(static_cast<unsigned>(n_units)), dim3(kAllocThreads), 0, s,
-                     g, var, var_stride, bits_out, rec, plane_off, inv_gain);
+                     g, var, var_stride, bits_out, rec, plane_off, inv_gain, parts, var_scale);
 }
 
 void launch_plane_offsets(const Geometry& g, int64_t n_units, RecordView rec, uint32_t* plane_off,
