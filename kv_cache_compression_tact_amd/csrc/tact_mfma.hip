@@ -483,7 +483,7 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
 //     plane per bin: the slab is one word wide);
 //   inverse (MODE_DEQUANT): decode + inverse W into LDS, then inverse H
 //     to global memory.
-// 8 waves; a wave owns whole rows of the plane (one w in the first
+// 16 waves; a wave owns whole rows of the plane (one w in the first
 // contraction, one kh in the second), so its LDS rows need no barrier
 // beyond the one between the two contractions.
 // ---------------------------------------------------------------------------
@@ -573,7 +573,7 @@ __device__ __forceinline__ void contract4(const typename Frag<NP>::vec (&ahi)[Fr
   }
 }
 
-constexpr int kPlaneWaves = 8;
+constexpr int kPlaneWaves = 16;
 
 template <int NPH, int NPW, int MODE>
 __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
@@ -739,6 +739,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
           whi[q] = static_cast<uint32_t>(w >> 32);
         }
       }
+#pragma unroll 4
       for (int kw = 0; kw < W; ++kw) {
         const int b = __builtin_amdgcn_readlane(bj, kw);
         float x = 0.f;
