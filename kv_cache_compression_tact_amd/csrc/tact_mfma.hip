@@ -739,7 +739,6 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
           whi[q] = static_cast<uint32_t>(w >> 32);
         }
       }
-#pragma unroll 4
       for (int kw = 0; kw < W; ++kw) {
         const int b = __builtin_amdgcn_readlane(bj, kw);
         float x = 0.f;
