@@ -49,7 +49,7 @@ from scipy.special import erfc
 __all__ = [
     "Params", "dct2_matrix", "dct3_forward", "dct3_inverse", "bin_variance",
     "total_bits", "waterfill_theta", "waterfill_rates", "round_bits",
-    "greedy_correct", "allocate_bits", "allocate_bits_by_sorting",
+    "greedy_correct", "allocate_bits", "allocate_bits_by_sorting", "allocate_uniform",
     "lloyd_max", "codebook_f32", "gains_f32", "quantize", "dequantize",
     "record_layout", "pack_record", "unpack_record", "round_to_bf16",
     "bf16_bits", "compress", "decompress", "roundtrip", "mse",
@@ -549,12 +549,25 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Whole codec                                          [Method/1-4], [Method/dec]
 # --------------------------------------------------------------------------
-def compress(x: np.ndarray, p: Params, axes=(0, 1, 2)) -> np.ndarray:
-    """One unit: transform, variances, allocation, quantization, record."""
+def allocate_uniform(var: np.ndarray, budget_bits: int) -> np.ndarray:
+    """Every bin gets the average budget: the page's "uniform allocation"
+    comparison ("Main Findings", transform and allocation ablation)."""
+    return np.full(np.asarray(var).size, int(budget_bits), dtype=np.int64)
+
+
+def compress(x: np.ndarray, p: Params, axes=(0, 1, 2), alloc: str = "waterfill") -> np.ndarray:
+    """One unit: transform, variances, allocation, quantization, record.
+
+    ``axes`` and ``alloc`` ("waterfill" or "uniform") select the page's
+    ablations; the method is all three axes with water-filling.
+    """
     x = np.asarray(x, dtype=np.float64).reshape(p.shape)
     coef = dct3_forward(x, axes)
     var = bin_variance(coef)
-    bits = allocate_bits(var, total_bits(p), p.max_bits).reshape(var.shape)
+    if alloc == "uniform":
+        bits = allocate_uniform(var, p.budget_bits).reshape(var.shape)
+    else:
+        bits = allocate_bits(var, total_bits(p), p.max_bits).reshape(var.shape)
     g = gains_f32(var)
     codes = quantize(coef, g, bits)
     return pack_record(codes, g, bits, p)
@@ -576,9 +589,10 @@ def decompress(rec: np.ndarray, p: Params, out_dtype="bf16",
     return xr
 
 
-def roundtrip(x: np.ndarray, p: Params, out_dtype="bf16"):
-    rec = compress(x, p)
-    return decompress(rec, p, out_dtype), rec
+def roundtrip(x: np.ndarray, p: Params, out_dtype="bf16", axes=(0, 1, 2),
+              alloc: str = "waterfill"):
+    rec = compress(x, p, axes, alloc)
+    return decompress(rec, p, out_dtype, axes), rec
 
 
 # --------------------------------------------------------------------------

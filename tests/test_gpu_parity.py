@@ -272,21 +272,24 @@ def test_compress_end_to_end(geo):
 
 def _roundtrip_check(x_gpu, g, units=None):
     op = _oparams(g)
-    out, rec = tact.roundtrip(x_gpu, g.budget_bits, g.max_bits)
+    axes = tuple(a for a in range(3) if g.axes & (1 << a))
+    alloc = "uniform" if g.alloc_mode == tact.ALLOC_UNIFORM else "waterfill"
+    out, rec = tact.roundtrip(x_gpu, g.budget_bits, g.max_bits, axes=g.axes,
+                              alloc_mode=g.alloc_mode)
     units = range(x_gpu.shape[0]) if units is None else units
     for u in units:
         xs = x_gpu[u].float().cpu().numpy().astype(np.float64)
         c = tact.dbg_dct3(x_gpu[u:u + 1], g).cpu().numpy()[0]
-        e = _rel(c, O.dct3_forward(xs))
+        e = _rel(c, O.dct3_forward(xs, axes))
         say(f"  unit {u}: forward rel err {e:.3e}")
         assert e <= 1e-5
         od = "bf16" if g.dtype == torch.bfloat16 else "f32"
-        ref_out, ref_rec = O.roundtrip(xs, op, od)
+        ref_out, ref_rec = O.roundtrip(xs, op, od, axes, alloc)
         m_gpu = O.mse(out[u].float().cpu().numpy(), xs)
         m_ref = O.mse(ref_out, xs)
         say(f"  unit {u}: mse gpu {m_gpu:.6e} oracle {m_ref:.6e}")
         assert abs(m_gpu / m_ref - 1) <= 1e-3
-        _compare_records(rec[u].cpu().numpy(), ref_rec, op, O.dct3_forward(xs))
+        _compare_records(rec[u].cpu().numpy(), ref_rec, op, O.dct3_forward(xs, axes))
 
 
 @pytest.mark.parametrize("geo", GEOMS)
@@ -294,6 +297,22 @@ def test_roundtrip_small(geo):
     g = _geom(*geo)
     say("roundtrip", geo)
     _roundtrip_check(_units(g, 3, seed=7), g)
+
+
+@pytest.mark.parametrize("axes", [1, 2, 4, 3, 5, 6])
+def test_roundtrip_axis_subsets(axes):
+    # the page's transform ablation: 1- and 2-axis DCTs through the codec
+    g = _geom(5, 7, 9, 2, 64, 2, axes=axes)
+    say("roundtrip axes", axes)
+    _roundtrip_check(_units(g, 2, seed=11), g)
+
+
+@pytest.mark.parametrize("geo", [(4, 8, 8, 2, 64, 1, 3, torch.float32), (3, 14, 14, 1, 128, 2, 8, torch.bfloat16)])
+def test_roundtrip_uniform_allocation(geo):
+    # the page's allocation ablation: every bin at the average budget
+    g = _geom(*geo, alloc_mode=tact.ALLOC_UNIFORM)
+    say("roundtrip uniform", geo)
+    _roundtrip_check(_units(g, 2, seed=12), g)
 
 
 def test_tiny_workload_all_units():

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 from oracle import (Params, absmax_to_std, allocate_bits, bin_variance,
-                    compress, dct3_forward, decompress, gains_f32,
+                    compress, dct3_forward, decompress, gains_f32, mse,
                     occupancy_bits, pack_record, quantize, record_layout,
                     total_bits, unpack_record)
 from tact_inputs import WORKLOADS, generate_unit
@@ -152,3 +152,24 @@ def test_generator_is_deterministic_and_shaped():
     assert a.dtype == torch.float32 and tuple(a.shape) == (4, 8, 8, 2, 64)
     assert torch.equal(a, b)
     assert not torch.equal(a, generate_unit(wl, 0, 0, 1))
+
+
+def test_ablations_transform_and_allocation_order():
+    # on a field correlated along all three axes, dropping axes or adaptive
+    # allocation can only lose (the page's ablation ordering); uniform
+    # allocation gives every bin the budget
+    from oracle import allocate_uniform, roundtrip
+    x = np.random.default_rng(5).standard_normal((8, 8, 8, 1, 64))
+    for ax, rho in ((0, 0.95), (1, 0.95), (2, 0.95)):
+        for i in range(1, x.shape[ax]):
+            cur = np.take(x, i, axis=ax)
+            prev = np.take(x, i - 1, axis=ax)
+            idx = [slice(None)] * x.ndim
+            idx[ax] = i
+            x[tuple(idx)] = rho * prev + np.sqrt(1 - rho * rho) * cur
+    p = Params(8, 8, 8, 1, 64, budget_bits=1, max_bits=8)
+    e3 = mse(roundtrip(x, p, None)[0], x)
+    e1 = mse(roundtrip(x, p, None, axes=(0,))[0], x)
+    eu = mse(roundtrip(x, p, None, alloc="uniform")[0], x)
+    assert e3 < e1 and e3 < eu
+    assert allocate_uniform(np.zeros(7), 3).tolist() == [3] * 7
