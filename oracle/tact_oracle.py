@@ -51,6 +51,7 @@ __all__ = [
     "total_bits", "waterfill_theta", "waterfill_rates", "round_bits",
     "greedy_correct", "allocate_bits", "allocate_bits_by_sorting", "allocate_uniform",
     "lloyd_max", "codebook_f32", "gains_f32", "quantize", "dequantize",
+    "splitmix64", "rotation_signs", "rotate", "unrotate", "ROTATION_SEED",
     "record_layout", "pack_record", "unpack_record", "round_to_bf16",
     "bf16_bits", "compress", "decompress", "roundtrip", "mse",
     "spectral_flatness", "occupancy_bits", "absmax_to_std",
@@ -390,6 +391,58 @@ def codebook_f32(bits: int):
 
 
 # --------------------------------------------------------------------------
+# O8b: the fixed shared orthogonal rotation            [Method/4]
+# --------------------------------------------------------------------------
+ROTATION_SEED = 0x54414354          # fixed: the rotation is shared by all bins
+_M64 = (1 << 64) - 1
+
+
+def splitmix64(x: int) -> int:
+    """SplitMix64 output for counter value x (Steele, Lea and Flood, 2014):
+    z = x + 0x9E3779B97F4A7C15; z = (z ^ z>>30) * 0xBF58476D1CE4E5B9;
+    z = (z ^ z>>27) * 0x94D049BB133111EB; return z ^ z>>31 (mod 2^64)."""
+    z = (x + 0x9E3779B97F4A7C15) & _M64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+    return z ^ (z >> 31)
+
+
+def rotation_signs(d: int) -> np.ndarray:
+    """Signs s_j = +1 or -1 (the top bit of SplitMix64(seed + j)), j < d."""
+    return np.array([1.0 - 2.0 * (splitmix64(ROTATION_SEED + j) >> 63) for j in range(d)])
+
+
+def _hadamard64() -> np.ndarray:
+    from scipy.linalg import hadamard
+    return hadamard(64).astype(np.float64)
+
+
+def rotate(u: np.ndarray) -> np.ndarray:
+    """v = R u with R = blockdiag over 64-coordinate blocks of H_64 diag(s) / 8.
+
+    READING: the page names a fixed shared orthogonal rotation of the
+    gain-normalized bin vector without giving it; this is a randomized
+    Hadamard rotation in blocks of 64 coordinates (one code word), with
+    signs from SplitMix64.  R is orthogonal: R R^T = I.
+    """
+    u = np.asarray(u, dtype=np.float64)
+    d = u.shape[-1]
+    s = rotation_signs(d)
+    h = _hadamard64() / 8.0
+    blocks = (u * s).reshape(u.shape[:-1] + (d // 64, 64))
+    return np.einsum("ij,...bj->...bi", h, blocks).reshape(u.shape)
+
+
+def unrotate(v: np.ndarray) -> np.ndarray:
+    """u = R^T v (H_64 is symmetric)."""
+    v = np.asarray(v, dtype=np.float64)
+    d = v.shape[-1]
+    h = _hadamard64() / 8.0
+    blocks = v.reshape(v.shape[:-1] + (d // 64, 64))
+    return np.einsum("ij,...bj->...bi", h, blocks).reshape(v.shape) * rotation_signs(d)
+
+
+# --------------------------------------------------------------------------
 # O9: gain-shape scalar quantization                   [Method/4], [Findings/SQ]
 # --------------------------------------------------------------------------
 def gains_f32(var: np.ndarray) -> np.ndarray:
@@ -402,14 +455,16 @@ def gains_f32(var: np.ndarray) -> np.ndarray:
     return np.sqrt(np.asarray(var, dtype=np.float64)).astype(np.float32)
 
 
-def quantize(coef: np.ndarray, gains: np.ndarray, bits: np.ndarray) -> np.ndarray:
+def quantize(coef: np.ndarray, gains: np.ndarray, bits: np.ndarray,
+             rotation: str = "none") -> np.ndarray:
     """Cell index of every coefficient at its bin's bit width [Method/4].
 
     Decided in float32 (the kernel's precision): r = 1/g (0 when g == 0),
-    u = fl32(c * r), code = number of fp32 thresholds <= u (a value exactly
-    on a threshold goes to the upper cell).  Bins with 0 bits get code 0 and
-    are not stored.  READING: the shared rotation of the page is the
-    identity here.  Returns uint8 codes with the shape of ``coef``.
+    u = fl32(c * r); with rotation="hadamard" the bin vector is rotated,
+    v = fl32(R u) (R u in fp64 from the fp32 u); code = number of fp32
+    thresholds <= the value (a value exactly on a threshold goes to the
+    upper cell).  Bins with 0 bits get code 0 and are not stored.  Returns
+    uint8 codes with the shape of ``coef``.
     """
     c32 = np.asarray(coef).astype(np.float32)
     g = np.asarray(gains, dtype=np.float32).reshape(c32.shape[:-1])
@@ -418,6 +473,8 @@ def quantize(coef: np.ndarray, gains: np.ndarray, bits: np.ndarray) -> np.ndarra
         r = np.where(g > 0, np.float32(1.0) / np.where(g > 0, g, np.float32(1.0)),
                      np.float32(0.0)).astype(np.float32)
     u = (c32 * r[..., None]).astype(np.float32)
+    if rotation == "hadamard":
+        u = rotate(u.astype(np.float64)).astype(np.float32)
     codes = np.zeros(c32.shape, dtype=np.uint8)
     for nb in range(1, 9):
         sel = b == nb
@@ -428,8 +485,10 @@ def quantize(coef: np.ndarray, gains: np.ndarray, bits: np.ndarray) -> np.ndarra
     return codes
 
 
-def dequantize(codes: np.ndarray, gains: np.ndarray, bits: np.ndarray) -> np.ndarray:
-    """c_hat = g * level_b[code]; 0-bit bins reconstruct to exactly 0 [Method/dec]."""
+def dequantize(codes: np.ndarray, gains: np.ndarray, bits: np.ndarray,
+               rotation: str = "none") -> np.ndarray:
+    """c_hat = g * R^T level_b[code] (R = I without rotation); 0-bit bins
+    reconstruct to exactly 0 [Method/dec]."""
     codes = np.asarray(codes)
     g = np.asarray(gains, dtype=np.float64).reshape(codes.shape[:-1])
     b = np.asarray(bits).reshape(codes.shape[:-1]).astype(np.int64)
@@ -439,7 +498,10 @@ def dequantize(codes: np.ndarray, gains: np.ndarray, bits: np.ndarray) -> np.nda
         if not sel.any():
             continue
         levels, _, _ = lloyd_max(nb)
-        out[sel] = g[sel][..., None] * levels[codes[sel].astype(np.int64)]
+        lv = levels[codes[sel].astype(np.int64)]
+        if rotation == "hadamard":
+            lv = unrotate(lv)
+        out[sel] = g[sel][..., None] * lv
     return out
 
 
@@ -555,11 +617,13 @@ def allocate_uniform(var: np.ndarray, budget_bits: int) -> np.ndarray:
     return np.full(np.asarray(var).size, int(budget_bits), dtype=np.int64)
 
 
-def compress(x: np.ndarray, p: Params, axes=(0, 1, 2), alloc: str = "waterfill") -> np.ndarray:
+def compress(x: np.ndarray, p: Params, axes=(0, 1, 2), alloc: str = "waterfill",
+             rotation: str = "none") -> np.ndarray:
     """One unit: transform, variances, allocation, quantization, record.
 
     ``axes`` and ``alloc`` ("waterfill" or "uniform") select the page's
     ablations; the method is all three axes with water-filling.
+    ``rotation`` is "hadamard" (the page's shared rotation) or "none".
     """
     x = np.asarray(x, dtype=np.float64).reshape(p.shape)
     coef = dct3_forward(x, axes)
@@ -569,19 +633,19 @@ def compress(x: np.ndarray, p: Params, axes=(0, 1, 2), alloc: str = "waterfill")
     else:
         bits = allocate_bits(var, total_bits(p), p.max_bits).reshape(var.shape)
     g = gains_f32(var)
-    codes = quantize(coef, g, bits)
+    codes = quantize(coef, g, bits, rotation)
     return pack_record(codes, g, bits, p)
 
 
 def decompress(rec: np.ndarray, p: Params, out_dtype="bf16",
-               axes=(0, 1, 2)) -> np.ndarray:
+               axes=(0, 1, 2), rotation: str = "none") -> np.ndarray:
     """Unpack, dequantize, inverse transform, round [Method/dec].
 
     READING: the output is rounded to bfloat16 (nearest even) for a bf16
     cache, or to float32 for a float32 cache.
     """
     codes, g, b = unpack_record(rec, p)
-    xr = dct3_inverse(dequantize(codes, g, b), axes)
+    xr = dct3_inverse(dequantize(codes, g, b, rotation), axes)
     if out_dtype == "bf16":
         return round_to_bf16(xr)
     if out_dtype == "f32":
@@ -590,9 +654,9 @@ def decompress(rec: np.ndarray, p: Params, out_dtype="bf16",
 
 
 def roundtrip(x: np.ndarray, p: Params, out_dtype="bf16", axes=(0, 1, 2),
-              alloc: str = "waterfill"):
-    rec = compress(x, p, axes, alloc)
-    return decompress(rec, p, out_dtype, axes), rec
+              alloc: str = "waterfill", rotation: str = "none"):
+    rec = compress(x, p, axes, alloc, rotation)
+    return decompress(rec, p, out_dtype, axes, rotation), rec
 
 
 # --------------------------------------------------------------------------

@@ -121,3 +121,40 @@ def test_eight_bit_roundtrip_distortion():
     r = dequantize(quantize(c, g, bits), g, bits)
     rel = np.mean((r - c) ** 2) / np.mean(c ** 2)
     assert abs(rel / lloyd_max(8)[2] - 1) < 0.05
+
+
+def test_splitmix64_reference_values():
+    # the generator's published reference sequence from state 0: outputs
+    # 1..3 are the mix of states gamma, 2 gamma, 3 gamma
+    from oracle import splitmix64
+    gamma = 0x9E3779B97F4A7C15
+    seq = [splitmix64(k * gamma % 2 ** 64) for k in range(3)]
+    assert seq == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_rotation_is_orthogonal_and_block_hadamard():
+    from scipy.linalg import hadamard
+    from oracle import rotate, rotation_signs, unrotate
+    for d in (64, 128, 256):
+        eye = np.eye(d)
+        R = rotate(eye).T                       # columns: R e_j
+        assert np.max(np.abs(R @ R.T - eye)) < 1e-14
+        s = rotation_signs(d)
+        assert set(np.unique(s)) <= {-1.0, 1.0} and 0.3 < np.mean(s > 0) < 0.7
+        # block structure: H_64 diag(s) / 8 on each 64-block
+        blk = hadamard(64) * s[:64] / 8.0
+        assert np.max(np.abs(R[:64, :64] - blk)) < 1e-15
+        if d > 64:
+            assert np.max(np.abs(R[:64, 64:])) == 0.0
+        x = np.random.default_rng(d).standard_normal((3, d))
+        assert np.max(np.abs(unrotate(rotate(x)) - x)) < 1e-13
+
+
+def test_rotation_flattens_a_spike():
+    # a single large coordinate spreads evenly: every rotated coordinate has
+    # magnitude |x| / 8, so the heavy-tail ratio absmax / rms drops to 1
+    from oracle import rotate
+    x = np.zeros(128)
+    x[5] = 8.0
+    v = rotate(x)
+    assert np.allclose(np.abs(v[:64]), 1.0) and np.all(v[64:] == 0.0)
