@@ -407,9 +407,9 @@ def splitmix64(x: int) -> int:
     return z ^ (z >> 31)
 
 
-def rotation_signs(d: int) -> np.ndarray:
-    """Signs s_j = +1 or -1 (the top bit of SplitMix64(seed + j)), j < d."""
-    return np.array([1.0 - 2.0 * (splitmix64(ROTATION_SEED + j) >> 63) for j in range(d)])
+def rotation_signs() -> np.ndarray:
+    """The 64 signs s_j = +1 or -1: the top bit of SplitMix64(seed + j)."""
+    return np.array([1.0 - 2.0 * (splitmix64(ROTATION_SEED + j) >> 63) for j in range(64)])
 
 
 def _hadamard64() -> np.ndarray:
@@ -418,18 +418,18 @@ def _hadamard64() -> np.ndarray:
 
 
 def rotate(u: np.ndarray) -> np.ndarray:
-    """v = R u with R = blockdiag over 64-coordinate blocks of H_64 diag(s) / 8.
+    """v = R u with R = I_(d/64) (x) H_64 diag(s) / 8: the same randomized
+    Hadamard rotation on every 64-coordinate block of the last axis.
 
     READING: the page names a fixed shared orthogonal rotation of the
     gain-normalized bin vector without giving it; this is a randomized
     Hadamard rotation in blocks of 64 coordinates (one code word), with
-    signs from SplitMix64.  R is orthogonal: R R^T = I.
+    Sylvester's H_64 and signs from SplitMix64.  R is orthogonal.
     """
     u = np.asarray(u, dtype=np.float64)
     d = u.shape[-1]
-    s = rotation_signs(d)
     h = _hadamard64() / 8.0
-    blocks = (u * s).reshape(u.shape[:-1] + (d // 64, 64))
+    blocks = (u.reshape(u.shape[:-1] + (d // 64, 64)) * rotation_signs())
     return np.einsum("ij,...bj->...bi", h, blocks).reshape(u.shape)
 
 
@@ -439,7 +439,7 @@ def unrotate(v: np.ndarray) -> np.ndarray:
     d = v.shape[-1]
     h = _hadamard64() / 8.0
     blocks = v.reshape(v.shape[:-1] + (d // 64, 64))
-    return np.einsum("ij,...bj->...bi", h, blocks).reshape(v.shape) * rotation_signs(d)
+    return (np.einsum("ij,...bj->...bi", h, blocks) * rotation_signs()).reshape(v.shape)
 
 
 # --------------------------------------------------------------------------
@@ -618,12 +618,13 @@ def allocate_uniform(var: np.ndarray, budget_bits: int) -> np.ndarray:
 
 
 def compress(x: np.ndarray, p: Params, axes=(0, 1, 2), alloc: str = "waterfill",
-             rotation: str = "none") -> np.ndarray:
+             rotation: str = "hadamard") -> np.ndarray:
     """One unit: transform, variances, allocation, quantization, record.
 
     ``axes`` and ``alloc`` ("waterfill" or "uniform") select the page's
     ablations; the method is all three axes with water-filling.
-    ``rotation`` is "hadamard" (the page's shared rotation) or "none".
+    ``rotation`` is "hadamard" (the page's shared rotation, the method)
+    or "none" (the identity, an ablation).
     """
     x = np.asarray(x, dtype=np.float64).reshape(p.shape)
     coef = dct3_forward(x, axes)
@@ -638,7 +639,7 @@ def compress(x: np.ndarray, p: Params, axes=(0, 1, 2), alloc: str = "waterfill",
 
 
 def decompress(rec: np.ndarray, p: Params, out_dtype="bf16",
-               axes=(0, 1, 2), rotation: str = "none") -> np.ndarray:
+               axes=(0, 1, 2), rotation: str = "hadamard") -> np.ndarray:
     """Unpack, dequantize, inverse transform, round [Method/dec].
 
     READING: the output is rounded to bfloat16 (nearest even) for a bf16
@@ -654,7 +655,7 @@ def decompress(rec: np.ndarray, p: Params, out_dtype="bf16",
 
 
 def roundtrip(x: np.ndarray, p: Params, out_dtype="bf16", axes=(0, 1, 2),
-              alloc: str = "waterfill", rotation: str = "none"):
+              alloc: str = "waterfill", rotation: str = "hadamard"):
     rec = compress(x, p, axes, alloc, rotation)
     return decompress(rec, p, out_dtype, axes, rotation), rec
 

@@ -139,11 +139,12 @@ def test_rotation_is_orthogonal_and_block_hadamard():
         eye = np.eye(d)
         R = rotate(eye).T                       # columns: R e_j
         assert np.max(np.abs(R @ R.T - eye)) < 1e-14
-        s = rotation_signs(d)
+        s = rotation_signs()
         assert set(np.unique(s)) <= {-1.0, 1.0} and 0.3 < np.mean(s > 0) < 0.7
-        # block structure: H_64 diag(s) / 8 on each 64-block
-        blk = hadamard(64) * s[:64] / 8.0
-        assert np.max(np.abs(R[:64, :64] - blk)) < 1e-15
+        # block structure: the same H_64 diag(s) / 8 on every 64-block
+        blk = hadamard(64) * s / 8.0
+        for b0 in range(0, d, 64):
+            assert np.max(np.abs(R[b0:b0 + 64, b0:b0 + 64] - blk)) < 1e-15
         if d > 64:
             assert np.max(np.abs(R[:64, 64:])) == 0.0
         x = np.random.default_rng(d).standard_normal((3, d))
