@@ -182,6 +182,7 @@ def main():
         "config": {"workload": wl.name, "units": U, "unit_shape": list(wl.unit_shape),
                    "cache_dtype": str(wl.dtype).replace("torch.", ""),
                    "budget_bits": budget, "max_bits": wl.max_bits,
+                   "rotation": "hadamard" if g.rotation else "none",
                    "input_bytes": in_bytes},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -81,6 +81,18 @@ enum { TACT_AXIS_S = 1, TACT_AXIS_H = 2, TACT_AXIS_W = 4, TACT_AXES_ALL = 7 };
  * bin budget_bits planes (the page's "uniform allocation" ablation). */
 enum { TACT_ALLOC_WATERFILL = 0, TACT_ALLOC_UNIFORM = 1 };
 
+/* The quantizer's fixed shared rotation (section "Methodology in Plain
+ * English", stage 4: the gain-normalized bin vector is rotated by one fixed
+ * orthogonal matrix before scalar quantization, and rotated back after
+ * dequantization).  TACT_ROTATION_HADAMARD (the method) is
+ * R = H_64 diag(s) / 8 on every 64-channel block of a bin: H_64 is
+ * Sylvester's Hadamard matrix, H[j][j'] = (-1)^popcount(j & j'), and s_j is
+ * -1 where the top bit of SplitMix64(0x54414354 + j) is set, else +1
+ * (SplitMix64: Steele, Lea and Flood, 2014).  Code bit j of a word is the
+ * cell of the rotated coordinate j.  TACT_ROTATION_NONE quantizes the
+ * normalized coefficients themselves (an ablation). */
+enum { TACT_ROTATION_NONE = 0, TACT_ROTATION_HADAMARD = 1 };
+
 typedef struct {
   int32_t S, H, W;      /* grid of the vision encoder, each 1..64            */
   int32_t kv_heads;     /* 1..64                                             */
@@ -90,10 +102,11 @@ typedef struct {
   int32_t dtype;        /* tact_dtype of the cache tensors (in == out)       */
   int32_t axes;         /* TACT_AXES_ALL, or a non-empty subset              */
   int32_t alloc_mode;   /* TACT_ALLOC_WATERFILL or TACT_ALLOC_UNIFORM        */
+  int32_t rotation;     /* TACT_ROTATION_HADAMARD or TACT_ROTATION_NONE      */
 } tact_params;
 
 /* Fills *p with the method's defaults for the given geometry and budget
- * (dtype bf16, all axes, water-filling, cap 8). */
+ * (dtype bf16, all axes, water-filling, cap 8, Hadamard rotation). */
 void tact_params_init(tact_params* p, int32_t S, int32_t H, int32_t W,
                       int32_t kv_heads, int32_t head_dim, int32_t budget_bits);
 

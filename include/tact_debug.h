@@ -37,7 +37,9 @@ tact_status tact_dbg_allocate(const tact_params* p, int64_t n_units,
 /* Stage 4: quantize fp32 coefficients with the given gains and bits and
  * write complete records (gains, bits, group index, codes).  The bits of
  * each unit must sum to budget_bits * n_bins and not exceed max_bits; the
- * kernel does not check this (the caller's bits come from an allocation). */
+ * kernel does not check this (the caller's bits come from an allocation).
+ * Quantizes the coefficients as they are: params->rotation must be
+ * TACT_ROTATION_NONE (else TACT_ERR_UNSUPPORTED). */
 tact_status tact_dbg_quantize(const tact_params* p, int64_t n_units,
                               const float* coef, const float* gains,
                               const uint8_t* bits, void* records,
@@ -49,7 +51,8 @@ tact_status tact_dbg_unpack(const tact_params* p, int64_t n_units,
                             const void* records, uint8_t* codes,
                             hipStream_t stream);
 
-/* Decoding, second step: dequantized fp32 coefficients g * level[code]. */
+/* Decoding, second step: dequantized fp32 coefficients g * level[code].
+ * params->rotation must be TACT_ROTATION_NONE (else TACT_ERR_UNSUPPORTED). */
 tact_status tact_dbg_dequantize(const tact_params* p, int64_t n_units,
                                 const void* records, float* coef,
                                 hipStream_t stream);

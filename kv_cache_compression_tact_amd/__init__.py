@@ -28,12 +28,13 @@ TACT_OK, TACT_ERR_INVALID_ARGUMENT, TACT_ERR_UNSUPPORTED, TACT_ERR_WORKSPACE, \
 TACT_BF16, TACT_F32 = 0, 1
 AXIS_S, AXIS_H, AXIS_W, AXES_ALL = 1, 2, 4, 7
 ALLOC_WATERFILL, ALLOC_UNIFORM = 0, 1
+ROTATION_NONE, ROTATION_HADAMARD = 0, 1
 
 
 class TactParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("S", "H", "W", "kv_heads", "head_dim", "budget_bits", "max_bits",
-                 "dtype", "axes", "alloc_mode")]
+                 "dtype", "axes", "alloc_mode", "rotation")]
 
 
 def _load():
@@ -107,6 +108,7 @@ class Geometry:
     dtype: torch.dtype = torch.bfloat16
     axes: int = AXES_ALL
     alloc_mode: int = ALLOC_WATERFILL
+    rotation: int = ROTATION_HADAMARD
 
     def params(self) -> TactParams:
         if self.dtype not in (torch.bfloat16, torch.float32):
@@ -114,7 +116,7 @@ class Geometry:
         return TactParams(self.S, self.H, self.W, self.kv_heads, self.head_dim,
                           self.budget_bits, self.max_bits,
                           TACT_BF16 if self.dtype == torch.bfloat16 else TACT_F32,
-                          self.axes, self.alloc_mode)
+                          self.axes, self.alloc_mode, self.rotation)
 
     @property
     def unit_shape(self):
@@ -178,9 +180,11 @@ def workspace(geom: Geometry, n_units: int, device=None) -> torch.Tensor:
 
 def compress(kv: torch.Tensor, budget_bits: int, max_bits: int = 8, *,
              records: torch.Tensor | None = None, ws: torch.Tensor | None = None,
-             axes: int = AXES_ALL, alloc_mode: int = ALLOC_WATERFILL) -> torch.Tensor:
+             axes: int = AXES_ALL, alloc_mode: int = ALLOC_WATERFILL,
+             rotation: int = ROTATION_HADAMARD) -> torch.Tensor:
     """kv (U, S, H, W, Hkv, d) bf16/fp32 on the GPU -> records uint8 (U, record_bytes)."""
-    g = Geometry.of(kv, budget_bits, max_bits=max_bits, axes=axes, alloc_mode=alloc_mode)
+    g = Geometry.of(kv, budget_bits, max_bits=max_bits, axes=axes, alloc_mode=alloc_mode,
+                    rotation=rotation)
     U = kv.shape[0]
     if records is None:
         records = torch.empty((U, g.record_bytes()), dtype=torch.uint8, device=kv.device)
@@ -211,9 +215,11 @@ def decompress(records: torch.Tensor, geom: Geometry, *, out: torch.Tensor | Non
 def roundtrip(kv: torch.Tensor, budget_bits: int, max_bits: int = 8, *,
               out: torch.Tensor | None = None, records: torch.Tensor | None = None,
               ws: torch.Tensor | None = None, keep_records: bool = True,
-              axes: int = AXES_ALL, alloc_mode: int = ALLOC_WATERFILL):
+              axes: int = AXES_ALL, alloc_mode: int = ALLOC_WATERFILL,
+              rotation: int = ROTATION_HADAMARD):
     """Compress then decompress; returns (kv_hat, records or None)."""
-    g = Geometry.of(kv, budget_bits, max_bits=max_bits, axes=axes, alloc_mode=alloc_mode)
+    g = Geometry.of(kv, budget_bits, max_bits=max_bits, axes=axes, alloc_mode=alloc_mode,
+                    rotation=rotation)
     U = kv.shape[0]
     if out is None:
         out = torch.empty_like(kv)

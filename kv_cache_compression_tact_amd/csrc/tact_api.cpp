@@ -59,6 +59,8 @@ tact_status make_geometry(const tact_params* p, Geometry* g) {
                 p->axes);
   if (p->alloc_mode != TACT_ALLOC_WATERFILL && p->alloc_mode != TACT_ALLOC_UNIFORM)
     return fail(TACT_ERR_INVALID_ARGUMENT, "alloc_mode=%d: must be 0 or 1", p->alloc_mode);
+  if (p->rotation != TACT_ROTATION_NONE && p->rotation != TACT_ROTATION_HADAMARD)
+    return fail(TACT_ERR_INVALID_ARGUMENT, "rotation=%d: must be 0 or 1", p->rotation);
   Geometry& G = *g;
   G.S = p->S;
   G.H = p->H;
@@ -69,6 +71,7 @@ tact_status make_geometry(const tact_params* p, Geometry* g) {
   G.budget_bits = p->budget_bits;
   G.axes = p->axes;
   G.alloc_mode = p->alloc_mode;
+  G.rotation = p->rotation;
   G.dtype = p->dtype;
   G.n_bins = int64_t(p->S) * p->H * p->W * p->kv_heads;
   G.n_entries = G.n_bins * p->head_dim;
@@ -293,6 +296,7 @@ void tact_params_init(tact_params* p, int32_t S, int32_t H, int32_t W, int32_t k
   p->dtype = TACT_BF16;
   p->axes = TACT_AXES_ALL;
   p->alloc_mode = TACT_ALLOC_WATERFILL;
+  p->rotation = TACT_ROTATION_HADAMARD;
 }
 
 size_t tact_record_bytes(const tact_params* p) {
@@ -485,6 +489,9 @@ tact_status tact_dbg_quantize(const tact_params* p, int64_t n_units, const float
   Geometry g;
   tact_status st;
   if ((st = make_geometry(p, &g)) != TACT_OK) return st;
+  if (g.rotation != TACT_ROTATION_NONE)
+    return fail(TACT_ERR_UNSUPPORTED, "tact_dbg_quantize: the stage entry point quantizes without the "
+                "shared rotation; set rotation = TACT_ROTATION_NONE");
   if ((st = check_units(n_units)) != TACT_OK) return st;
   if (n_units == 0) return ok();
   if ((st = check_buffer(coef, "coef", 16)) != TACT_OK) return st;
@@ -514,6 +521,9 @@ tact_status tact_dbg_dequantize(const tact_params* p, int64_t n_units, const voi
   Geometry g;
   tact_status st;
   if ((st = make_geometry(p, &g)) != TACT_OK) return st;
+  if (g.rotation != TACT_ROTATION_NONE)
+    return fail(TACT_ERR_UNSUPPORTED, "tact_dbg_dequantize: the stage entry point quantizes without the "
+                "shared rotation; set rotation = TACT_ROTATION_NONE");
   if ((st = check_units(n_units)) != TACT_OK) return st;
   if (n_units == 0) return ok();
   if ((st = check_buffer(records, "records", 256)) != TACT_OK) return st;

@@ -14,7 +14,7 @@ namespace tact {
 // Geometry of one unit and of its record, derived from validated params.
 struct Geometry {
   int S, H, W, kv_heads, head_dim;
-  int max_bits, budget_bits, axes, alloc_mode;
+  int max_bits, budget_bits, axes, alloc_mode, rotation;
   int dtype;
   int64_t n_bins;        // S*H*W*kv_heads
   int64_t n_entries;     // n_bins * head_dim

@@ -82,6 +82,81 @@ __device__ __forceinline__ uint16_t bf16_rne_bits(float v) {
   return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// ---------------------------------------------------------------------------
+// The shared rotation of the quantizer (stage 4): R = H_64 diag(s) / 8 on
+// every 64-channel block of a bin, H_64 Sylvester's Hadamard matrix
+// (H[j][j'] = (-1)^popcount(j & j')), s_j the top bit of SplitMix64(seed+j)
+// mapped to +1 / -1.  In the fragments the 6 channel bits split into 4 lane
+// bits (lanes of a 16-lane row) and 2 register bits (4 values per lane).
+// ---------------------------------------------------------------------------
+constexpr uint64_t kRotationSeed = 0x54414354ull;
+
+// SplitMix64 (Steele, Lea and Flood, OOPSLA 2014), one output per counter.
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+  uint64_t z = x + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__device__ __forceinline__ float rotation_sign(int j) {
+  return (splitmix64(kRotationSeed + static_cast<uint64_t>(j)) >> 63) ? -1.0f : 1.0f;
+}
+
+// Partner values across the lanes of a 16-lane row: lane ^ 1, ^ 2 (quad
+// permutes), ^ 4 (swizzle, bit mask mode), ^ 8 (row rotate by 8).
+__device__ __forceinline__ float lane_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane_xor4(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
+}
+__device__ __forceinline__ float lane_xor8(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));
+}
+
+// Per-lane constants of the 16-point butterflies: sg[k] = -1 where lane bit
+// k is set; the product of the four is the sign the butterflies leave.
+struct LaneWht {
+  float sg[4];
+  float parity;
+  __device__ __forceinline__ explicit LaneWht(int lane) {
+    parity = 1.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      sg[k] = ((lane >> k) & 1) ? -1.f : 1.f;
+      parity *= sg[k];
+    }
+  }
+};
+
+// In-register butterflies over the 2 register bits, then the 4 lane
+// butterflies.  A lane butterfly keeps x + sg * x_partner: where the lane
+// bit is set that is x_self - x_partner, minus the Sylvester value, and the
+// partner carries the same sign history, so the result is
+// parity * (H_64 x) for each of the 4 values.
+__device__ __forceinline__ void wht64(float& a0, float& a1, float& a2, float& a3,
+                                      const LaneWht& w) {
+  float b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;
+  a0 = b0 + b2;
+  a2 = b0 - b2;
+  a1 = b1 + b3;
+  a3 = b1 - b3;
+  float* v[4] = {&a0, &a1, &a2, &a3};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float x = *v[q];
+    x = fmaf(lane_xor1(x), w.sg[0], x);
+    x = fmaf(lane_xor2(x), w.sg[1], x);
+    x = fmaf(lane_xor4(x), w.sg[2], x);
+    x = fmaf(lane_xor8(x), w.sg[3], x);
+    *v[q] = x;
+  }
+}
+
 // Number of the 2^b - 1 ascending thresholds (LDS copy) that are <= u.
 __device__ __forceinline__ int cell_index_lds(const float* thr, float u, int b) {
   const float* t = thr + ((1 << b) - b - 1);
@@ -115,6 +190,7 @@ struct AxisArgs {
   int64_t var_stride;
   RecordView rec;            // EPI_QUANT, PRO_DEQUANT
   const uint32_t* plane_off; // per-bin first plane, u * n_bins + bin
+  int rotate;                // EPI_QUANT, PRO_DEQUANT: apply the shared rotation
 };
 
 template <int NP>
@@ -178,6 +254,17 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
     __syncthreads();
   }
   const int N = a.N;
+  // the shared rotation: lane butterflies and per-tile post factors
+  // (dequantize: channel 4t + i; quantize: channel 16 (i % 4) + t)
+  const LaneWht wl(lane);
+  float rpost[4] = {1.f, 1.f, 1.f, 1.f};
+  const bool rot = (PRO == PRO_DEQUANT || EPI == EPI_QUANT) && a.rotate;
+  if (rot) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      rpost[i] = (PRO == PRO_DEQUANT) ? 0.125f * wl.parity * rotation_sign(4 * t + i)
+                                      : rotation_sign(16 * i + t);
+  }
 
   // A fragments (the DCT matrix scaled by 2^12, or its transpose), hi / lo
   vec ahi[F::MT][F::KSTEPS], alo[F::MT][F::KSTEPS];
@@ -282,6 +369,14 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
           xv[2][ks][v] = q.z;
           xv[3][ks][v] = q.w;
         }
+      // R^T = diag(s) H / 8: H here, the rest with the output scale
+      if (rot) {
+#pragma unroll
+        for (int ks = 0; ks < F::KSTEPS; ++ks)
+#pragma unroll
+          for (int v = 0; v < F::KV; ++v)
+            wht64(xv[0][ks][v], xv[1][ks][v], xv[2][ks][v], xv[3][ks][v], wl);
+      }
     } else if constexpr (INTL) {
       // TPW consecutive elements per lane: one 16-byte vector per row
 #pragma unroll
@@ -350,7 +445,7 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
       int e = 0;
       if (mx > 0.f) frexpf(mx, &e);
       const float sc = ldexpf(1.0f, 14 - e);
-      const float unscale = ldexpf(1.0f, e - 26);
+      const float unscale = ldexpf(1.0f, e - 26) * rpost[i % 4];
 #pragma unroll
       for (int ks = 0; ks < F::KSTEPS; ++ks) {
         vec bhi, blo;
@@ -425,6 +520,25 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
       const float* invg = a.inv_gain + u * a.var_stride;
       constexpr int HALVES = TPW / 4;                  // 64-channel words per plane
       float* zt = s_z + (threadIdx.x / kWave) * ZROWS * ZROW;
+      if (rot) {
+        // R = H diag(s) / 8 on each 64-channel word (the signs came with
+        // the output scale): channel 16 i' + t of word h is acc[4h + i']
+        const float post = 0.125f * wl.parity;
+#pragma unroll
+        for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+          for (int m = 0; m < F::MT; ++m)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              float y0 = acc[4 * h][m][rr], y1 = acc[4 * h + 1][m][rr];
+              float y2 = acc[4 * h + 2][m][rr], y3 = acc[4 * h + 3][m][rr];
+              wht64(y0, y1, y2, y3, wl);
+              acc[4 * h][m][rr] = y0 * post;
+              acc[4 * h + 1][m][rr] = y1 * post;
+              acc[4 * h + 2][m][rr] = y2 * post;
+              acc[4 * h + 3][m][rr] = y3 * post;
+            }
+      }
 #pragma unroll
       for (int s0 = 0; s0 < NP; s0 += ZROWS) {
         // bin-major staging: row k - s0 holds the head's 16 * TPW coefficients
@@ -528,13 +642,13 @@ __device__ __forceinline__ void load_afrag(const float* tab, int inverse, int t,
       }
 }
 
-// acc[i][m] += A * B for 4 interleaved column tiles whose K values are
-// xv[i][ks][v]; per-column power-of-two scaling, 3-term split products.
+// acc[i][m] = post[i] * A * B for 4 interleaved column tiles whose K values
+// are xv[i][ks][v]; per-column power-of-two scaling, 3-term split products.
 template <int NP>
 __device__ __forceinline__ void contract4(const typename Frag<NP>::vec (&ahi)[Frag<NP>::MT][Frag<NP>::KSTEPS],
                                           const typename Frag<NP>::vec (&alo)[Frag<NP>::MT][Frag<NP>::KSTEPS],
                                           float (&xv)[4][Frag<NP>::KSTEPS][Frag<NP>::KV],
-                                          f32x4 (&acc)[4][Frag<NP>::MT]) {
+                                          f32x4 (&acc)[4][Frag<NP>::MT], const float (&post)[4]) {
   using F = Frag<NP>;
   using vec = typename F::vec;
 #pragma unroll
@@ -550,7 +664,7 @@ __device__ __forceinline__ void contract4(const typename Frag<NP>::vec (&ahi)[Fr
     int e = 0;
     if (mx > 0.f) frexpf(mx, &e);
     const float sc = ldexpf(1.0f, 14 - e);
-    const float unscale = ldexpf(1.0f, e - 26);
+    const float unscale = ldexpf(1.0f, e - 26) * post[i];
 #pragma unroll
     for (int ks = 0; ks < F::KSTEPS; ++ks) {
       vec bhi, blo;
@@ -573,10 +687,23 @@ __device__ __forceinline__ void contract4(const typename Frag<NP>::vec (&ahi)[Fr
   }
 }
 
+// the shared rotation on the channel index 4t + i of fragment values
+// xv[i][ks][v] (the same K index across a 16-lane row)
+template <int NP>
+__device__ __forceinline__ void rotate_frag(float (&xv)[4][Frag<NP>::KSTEPS][Frag<NP>::KV],
+                                            const LaneWht& w) {
+#pragma unroll
+  for (int ks = 0; ks < Frag<NP>::KSTEPS; ++ks)
+#pragma unroll
+    for (int v = 0; v < Frag<NP>::KV; ++v)
+      wht64(xv[0][ks][v], xv[1][ks][v], xv[2][ks][v], xv[3][ks][v], w);
+}
+
 constexpr int kPlaneWaves = 16;
 
-template <int NPH, int NPW, int MODE>
+template <int NPH, int NPW, int MODE, bool ROT>
 __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
+  static_assert(!ROT || MODE != MODE_STATS, "the variance does not see the rotation");
   using FH = Frag<NPH>;
   using FW = Frag<NPW>;
   extern __shared__ float plane[];          // [H][W][64] fp32
@@ -600,6 +727,25 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
     return ((static_cast<int64_t>(s) * H + kh) * W + kw) * a.kv_heads + head;
   };
   const int64_t vol = u * a.ustride + static_cast<int64_t>(s) * H * W * a.C;   // (s, 0, 0, 0)
+  // rotation constants: lane butterflies; s_j of the lane's channels 4t + i
+  // (sgn, with the first forward contraction) and the scale after the W
+  // contraction (post_w: the butterflies' sign and 1/8, and s_j inverse)
+  const LaneWht wl(lane);
+  float sgn[4] = {1.f, 1.f, 1.f, 1.f};
+  float post_w[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (ROT) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float si = rotation_sign(4 * t + i);
+      if constexpr (MODE == MODE_QUANT) {
+        sgn[i] = si;
+        post_w[i] = 0.125f * wl.parity;
+      } else {
+        post_w[i] = 0.125f * wl.parity * si;
+      }
+    }
+  }
+  constexpr float kOne[4] = {1.f, 1.f, 1.f, 1.f};
 
   if constexpr (MODE != MODE_DEQUANT) {
     // ---- H axis: global -> LDS; a wave owns the columns of one w --------
@@ -617,7 +763,8 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
           xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
         }
       f32x4 acc[4][FH::MT];
-      contract4<NPH>(ahi, alo, xv, acc);
+      // R = H diag(s) / 8: the signs go with the first contraction
+      contract4<NPH>(ahi, alo, xv, acc, sgn);
 #pragma unroll
       for (int m = 0; m < FH::MT; ++m)
 #pragma unroll
@@ -644,7 +791,14 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
           xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
         }
       f32x4 acc[4][FW::MT];
-      contract4<NPW>(bhi_w, blo_w, xv, acc);
+      if constexpr (ROT) {
+        // H on the channels, then the butterflies' sign and 1/8 after the
+        // (channel-wise) W contraction
+        rotate_frag<NPW>(xv, wl);
+        contract4<NPW>(bhi_w, blo_w, xv, acc, post_w);
+      } else {
+        contract4<NPW>(bhi_w, blo_w, xv, acc, kOne);
+      }
       if constexpr (MODE == MODE_STATS) {
 #pragma unroll
         for (int m = 0; m < FW::MT; ++m)
@@ -771,7 +925,14 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
           xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
         }
       f32x4 acc[4][FW::MT];
-      contract4<NPW>(ahi_w, alo_w, xv, acc);
+      if constexpr (ROT) {
+        // R^T = diag(s) H / 8: H on the decoded channels, the signs and 1/8
+        // after the (channel-wise) W contraction
+        rotate_frag<NPW>(xv, wl);
+        contract4<NPW>(ahi_w, alo_w, xv, acc, post_w);
+      } else {
+        contract4<NPW>(ahi_w, alo_w, xv, acc, kOne);
+      }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -800,7 +961,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
           xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
         }
       f32x4 acc[4][FH::MT];
-      contract4<NPH>(ahi_h, alo_h, xv, acc);
+      contract4<NPH>(ahi_h, alo_h, xv, acc, kOne);
 #pragma unroll
       for (int m = 0; m < FH::MT; ++m)
 #pragma unroll
@@ -1235,6 +1396,7 @@ void launch_axis(const Geometry& g, int64_t n_units, int axis, int inverse, int 
   a.var_stride = var_stride;
   a.rec = rec;
   a.plane_off = plane_off;
+  a.rotate = g.rotation == TACT_ROTATION_HADAMARD;
   const int tpw = (epi == EPI_STATS || epi == EPI_QUANT) ? g.head_dim / 16 : 4;
   if (a.N <= 16) launch_axis_np<16>(a, pro, epi, tpw, s);
   else if (a.N <= 32) launch_axis_np<32>(a, pro, epi, tpw, s);
@@ -1275,18 +1437,21 @@ void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in,
   const dim3 block(64 * kPlaneWaves);
   const size_t lds = static_cast<size_t>(g.H) * g.W * 64 * sizeof(float);
   const bool h16 = g.H <= 16, w16 = g.W <= 16;
+  const bool rot = g.rotation == TACT_ROTATION_HADAMARD;
   // the plane needs more dynamic LDS than the default limit
-#define TACT_PLANE_ONE(NH, NW, M)                                                               \
+#define TACT_PLANE_ONE(NH, NW, M, R)                                                            \
   do {                                                                                          \
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_plane<NH, NW, M>),                \
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_plane<NH, NW, M, R>),             \
                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));     \
-    hipLaunchKernelGGL((k_plane<NH, NW, M>), grid, block, lds, s, a);                           \
+    hipLaunchKernelGGL((k_plane<NH, NW, M, R>), grid, block, lds, s, a);                        \
   } while (0)
 #define TACT_PLANE(NH, NW)                                                                      \
   do {                                                                                          \
-    if (mode == MODE_STATS) TACT_PLANE_ONE(NH, NW, MODE_STATS);                                 \
-    else if (mode == MODE_QUANT) TACT_PLANE_ONE(NH, NW, MODE_QUANT);                            \
-    else TACT_PLANE_ONE(NH, NW, MODE_DEQUANT);                                                  \
+    if (mode == MODE_STATS) TACT_PLANE_ONE(NH, NW, MODE_STATS, false);                          \
+    else if (mode == MODE_QUANT && rot) TACT_PLANE_ONE(NH, NW, MODE_QUANT, true);               \
+    else if (mode == MODE_QUANT) TACT_PLANE_ONE(NH, NW, MODE_QUANT, false);                     \
+    else if (rot) TACT_PLANE_ONE(NH, NW, MODE_DEQUANT, true);                                   \
+    else TACT_PLANE_ONE(NH, NW, MODE_DEQUANT, false);                                           \
   } while (0)
   if (h16 && w16) TACT_PLANE(16, 16);
   else if (h16) TACT_PLANE(16, 32);

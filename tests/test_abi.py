@@ -40,7 +40,7 @@ def _params(**kw):
 
 def test_params_init_defaults():
     p = _params()
-    assert (p.max_bits, p.dtype, p.axes, p.alloc_mode) == (8, 0, 7, 0)
+    assert (p.max_bits, p.dtype, p.axes, p.alloc_mode, p.rotation) == (8, 0, 7, 0, 1)
 
 
 def test_record_bytes_matches_layout():
@@ -59,6 +59,7 @@ def test_record_bytes_matches_layout():
     ("S", 0, 2), ("H", 65, 2), ("W", -1, 2), ("kv_heads", 0, 2), ("head_dim", 96, 2),
     ("max_bits", 0, 1), ("max_bits", 9, 1), ("budget_bits", 9, 1), ("budget_bits", -1, 1),
     ("dtype", 5, 1), ("axes", 0, 1), ("axes", 8, 1), ("alloc_mode", 2, 1),
+    ("rotation", 2, 1), ("rotation", -1, 1),
 ])
 def test_invalid_params_rejected(field, value, status):
     p = _params(**{field: value})
@@ -95,6 +96,16 @@ def test_null_and_misaligned_pointers_rejected():
                             ctypes.c_void_p((1 << 20) + 4096), 32768, None, fake, ws,
                             None) == 1
     assert L.tact_compress(None, 2, fake, 32768, fake, fake, ws, None) == 1
+
+
+def test_stage_quantizers_refuse_the_rotation():
+    # the stage entry points quantize and dequantize without the rotation
+    fake = ctypes.c_void_p(1 << 20)
+    L = lib()
+    p = _params()
+    assert L.tact_dbg_quantize(ctypes.byref(p), 1, fake, fake, fake, fake, None) == 2
+    assert L.tact_dbg_dequantize(ctypes.byref(p), 1, fake, fake, None) == 2
+    assert b"rotation" in L.tact_last_error()
 
 
 def test_zero_units_is_a_noop():

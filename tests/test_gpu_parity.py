@@ -6,12 +6,14 @@ seeded synthetic inputs and compares with the oracle on the same inputs:
   * variances:              <= 1e-6 relative per bin (fp32 sum of squares)
   * bits:                   bit-exact given identical variances
   * codes / records:        byte-exact given identical coefficients, gains
-                            and bits (both sides decide in fp32)
+                            and bits (both sides decide in fp32; the stage
+                            entry points quantize without the rotation)
   * unpack:                 byte-exact; dequantize within 1 fp32 rounding
   * decompress:             bf16 outputs equal except 1-ulp differences on
                             <= 0.1% of entries (rounding of a ~1e-6 error)
   * end to end:             bits equal except at the cut, codes >= 99.99%
-                            equal with mismatches next to a threshold, and
+                            equal with mismatches next to a threshold (of
+                            the rotated value when the rotation is on), and
                             round-trip MSE within 1e-3 relative.
 """
 import math
@@ -39,6 +41,10 @@ def _geom(S, H, W, hk, d, budget, bmax=8, dtype=torch.bfloat16, **kw):
 
 def _oparams(g):
     return O.Params(g.S, g.H, g.W, g.kv_heads, g.head_dim, g.budget_bits, g.max_bits)
+
+
+def _orot(g):
+    return "hadamard" if g.rotation == tact.ROTATION_HADAMARD else "none"
 
 
 def _units(g, n, seed=0, scale_spike=True):
@@ -91,6 +97,13 @@ def test_dct_forward_and_inverse(geo):
         assert e <= 1e-5
         # forward then inverse: two transforms, each within 1e-5
         assert _rel(y[u], xs[u]) <= 2e-5
+
+
+# W beyond 32: the H and W axes run as separate passes
+GEOMS_AXIS_PATH = [
+    (3, 5, 40, 1, 128, 2, 8, torch.bfloat16),
+    (2, 36, 3, 2, 64, 1, 8, torch.float32),
+]
 
 
 @pytest.mark.parametrize("axes", [1, 2, 4, 3, 6, 5])
@@ -157,7 +170,7 @@ def test_uniform_allocation():
 
 @pytest.mark.parametrize("geo", GEOMS)
 def test_quantize_pack_byte_exact(geo):
-    g = _geom(*geo)
+    g = _geom(*geo, rotation=0)
     say("quantize", geo)
     op = _oparams(g)
     rng = np.random.default_rng(3)
@@ -181,11 +194,11 @@ def test_quantize_pack_byte_exact(geo):
 
 @pytest.mark.parametrize("geo", GEOMS)
 def test_unpack_and_dequantize(geo):
-    g = _geom(*geo)
+    g = _geom(*geo, rotation=0)
     say("unpack", geo)
     op = _oparams(g)
     x = _units(g, 2, seed=4).float().cpu().numpy().astype(np.float64)
-    recs = np.stack([O.compress(x[u], op) for u in range(2)])
+    recs = np.stack([O.compress(x[u], op, rotation="none") for u in range(2)])
     rt = torch.from_numpy(recs).cuda()
     codes = tact.dbg_unpack(rt, g).cpu().numpy()
     deq = tact.dbg_dequantize(rt, g).cpu().numpy()
@@ -196,17 +209,18 @@ def test_unpack_and_dequantize(geo):
         assert np.all(np.abs(deq[u] - ref) <= 2.0 ** -23 * np.abs(ref))
 
 
-@pytest.mark.parametrize("geo", GEOMS)
-def test_decompress_from_oracle_records(geo):
-    g = _geom(*geo)
-    say("decompress", geo)
+@pytest.mark.parametrize("rot", [1, 0])
+@pytest.mark.parametrize("geo", GEOMS + GEOMS_AXIS_PATH)
+def test_decompress_from_oracle_records(geo, rot):
+    g = _geom(*geo, rotation=rot)
+    say("decompress", geo, "rotation", rot)
     op = _oparams(g)
     x = _units(g, 2, seed=5).float().cpu().numpy().astype(np.float64)
-    recs = np.stack([O.compress(x[u], op) for u in range(2)])
+    recs = np.stack([O.compress(x[u], op, rotation=_orot(g)) for u in range(2)])
     out = tact.decompress(torch.from_numpy(recs).cuda(), g).float().cpu().numpy()
     for u in range(2):
         if g.dtype == torch.bfloat16:
-            exact = O.decompress(recs[u], op, None)
+            exact = O.decompress(recs[u], op, None, rotation=_orot(g))
             ref = O.round_to_bf16(exact)
             a, b = O.bf16_bits(out[u]), O.bf16_bits(ref)
             diff = a != b
@@ -220,11 +234,11 @@ def test_decompress_from_oracle_records(geo):
             rms = math.sqrt(np.mean(exact ** 2))
             assert np.all(np.abs(out[u][diff] - exact[diff]) <= 0.5 * ulp + 1e-5 * rms)
         else:
-            ref = O.decompress(recs[u], op, None)
+            ref = O.decompress(recs[u], op, None, rotation=_orot(g))
             assert _rel(out[u], ref) <= 1e-5
 
 
-def _compare_records(rec_gpu, rec_ref, op, coef_ref):
+def _compare_records(rec_gpu, rec_ref, op, coef_ref, rotation="hadamard"):
     """End-to-end record comparison; returns stats."""
     c1, g1, b1 = O.unpack_record(rec_gpu, op)
     c2, g2, b2 = O.unpack_record(rec_ref, op)
@@ -247,7 +261,11 @@ def _compare_records(rec_gpu, rec_ref, op, coef_ref):
     assert eq.mean() >= 0.9999
     # every mismatching code sits next to a decision threshold
     if (~eq).any():
-        u = coef_ref[same][~eq] / g2[same][:, None].repeat(op.head_dim, 1)[~eq]
+        # the value the quantizer decides on: c / g, rotated
+        u_all = coef_ref[same] / g2[same][:, None].astype(np.float64)
+        if rotation == "hadamard":
+            u_all = O.rotate(u_all)
+        u = u_all[~eq]
         bb = b1[same][:, None].repeat(op.head_dim, 1)[~eq]
         for ui, bi in zip(u, bb):
             _, thr = O.codebook_f32(int(bi))
@@ -257,17 +275,18 @@ def _compare_records(rec_gpu, rec_ref, op, coef_ref):
     return differ.mean(), 1 - eq.mean()
 
 
-@pytest.mark.parametrize("geo", GEOMS)
-def test_compress_end_to_end(geo):
-    g = _geom(*geo)
-    say("compress", geo)
+@pytest.mark.parametrize("rot", [1, 0])
+@pytest.mark.parametrize("geo", GEOMS + GEOMS_AXIS_PATH)
+def test_compress_end_to_end(geo, rot):
+    g = _geom(*geo, rotation=rot)
+    say("compress", geo, "rotation", rot)
     op = _oparams(g)
     x = _units(g, 2, seed=6)
-    rec = tact.compress(x, g.budget_bits, g.max_bits).cpu().numpy()
+    rec = tact.compress(x, g.budget_bits, g.max_bits, rotation=rot).cpu().numpy()
     xs = x.float().cpu().numpy().astype(np.float64)
     for u in range(2):
-        ref = O.compress(xs[u], op)
-        _compare_records(rec[u], ref, op, O.dct3_forward(xs[u]))
+        ref = O.compress(xs[u], op, rotation=_orot(g))
+        _compare_records(rec[u], ref, op, O.dct3_forward(xs[u]), _orot(g))
 
 
 def _roundtrip_check(x_gpu, g, units=None):
@@ -275,7 +294,7 @@ def _roundtrip_check(x_gpu, g, units=None):
     axes = tuple(a for a in range(3) if g.axes & (1 << a))
     alloc = "uniform" if g.alloc_mode == tact.ALLOC_UNIFORM else "waterfill"
     out, rec = tact.roundtrip(x_gpu, g.budget_bits, g.max_bits, axes=g.axes,
-                              alloc_mode=g.alloc_mode)
+                              alloc_mode=g.alloc_mode, rotation=g.rotation)
     units = range(x_gpu.shape[0]) if units is None else units
     for u in units:
         xs = x_gpu[u].float().cpu().numpy().astype(np.float64)
@@ -284,19 +303,41 @@ def _roundtrip_check(x_gpu, g, units=None):
         say(f"  unit {u}: forward rel err {e:.3e}")
         assert e <= 1e-5
         od = "bf16" if g.dtype == torch.bfloat16 else "f32"
-        ref_out, ref_rec = O.roundtrip(xs, op, od, axes, alloc)
+        ref_out, ref_rec = O.roundtrip(xs, op, od, axes, alloc, _orot(g))
         m_gpu = O.mse(out[u].float().cpu().numpy(), xs)
         m_ref = O.mse(ref_out, xs)
         say(f"  unit {u}: mse gpu {m_gpu:.6e} oracle {m_ref:.6e}")
         assert abs(m_gpu / m_ref - 1) <= 1e-3
-        _compare_records(rec[u].cpu().numpy(), ref_rec, op, O.dct3_forward(xs, axes))
+        _compare_records(rec[u].cpu().numpy(), ref_rec, op, O.dct3_forward(xs, axes), _orot(g))
 
 
-@pytest.mark.parametrize("geo", GEOMS)
+@pytest.mark.parametrize("geo", GEOMS + GEOMS_AXIS_PATH)
 def test_roundtrip_small(geo):
     g = _geom(*geo)
     say("roundtrip", geo)
     _roundtrip_check(_units(g, 3, seed=7), g)
+
+
+@pytest.mark.parametrize("geo", [GEOMS[1], GEOMS[3], GEOMS_AXIS_PATH[0]])
+def test_roundtrip_without_rotation(geo):
+    # the rotation ablation: the normalized coefficients quantized as they are
+    g = _geom(*geo, rotation=0)
+    say("roundtrip no rotation", geo)
+    _roundtrip_check(_units(g, 2, seed=13), g)
+
+
+def test_rotation_spreads_a_spike_channel():
+    # one channel x64 louder than the rest: at 8 bits the identity clips it,
+    # the rotation spreads it over the 64 coordinates of its word
+    g = _geom(4, 8, 8, 2, 64, 8, 8, dtype=torch.float32)
+    x = _units(g, 1, seed=14, scale_spike=False)
+    x[..., 0, 5] *= 64.0
+    e = {}
+    for rot in (0, 1):
+        out, _ = tact.roundtrip(x, 8, 8, rotation=rot)
+        e[rot] = O.mse(out[0].cpu().numpy(), x[0].cpu().numpy())
+    say("spike mse", e)
+    assert e[1] < 0.1 * e[0]
 
 
 @pytest.mark.parametrize("axes", [1, 2, 4, 3, 5, 6])
