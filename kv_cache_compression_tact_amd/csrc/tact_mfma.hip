@@ -70,11 +70,26 @@ __device__ __forceinline__ void split2(float x, _Float16& hi, _Float16& lo) {
   lo = static_cast<_Float16>(x - static_cast<float>(hi));
 }
 
-// max over the 4 lane groups that hold the K ranges of one column
+// max over the 4 lane groups that hold the K ranges of one column: the
+// permlane swaps exchange lanes l and l ^ 32 (then l ^ 16) between two
+// copies of v, so the max of the two results is the pairwise max
 __device__ __forceinline__ float column_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(m);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Sum over the 16 lanes of each row (every lane gets the row sum): adds of
+// rotated copies (DPP row rotate by 8, 4, 2, 1).
+__device__ __forceinline__ float row_sum16(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xF, 0xF, true));
+  return x;
 }
 
 __device__ __forceinline__ uint16_t bf16_rne_bits(float v) {
@@ -155,6 +170,29 @@ __device__ __forceinline__ void wht64(float& a0, float& a1, float& a2, float& a3
     x = fmaf(lane_xor8(x), w.sg[3], x);
     *v[q] = x;
   }
+}
+
+// Raw buffer access (descriptor word 3 of gfx9 raw buffers): loads past
+// the descriptor's byte range return 0 and stores past it are dropped, so
+// padded rows need no branch.  voff is per lane, soff uniform.
+constexpr int kBufWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufWord3);
+}
+__device__ __forceinline__ float4 buf_ld4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, int voff, int soff, float4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint32_t __attribute__((ext_vector_type(4))), v),
+                                         r, voff, soff, 0);
+}
+
+// 128-bit LDS access at a float offset that is a multiple of 4
+__device__ __forceinline__ float4 lds_ld4(const float* p) {
+  return *static_cast<const float4*>(__builtin_assume_aligned(p, 16));
+}
+__device__ __forceinline__ void lds_st4(float* p, float4 v) {
+  *static_cast<float4*>(__builtin_assume_aligned(p, 16)) = v;
 }
 
 // Number of the 2^b - 1 ascending thresholds (LDS copy) that are <= u.
@@ -244,8 +282,8 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
   constexpr int ZROW = 16 * TPW + 4;
   // rows staged at once: at most 32 for the widest heads (LDS budget)
   constexpr int ZROWS = (TPW == 16 && NP > 32) ? 32 : NP;
-  __shared__ float s_z[(EPI == EPI_QUANT) ? 4 * ZROWS * ZROW : 1];
-  __shared__ float s_d[(PRO == PRO_DEQUANT) ? 4 * NP * 68 : 1];
+  __shared__ __attribute__((aligned(16))) float s_z[(EPI == EPI_QUANT) ? 4 * ZROWS * ZROW : 1];
+  __shared__ __attribute__((aligned(16))) float s_d[(PRO == PRO_DEQUANT) ? 4 * NP * 68 : 1];
   if constexpr (PRO == PRO_DEQUANT || EPI == EPI_QUANT) {
     if constexpr (PRO == PRO_DEQUANT)
       for (int j = threadIdx.x; j < TACT_CODEBOOK_LEVELS; j += blockDim.x) s_levels[j] = c_levels[j];
@@ -363,7 +401,7 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
         for (int v = 0; v < F::KV; ++v) {
           const int n = ks * F::KPER + F::KV * g + v;
           float4 q = float4{0.f, 0.f, 0.f, 0.f};
-          if (n < N) q = *reinterpret_cast<const float4*>(dt + n * 68 + TPW * t);
+          if (n < N) q = lds_ld4(dt + n * 68 + TPW * t);
           xv[0][ks][v] = q.x;
           xv[1][ks][v] = q.y;
           xv[2][ks][v] = q.z;
@@ -507,8 +545,7 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
           float sq = 0.f;
 #pragma unroll
           for (int i = 0; i < TPW; ++i) sq = fmaf(acc[i][m][rr], acc[i][m][rr], sq);
-#pragma unroll
-          for (int off = 8; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, kWave);
+          sq = row_sum16(sq);
           const int k = 16 * m + 4 * g + rr;
           if (t == 0 && k < N) a.var[u * a.var_stride + bin0 + k * bins_per_k] = sq;
         }
@@ -706,7 +743,10 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
   static_assert(!ROT || MODE != MODE_STATS, "the variance does not see the rotation");
   using FH = Frag<NPH>;
   using FW = Frag<NPW>;
-  extern __shared__ float plane[];          // [H][W][64] fp32
+  // [H][W][64] fp32; 16-byte aligned so that float4 accesses are single
+  // 128-bit LDS operations (a 16-lane group then covers all 64 banks once)
+  extern __shared__ float4 plane_v4[];
+  float* plane = reinterpret_cast<float*>(plane_v4);
   __shared__ float s_cb[(MODE == MODE_QUANT) ? TACT_CODEBOOK_THRESHOLDS
                                              : (MODE == MODE_DEQUANT ? TACT_CODEBOOK_LEVELS : 1)];
   const int lane = threadIdx.x % kWave;
@@ -727,6 +767,10 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
     return ((static_cast<int64_t>(s) * H + kh) * W + kw) * a.kv_heads + head;
   };
   const int64_t vol = u * a.ustride + static_cast<int64_t>(s) * H * W * a.C;   // (s, 0, 0, 0)
+  // byte strides of the slice: one w step, one h row; this lane's columns
+  const int cbytes = static_cast<int>(a.C) * 4;
+  const int row_bytes = W * cbytes;
+  const int lane_col = static_cast<int>(c0 + 4 * t) * 4;
   // rotation constants: lane butterflies; s_j of the lane's channels 4t + i
   // (sgn, with the first forward contraction) and the scale after the W
   // contraction (post_w: the butterflies' sign and 1/8, and s_j inverse)
@@ -751,15 +795,16 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
     // ---- H axis: global -> LDS; a wave owns the columns of one w --------
     typename FH::vec ahi[FH::MT][FH::KSTEPS], alo[FH::MT][FH::KSTEPS];
     load_afrag<NPH>(a.tab + 1 * 4096, 0, t, g, ahi, alo);
+    // the slice (s) of this unit as a buffer: rows h >= H read as 0
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(a.in + vol, row_bytes * H);
     for (int w = wv; w < W; w += kPlaneWaves) {
       float xv[4][FH::KSTEPS][FH::KV];
+      const int voff = (FH::KV * g * W + w) * cbytes + lane_col;
 #pragma unroll
       for (int ks = 0; ks < FH::KSTEPS; ++ks)
 #pragma unroll
         for (int v = 0; v < FH::KV; ++v) {
-          const int h = ks * FH::KPER + FH::KV * g + v;
-          float4 q = float4{0.f, 0.f, 0.f, 0.f};
-          if (h < H) q = *reinterpret_cast<const float4*>(a.in + vol + (static_cast<int64_t>(h) * W + w) * a.C + c0 + 4 * t);
+          const float4 q = buf_ld4(rin, voff, (ks * FH::KPER + v) * row_bytes);
           xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
         }
       f32x4 acc[4][FH::MT];
@@ -771,8 +816,8 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
         for (int rr = 0; rr < 4; ++rr) {
           const int kh = 16 * m + 4 * g + rr;
           if (kh < H)
-            *reinterpret_cast<float4*>(plane + (kh * W + w) * 64 + 4 * t) =
-                float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]};
+            lds_st4(plane + (kh * W + w) * 64 + 4 * t,
+                    float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
         }
     }
     __syncthreads();
@@ -787,7 +832,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
         for (int v = 0; v < FW::KV; ++v) {
           const int w = ks * FW::KPER + FW::KV * g + v;
           float4 q = float4{0.f, 0.f, 0.f, 0.f};
-          if (w < W) q = *reinterpret_cast<const float4*>(plane + (kh * W + w) * 64 + 4 * t);
+          if (w < W) q = lds_ld4(plane + (kh * W + w) * 64 + 4 * t);
           xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
         }
       f32x4 acc[4][FW::MT];
@@ -800,6 +845,9 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
         contract4<NPW>(bhi_w, blo_w, xv, acc, kOne);
       }
       if constexpr (MODE == MODE_STATS) {
+        // partial sums of bin (s, kh, kw, head): kw steps kv_heads * parts
+        float* vrow = a.var_part + u * a.var_stride + bin_of3(kh, 0) * a.parts + half;
+        const int kw_step = a.kv_heads * a.parts;
 #pragma unroll
         for (int m = 0; m < FW::MT; ++m)
 #pragma unroll
@@ -807,11 +855,9 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
             float sq = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) sq = fmaf(acc[i][m][rr], acc[i][m][rr], sq);
-#pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, kWave);
+            sq = row_sum16(sq);
             const int kw = 16 * m + 4 * g + rr;
-            if (t == 0 && kw < W)
-              a.var_part[u * a.var_stride + bin_of3(kh, kw) * a.parts + half] = sq;
+            if (t == 0 && kw < W) vrow[kw * kw_step] = sq;
           }
       } else {
         // stage the coefficients bin-major in this wave's own plane row
@@ -825,8 +871,8 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
           for (int rr = 0; rr < 4; ++rr) {
             const int kw = 16 * m + 4 * g + rr;
             if (kw < W)
-              *reinterpret_cast<float4*>(zt + kw * 64 + 4 * t) =
-                  float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]};
+              lds_st4(zt + kw * 64 + 4 * t,
+                      float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
           }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -921,7 +967,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
         for (int v = 0; v < FW::KV; ++v) {
           const int kw = ks * FW::KPER + FW::KV * g + v;
           float4 q = float4{0.f, 0.f, 0.f, 0.f};
-          if (kw < W) q = *reinterpret_cast<const float4*>(row + kw * 64 + 4 * t);
+          if (kw < W) q = lds_ld4(row + kw * 64 + 4 * t);
           xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
         }
       f32x4 acc[4][FW::MT];
@@ -941,12 +987,13 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
         for (int rr = 0; rr < 4; ++rr) {
           const int w = 16 * m + 4 * g + rr;
           if (w < W)
-            *reinterpret_cast<float4*>(row + w * 64 + 4 * t) =
-                float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]};
+            lds_st4(row + w * 64 + 4 * t,
+                    float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
         }
     }
     __syncthreads();
     // ---- inverse H: LDS -> global; a wave owns the columns of one w -------
+    const __amdgpu_buffer_rsrc_t rout = make_rsrc(a.out + vol, static_cast<int64_t>(row_bytes) * H);
     typename FH::vec ahi_h[FH::MT][FH::KSTEPS], alo_h[FH::MT][FH::KSTEPS];
     load_afrag<NPH>(a.tab + 1 * 4096, 1, t, g, ahi_h, alo_h);
     for (int w = wv; w < W; w += kPlaneWaves) {
@@ -957,20 +1004,19 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
         for (int v = 0; v < FH::KV; ++v) {
           const int kh = ks * FH::KPER + FH::KV * g + v;
           float4 q = float4{0.f, 0.f, 0.f, 0.f};
-          if (kh < H) q = *reinterpret_cast<const float4*>(plane + (kh * W + w) * 64 + 4 * t);
+          if (kh < H) q = lds_ld4(plane + (kh * W + w) * 64 + 4 * t);
           xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
         }
       f32x4 acc[4][FH::MT];
       contract4<NPH>(ahi_h, alo_h, xv, acc, kOne);
+      // rows h >= H fall past the buffer's range and are dropped
+      const int voff = (4 * g * W + w) * cbytes + lane_col;
 #pragma unroll
       for (int m = 0; m < FH::MT; ++m)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int h = 16 * m + 4 * g + rr;
-          if (h < H)
-            *reinterpret_cast<float4*>(a.out + vol + (static_cast<int64_t>(h) * W + w) * a.C + c0 + 4 * t) =
-                float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]};
-        }
+        for (int rr = 0; rr < 4; ++rr)
+          buf_st4(rout, voff, (16 * m + rr) * row_bytes,
+                  float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
     }
   }
 }
