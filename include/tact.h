@@ -94,6 +94,8 @@ enum { TACT_ALLOC_WATERFILL = 0, TACT_ALLOC_UNIFORM = 1 };
 enum { TACT_ROTATION_NONE = 0, TACT_ROTATION_HADAMARD = 1 };
 
 typedef struct {
+  /* A unit (S * H * W * kv_heads * head_dim entries) holds at most 2^29
+   * entries; larger units are TACT_ERR_UNSUPPORTED. */
   int32_t S, H, W;      /* grid of the vision encoder, each 1..64            */
   int32_t kv_heads;     /* 1..64                                             */
   int32_t head_dim;     /* 64, 128 or 256                                    */

@@ -75,6 +75,10 @@ tact_status make_geometry(const tact_params* p, Geometry* g) {
   G.dtype = p->dtype;
   G.n_bins = int64_t(p->S) * p->H * p->W * p->kv_heads;
   G.n_entries = G.n_bins * p->head_dim;
+  if (G.n_entries > (int64_t(1) << 29))
+    return fail(TACT_ERR_UNSUPPORTED,
+                "unit of %lld entries: at most 2^29 per unit (32-bit byte offsets)",
+                static_cast<long long>(G.n_entries));
   G.total_bits = int64_t(p->budget_bits) * G.n_bins;
   G.n_groups = (G.n_bins + 63) / 64;
   G.code_bytes = G.total_bits * p->head_dim / 8;

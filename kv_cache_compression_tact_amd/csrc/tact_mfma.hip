@@ -325,9 +325,58 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
   const int64_t obase = o * static_cast<int64_t>(N) * a.inner;
   const int64_t bins_per_k = (a.inner / a.C) * a.kv_heads;   // bin step per frequency
 
+  // Plain passes (interleaved columns): rows n of this (unit, o) through a
+  // buffer of N rows, so rows n >= N read 0 and output rows k >= N are
+  // dropped; byte offsets fit 32 bits (a unit holds at most 2^29 entries).
+  // The next column group's rows are fetched while this one is computed.
+  constexpr bool PF = INTL && PRO != PRO_DEQUANT;
+  constexpr int ES_IN = (PRO == PRO_BF16) ? 2 : 4;
+  constexpr int ES_OUT = (EPI == EPI_BF16) ? 2 : 4;
+  const int row_in = static_cast<int>(a.inner) * ES_IN;
+  const int row_out = static_cast<int>(a.inner) * ES_OUT;
+  const __amdgpu_buffer_rsrc_t rin = make_rsrc(
+      PF ? static_cast<const char*>(a.in) + (u * a.in_ustride + obase) * ES_IN : nullptr,
+      PF ? static_cast<int64_t>(row_in) * N : 0);
+  const __amdgpu_buffer_rsrc_t rout = make_rsrc(
+      INTL ? static_cast<const char*>(a.out) + (u * a.out_ustride + obase) * ES_OUT : nullptr,
+      INTL ? static_cast<int64_t>(row_out) * N : 0);
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  auto fetch = [&](int64_t grp_, u32x4 (&r)[F::KSTEPS][F::KV]) {
+    const int vo = F::KV * g * row_in + static_cast<int>(grp_ * (16 * TPW) + TPW * t) * ES_IN;
+#pragma unroll
+    for (int ks = 0; ks < F::KSTEPS; ++ks)
+#pragma unroll
+      for (int v = 0; v < F::KV; ++v) {
+        const int so = (ks * F::KPER + v) * row_in;
+        if constexpr (TPW * ES_IN == 16) {
+          r[ks][v] = __builtin_amdgcn_raw_buffer_load_b128(rin, vo, so, 0);
+        } else {
+          const auto q = __builtin_amdgcn_raw_buffer_load_b64(rin, vo, so, 0);
+          r[ks][v] = u32x4{q[0], q[1], 0u, 0u};
+        }
+      }
+  };
+  const int64_t grp_step = static_cast<int64_t>(gridDim.x) * 4;
+  u32x4 cur[PF ? F::KSTEPS : 1][PF ? F::KV : 1];
+  if constexpr (PF) {
+    const int64_t g0 = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+    if (g0 < groups) fetch(g0, cur);
+  }
+
   for (int64_t grp = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave; grp < groups;
-       grp += static_cast<int64_t>(gridDim.x) * 4) {
+       grp += grp_step) {
     const int64_t c0 = grp * (16 * TPW);
+    u32x4 nxt[PF ? F::KSTEPS : 1][PF ? F::KV : 1];
+    if constexpr (PF) {
+      if (grp + grp_step < groups) {
+        fetch(grp + grp_step, nxt);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < F::KSTEPS; ++ks)
+#pragma unroll
+          for (int v = 0; v < F::KV; ++v) nxt[ks][v] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
     // bin of frequency k at this column start: bin0 + k * bins_per_k
     const int64_t bin0 =
         (o * N * (a.inner / a.C) + c0 / a.C) * a.kv_heads + (c0 % a.C) / a.head_dim;
@@ -338,7 +387,7 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
 #pragma unroll
       for (int m = 0; m < F::MT; ++m) acc[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    float xv[TPW][F::KSTEPS][F::KV];
+    float xv[PF ? 1 : TPW][F::KSTEPS][F::KV];
     if constexpr (PRO == PRO_DEQUANT) {
       // first inverse axis: coefficients come from the record
       const uint8_t* r = a.rec.base + u * a.rec.stride;
@@ -416,38 +465,7 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
             wht64(xv[0][ks][v], xv[1][ks][v], xv[2][ks][v], xv[3][ks][v], wl);
       }
     } else if constexpr (INTL) {
-      // TPW consecutive elements per lane: one 16-byte vector per row
-#pragma unroll
-      for (int ks = 0; ks < F::KSTEPS; ++ks)
-#pragma unroll
-        for (int v = 0; v < F::KV; ++v) {
-          const int n = ks * F::KPER + F::KV * g + v;
-          if (n < N) {
-            const int64_t idx = u * a.in_ustride + obase + n * col_stride + c0 + TPW * t;
-            if constexpr (PRO == PRO_BF16) {
-              uint32_t w4[4];
-              if constexpr (TPW == 8) {
-                const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.in) + idx);
-                w4[0] = q.x; w4[1] = q.y; w4[2] = q.z; w4[3] = q.w;
-              } else {
-                const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.in) + idx);
-                w4[0] = q.x; w4[1] = q.y; w4[2] = 0; w4[3] = 0;
-              }
-#pragma unroll
-              for (int i = 0; i < TPW; ++i)
-                xv[i][ks][v] = __uint_as_float((i & 1) ? (w4[i / 2] & 0xFFFF0000u) : (w4[i / 2] << 16));
-            } else {
-              const float4 q = *reinterpret_cast<const float4*>(static_cast<const float*>(a.in) + idx);
-              xv[0][ks][v] = q.x;
-              xv[1][ks][v] = q.y;
-              xv[2][ks][v] = q.z;
-              xv[3][ks][v] = q.w;
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < TPW; ++i) xv[i][ks][v] = 0.f;
-          }
-        }
+      // rows come from the prefetch registers (cur), one tile at a time
     } else {
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
@@ -472,11 +490,26 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
 
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
+      // tile i: column c0 + TPW t + i (interleaved) or c0 + 16 i + t
+      float xi[F::KSTEPS][F::KV];
+#pragma unroll
+      for (int ks = 0; ks < F::KSTEPS; ++ks)
+#pragma unroll
+        for (int v = 0; v < F::KV; ++v) {
+          if constexpr (PF && PRO == PRO_BF16) {
+            const uint32_t w = cur[ks][v][i / 2];
+            xi[ks][v] = __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+          } else if constexpr (PF) {
+            xi[ks][v] = __uint_as_float(cur[ks][v][i]);
+          } else {
+            xi[ks][v] = xv[i][ks][v];
+          }
+        }
       float mx = 0.f;
 #pragma unroll
       for (int ks = 0; ks < F::KSTEPS; ++ks)
 #pragma unroll
-        for (int v = 0; v < F::KV; ++v) mx = fmaxf(mx, fabsf(xv[i][ks][v]));
+        for (int v = 0; v < F::KV; ++v) mx = fmaxf(mx, fabsf(xi[ks][v]));
       mx = column_max(mx);
       // scale 2^(14 - e) puts the column maximum m = f 2^e in [2^13, 2^14);
       // output scale: 2^-12 (matrix) * 2^(e - 14) (column)
@@ -490,7 +523,7 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
 #pragma unroll
         for (int v = 0; v < F::KV; ++v) {
           _Float16 h, l;
-          split2(xv[i][ks][v] * sc, h, l);
+          split2(xi[ks][v] * sc, h, l);
           bhi[v] = h;
           blo[v] = l;
         }
@@ -509,30 +542,30 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
 
     // ---- epilogues ---------------------------------------------------------
     if constexpr (EPI == EPI_F32 || EPI == EPI_BF16) {
+      // output row k = 16 m + 4 g + rr; rows k >= N fall past the buffer
+      const int vo = 4 * g * row_out + static_cast<int>(c0 + TPW * t) * ES_OUT;
 #pragma unroll
       for (int m = 0; m < F::MT; ++m)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int k = 16 * m + 4 * g + rr;
-          if (k < N) {
-            const int64_t idx = u * a.out_ustride + obase + k * col_stride + c0 + TPW * t;
-            if constexpr (EPI == EPI_F32) {
-              float* dst = static_cast<float*>(a.out) + idx;
+          const int so = (16 * m + rr) * row_out;
+          if constexpr (EPI == EPI_F32) {
 #pragma unroll
-              for (int i = 0; i < TPW; i += 4)
-                *reinterpret_cast<float4*>(dst + i) =
-                    float4{acc[i][m][rr], acc[i + 1][m][rr], acc[i + 2][m][rr], acc[i + 3][m][rr]};
-            } else {
-              uint16_t* dst = static_cast<uint16_t*>(a.out) + idx;
+            for (int i = 0; i < TPW; i += 4)
+              buf_st4(rout, vo + 4 * i, so,
+                      float4{acc[i][m][rr], acc[i + 1][m][rr], acc[i + 2][m][rr], acc[i + 3][m][rr]});
+          } else {
+            uint32_t w[TPW / 2];
 #pragma unroll
-              for (int i = 0; i < TPW; i += 4) {
-                const uint32_t lo = bf16_rne_bits(acc[i][m][rr]) |
-                                    (static_cast<uint32_t>(bf16_rne_bits(acc[i + 1][m][rr])) << 16);
-                const uint32_t hi = bf16_rne_bits(acc[i + 2][m][rr]) |
-                                    (static_cast<uint32_t>(bf16_rne_bits(acc[i + 3][m][rr])) << 16);
-                *reinterpret_cast<uint2*>(dst + i) = uint2{lo, hi};
-              }
-            }
+            for (int i = 0; i < TPW; i += 2)
+              w[i / 2] = bf16_rne_bits(acc[i][m][rr]) |
+                         (static_cast<uint32_t>(bf16_rne_bits(acc[i + 1][m][rr])) << 16);
+            if constexpr (TPW == 8)
+              __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, rout, vo, so, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b64(
+                  __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))), uint2{w[0], w[1]}),
+                  rout, vo, so, 0);
           }
         }
     } else if constexpr (EPI == EPI_STATS) {
@@ -620,6 +653,12 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
       }
+    }
+    if constexpr (PF) {
+#pragma unroll
+      for (int ks = 0; ks < F::KSTEPS; ++ks)
+#pragma unroll
+        for (int v = 0; v < F::KV; ++v) cur[ks][v] = nxt[ks][v];
     }
   }
 }

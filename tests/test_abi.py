@@ -71,6 +71,17 @@ def test_invalid_params_rejected(field, value, status):
     assert len(lib().tact_last_error()) > 0
 
 
+def test_unit_size_cap():
+    # at most 2^29 entries per unit
+    big = _params(S=64, H=64, W=64, kv_heads=32, head_dim=64)     # 2^29: allowed
+    assert lib().tact_record_bytes(ctypes.byref(big)) > 0
+    bigger = _params(S=64, H=64, W=64, kv_heads=64, head_dim=64)  # 2^30
+    assert lib().tact_record_bytes(ctypes.byref(bigger)) == 0
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib().tact_compress(ctypes.byref(bigger), 1, fake, 1 << 30, fake, fake, 1 << 40,
+                               None) == 2
+
+
 def test_null_and_misaligned_pointers_rejected():
     p = _params()
     ws = lib().tact_workspace_bytes(ctypes.byref(p), 2)
