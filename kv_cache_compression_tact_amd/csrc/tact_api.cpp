@@ -220,14 +220,14 @@ void compress_chunk(const Geometry& g, int64_t cn, const void* kv, int64_t kv_st
   const float inv_d = 1.0f / static_cast<float>(g.head_dim);
   if (g.axes == TACT_AXES_ALL && plane_supported(g)) {
     // S on the matrix cores into the fp32 volume, then H and W fused in LDS
+    // (the final coefficients replace the volume), the allocation, and one
+    // streaming pass over the coded bins
     launch_axis(g, cn, 0, 0, in_pro, AX_EPI_F32, kv, kv_stride, w.coef, g.n_entries, w.tab,
                 nullptr, nullptr, 0, none, nullptr, s);
-    launch_plane(g, cn, 0, w.coef, nullptr, g.n_entries, w.tab, w.var, vs, nullptr, none,
-                 nullptr, s);
+    launch_plane(g, cn, 0, w.coef, w.coef, g.n_entries, w.tab, w.var, vs, none, nullptr, s);
     launch_allocate2(g, cn, w.var, vs, static_cast<int>(var_parts(g)), inv_d, nullptr,
                      view(g, recs), w.poff, w.invg, s);
-    launch_plane(g, cn, 1, w.coef, nullptr, g.n_entries, w.tab, nullptr, vs, w.invg,
-                 view(g, recs), w.poff, s);
+    launch_quant(g, cn, w.coef, g.n_entries, w.invg, vs, view(g, recs), w.poff, s);
     return;
   }
   int ax[3];
@@ -261,8 +261,7 @@ void decompress_chunk(const Geometry& g, int64_t cn, const uint8_t* recs, void* 
   const int out_epi = g.dtype == TACT_BF16 ? AX_EPI_BF16 : AX_EPI_F32;
   launch_plane_offsets(g, cn, rv, w.poff, s);
   if (g.axes == TACT_AXES_ALL && plane_supported(g)) {
-    launch_plane(g, cn, 2, nullptr, w.coef, g.n_entries, w.tab, nullptr, 0, nullptr, rv,
-                 w.poff, s);
+    launch_plane(g, cn, 2, nullptr, w.coef, g.n_entries, w.tab, nullptr, 0, rv, w.poff, s);
     launch_axis(g, cn, 0, 1, AX_PRO_F32, out_epi, w.coef, g.n_entries, out, out_stride, w.tab,
                 nullptr, nullptr, 0, rv, w.poff, s);
     return;

@@ -93,13 +93,19 @@ void launch_allocate2(const Geometry& g, int64_t n_units, const float* var, int6
                       int parts, float var_scale, uint8_t* bits_out, RecordView rec,
                       uint32_t* plane_off, float* inv_gain, hipStream_t stream);
 
-// Fused H and W axes (see tact_mfma.hip); mode 0 = variance partial sums,
-// 1 = quantize + pack, 2 = decode + inverse.
+// Fused H and W axes (see tact_mfma.hip); mode 0 = forward: coefficients
+// to `out` (may equal `in`) and variance partial sums; 2 = decode + inverse.
 bool plane_supported(const Geometry& g);
 void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in, float* out,
                   int64_t ustride, const float* tab, float* var_part, int64_t var_stride,
-                  const float* inv_gain, RecordView rec, const uint32_t* plane_off,
-                  hipStream_t stream);
+                  RecordView rec, const uint32_t* plane_off, hipStream_t stream);
+
+// Quantize + pack the final coefficients coef ([u][bin][head_dim], unit
+// stride ustride) into the records, given 1/gain and first planes
+// (tact_quant.hip).
+void launch_quant(const Geometry& g, int64_t n_units, const float* coef, int64_t ustride,
+                  const float* inv_gain, int64_t var_stride, RecordView rec,
+                  const uint32_t* plane_off, hipStream_t stream);
 
 // Per-bin first planes from the bits stored in records.
 void launch_plane_offsets(const Geometry& g, int64_t n_units, RecordView rec,

@@ -664,24 +664,25 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_plane: the H and W axes of one (unit, slice s, 64-channel slab) in one
-// block.  The H x W x 64 plane lives in LDS between the two contractions,
-// so the fp32 volume crosses HBM once per direction instead of twice.
-//   forward (MODE_STATS / MODE_QUANT): H from global memory into LDS, then
-//     W from LDS with the variance epilogue (per-slab partial sums of
-//     squares) or the quantize + pack epilogue (one 64-bit code word per
-//     plane per bin: the slab is one word wide);
+// k_plane: the H and W axes of one (unit, slice s, 64-channel slab) at a
+// time in one block.  The H x W x 64 plane lives in LDS between the two
+// contractions, so the fp32 volume crosses HBM once per direction instead
+// of twice.
+//   forward (MODE_STATS): H from global memory into LDS, then W from LDS;
+//     the final coefficients go back over the input (in place) together
+//     with per-slab partial sums of squares of every bin;
 //   inverse (MODE_DEQUANT): decode + inverse W into LDS, then inverse H
 //     to global memory.
-// 16 waves; a wave owns whole rows of the plane (one w in the first
-// contraction, one kh in the second), so its LDS rows need no barrier
-// beyond the one between the two contractions.
+// A wave owns whole rows of the plane (w columns in the first contraction,
+// kh rows in the second), so its LDS rows need no barrier beyond the one
+// between the two contractions.
 // ---------------------------------------------------------------------------
-enum PlaneMode { MODE_STATS = 0, MODE_QUANT = 1, MODE_DEQUANT = 2 };
+enum PlaneMode { MODE_STATS = 0, MODE_DEQUANT = 2 };
 
 struct PlaneArgs {
   const float* in;           // forward: the volume after the S axis; unused inverse
-  float* out;                // inverse: the volume before the inverse S axis
+  float* out;                // forward: the coefficients (may equal in);
+                             // inverse: the volume before the inverse S axis
   int64_t ustride;           // elements between units of in / out
   const float* tab;          // tab[3][64][64]
   int S, H, W;
@@ -691,10 +692,10 @@ struct PlaneArgs {
   int max_bits;
   float* var_part;           // MODE_STATS: raw sums of squares, [u][bin][part]
   int parts;                 // head_dim / 64
-  int64_t var_stride;        // floats per unit in var_part / inv_gain
-  const float* inv_gain;     // MODE_QUANT
+  int64_t var_stride;        // floats per unit in var_part
   RecordView rec;
   const uint32_t* plane_off;
+  int64_t n_units;
 };
 
 template <int NP>
@@ -775,287 +776,365 @@ __device__ __forceinline__ void rotate_frag(float (&xv)[4][Frag<NP>::KSTEPS][Fra
       wht64(xv[0][ks][v], xv[1][ks][v], xv[2][ks][v], xv[3][ks][v], w);
 }
 
-constexpr int kPlaneWaves = 16;
+// Persistent blocks of 8 waves (256 VGPRs each): a block walks the planes
+// blockIdx.x, blockIdx.x + gridDim.x, ...  While plane p is transformed,
+// the data of plane p + gridDim.x is fetched into the registers the wave
+// has just consumed (forward: the H columns of its w; inverse: the record
+// words and side info of its kh rows), so memory and compute overlap.
+constexpr int kPlaneWaves = 8;
 
-template <int NPH, int NPW, int MODE, bool ROT>
+// DCT fragments of one contraction (hi / lo per lane) kept in LDS: built
+// once per block, read back right before each contraction
+template <int NP>
+struct FragLds {
+  typename Frag<NP>::vec v[Frag<NP>::MT][Frag<NP>::KSTEPS][2][kWave];
+};
+
+template <int NP>
+__device__ __forceinline__ void frag_to_lds(FragLds<NP>& f, const float* tab, int inverse, int lane) {
+  typename Frag<NP>::vec hi[Frag<NP>::MT][Frag<NP>::KSTEPS], lo[Frag<NP>::MT][Frag<NP>::KSTEPS];
+  load_afrag<NP>(tab, inverse, lane % 16, lane / 16, hi, lo);
+#pragma unroll
+  for (int m = 0; m < Frag<NP>::MT; ++m)
+#pragma unroll
+    for (int ks = 0; ks < Frag<NP>::KSTEPS; ++ks) {
+      f.v[m][ks][0][lane] = hi[m][ks];
+      f.v[m][ks][1][lane] = lo[m][ks];
+    }
+}
+
+// lane offset hidden from the optimizer, so that the fragment reads stay
+// next to their contraction instead of being hoisted into registers
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+template <int NP>
+__device__ __forceinline__ void frag_from_lds(const FragLds<NP>& f, int lane,
+                                              typename Frag<NP>::vec (&hi)[Frag<NP>::MT][Frag<NP>::KSTEPS],
+                                              typename Frag<NP>::vec (&lo)[Frag<NP>::MT][Frag<NP>::KSTEPS]) {
+  const int l = opaque(lane);
+#pragma unroll
+  for (int m = 0; m < Frag<NP>::MT; ++m)
+#pragma unroll
+    for (int ks = 0; ks < Frag<NP>::KSTEPS; ++ks) {
+      hi[m][ks] = f.v[m][ks][0][l];
+      lo[m][ks] = f.v[m][ks][1][l];
+    }
+}
+
+// plane p -> (unit, slice s, 64-channel slab): slab fastest
+struct PlaneId {
+  int64_t u;
+  int s;
+  int64_t c0;      // first channel of the slab
+  int64_t head;
+  int half;        // 64-channel word of the head
+  int64_t vol;     // element offset of (u, s, 0, 0, 0)
+};
+
+__device__ __forceinline__ PlaneId plane_id(const PlaneArgs& a, int64_t p) {
+  const int64_t n_slabs = a.C / 64;
+  PlaneId id;
+  const int64_t slab = p % n_slabs;
+  const int64_t rest = p / n_slabs;
+  id.s = static_cast<int>(rest % a.S);
+  id.u = rest / a.S;
+  id.c0 = slab * 64;
+  id.head = id.c0 / a.head_dim;
+  id.half = static_cast<int>((id.c0 % a.head_dim) / 64);
+  id.vol = id.u * a.ustride + static_cast<int64_t>(id.s) * a.H * a.W * a.C;
+  return id;
+}
+
+template <int NPH, int NPW, int MODE, bool ROT, int SL>
 __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
-  static_assert(!ROT || MODE != MODE_STATS, "the variance does not see the rotation");
+  static_assert(!ROT || MODE == MODE_DEQUANT, "the rotation is undone after dequantization");
   using FH = Frag<NPH>;
   using FW = Frag<NPW>;
+  // w columns (H passes) and kh rows (W passes) per wave: SL covers
+  // ceil(max(H, W) / 8)
+  constexpr int SLW = (SL < NPW / kPlaneWaves) ? SL : NPW / kPlaneWaves;
+  constexpr int SLH = (SL < NPH / kPlaneWaves) ? SL : NPH / kPlaneWaves;
   // [H][W][64] fp32; 16-byte aligned so that float4 accesses are single
   // 128-bit LDS operations (a 16-lane group then covers all 64 banks once)
   extern __shared__ float4 plane_v4[];
   float* plane = reinterpret_cast<float*>(plane_v4);
-  __shared__ float s_cb[(MODE == MODE_QUANT) ? TACT_CODEBOOK_THRESHOLDS
-                                             : (MODE == MODE_DEQUANT ? TACT_CODEBOOK_LEVELS : 1)];
+  __shared__ float s_cb[(MODE == MODE_DEQUANT) ? TACT_CODEBOOK_LEVELS : 1];
   const int lane = threadIdx.x % kWave;
   const int wv = threadIdx.x / kWave;
   const int t = lane % 16, g = lane / 16;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64;
-  const int s = blockIdx.y;
-  const int64_t u = blockIdx.z;
   const int H = a.H, W = a.W;
-  const int64_t head = c0 / a.head_dim;
-  const int half = static_cast<int>((c0 % a.head_dim) / 64);
-  if constexpr (MODE == MODE_QUANT)
-    for (int j = threadIdx.x; j < TACT_CODEBOOK_THRESHOLDS; j += blockDim.x) s_cb[j] = c_thresholds[j];
+  const int64_t n_planes = a.n_units * a.S * (a.C / 64);
+  const int64_t pstep = gridDim.x;
   if constexpr (MODE == MODE_DEQUANT)
     for (int j = threadIdx.x; j < TACT_CODEBOOK_LEVELS; j += blockDim.x) s_cb[j] = c_levels[j];
-  // bin of (s, kh, kw) for this slab's head
-  auto bin_of3 = [&](int kh, int kw) -> int64_t {
-    return ((static_cast<int64_t>(s) * H + kh) * W + kw) * a.kv_heads + head;
-  };
-  const int64_t vol = u * a.ustride + static_cast<int64_t>(s) * H * W * a.C;   // (s, 0, 0, 0)
-  // byte strides of the slice: one w step, one h row; this lane's columns
+  // byte strides of a slice: one w step, one h row; this lane's columns
   const int cbytes = static_cast<int>(a.C) * 4;
   const int row_bytes = W * cbytes;
-  const int lane_col = static_cast<int>(c0 + 4 * t) * 4;
-  // rotation constants: lane butterflies; s_j of the lane's channels 4t + i
-  // (sgn, with the first forward contraction) and the scale after the W
-  // contraction (post_w: the butterflies' sign and 1/8, and s_j inverse)
+  // bin of (s, kh, kw) of a plane's head
+  auto bin_of3 = [&](const PlaneId& id, int kh, int kw) -> int64_t {
+    return ((static_cast<int64_t>(id.s) * H + kh) * W + kw) * a.kv_heads + id.head;
+  };
+  // inverse rotation constants: lane butterflies, and the scale after the
+  // inverse W contraction (the butterflies' sign, 1/8 and s_j of the
+  // lane's channels 4t + i)
   const LaneWht wl(lane);
-  float sgn[4] = {1.f, 1.f, 1.f, 1.f};
   float post_w[4] = {1.f, 1.f, 1.f, 1.f};
   if constexpr (ROT) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float si = rotation_sign(4 * t + i);
-      if constexpr (MODE == MODE_QUANT) {
-        sgn[i] = si;
-        post_w[i] = 0.125f * wl.parity;
-      } else {
-        post_w[i] = 0.125f * wl.parity * si;
-      }
-    }
+    for (int i = 0; i < 4; ++i) post_w[i] = 0.125f * wl.parity * rotation_sign(4 * t + i);
   }
   constexpr float kOne[4] = {1.f, 1.f, 1.f, 1.f};
+  const int wpp = a.head_dim / 64;
+
+  __shared__ FragLds<NPH> s_fh;
+  __shared__ FragLds<NPW> s_fw;
+  if (wv == 0) {
+    frag_to_lds<NPH>(s_fh, a.tab + 1 * 4096, MODE == MODE_DEQUANT, lane);
+    frag_to_lds<NPW>(s_fw, a.tab + 2 * 4096, MODE == MODE_DEQUANT, lane);
+  }
+  __syncthreads();                           // fragments and codebook in LDS
 
   if constexpr (MODE != MODE_DEQUANT) {
-    // ---- H axis: global -> LDS; a wave owns the columns of one w --------
-    typename FH::vec ahi[FH::MT][FH::KSTEPS], alo[FH::MT][FH::KSTEPS];
-    load_afrag<NPH>(a.tab + 1 * 4096, 0, t, g, ahi, alo);
-    // the slice (s) of this unit as a buffer: rows h >= H read as 0
-    const __amdgpu_buffer_rsrc_t rin = make_rsrc(a.in + vol, row_bytes * H);
-    for (int w = wv; w < W; w += kPlaneWaves) {
-      float xv[4][FH::KSTEPS][FH::KV];
-      const int voff = (FH::KV * g * W + w) * cbytes + lane_col;
+    // the H columns (all h, 64 channels) of this wave's w = wv + 8 j
+    float xs[SLW][4][FH::KSTEPS][FH::KV];
+    auto fetch_cols = [&](int64_t p, int j) {
+      const PlaneId id = plane_id(a, p);
+      const int w = wv + kPlaneWaves * j;
+      // the slice as a buffer: rows h >= H read as 0
+      const __amdgpu_buffer_rsrc_t rin = make_rsrc(a.in + id.vol, static_cast<int64_t>(row_bytes) * H);
+      const int voff = (FH::KV * g * W + w) * cbytes + static_cast<int>(id.c0 + 4 * t) * 4;
 #pragma unroll
       for (int ks = 0; ks < FH::KSTEPS; ++ks)
 #pragma unroll
         for (int v = 0; v < FH::KV; ++v) {
           const float4 q = buf_ld4(rin, voff, (ks * FH::KPER + v) * row_bytes);
-          xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
+          xs[j][0][ks][v] = q.x; xs[j][1][ks][v] = q.y; xs[j][2][ks][v] = q.z; xs[j][3][ks][v] = q.w;
         }
-      f32x4 acc[4][FH::MT];
-      // R = H diag(s) / 8: the signs go with the first contraction
-      contract4<NPH>(ahi, alo, xv, acc, sgn);
+    };
+    if (static_cast<int64_t>(blockIdx.x) < n_planes) {
 #pragma unroll
-      for (int m = 0; m < FH::MT; ++m)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int kh = 16 * m + 4 * g + rr;
-          if (kh < H)
-            lds_st4(plane + (kh * W + w) * 64 + 4 * t,
-                    float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
-        }
+      for (int j = 0; j < SLW; ++j)
+        if (wv + kPlaneWaves * j < W) fetch_cols(blockIdx.x, j);
     }
-    __syncthreads();
-    // ---- W axis: LDS -> epilogue; a wave owns the columns of one kh ------
-    typename FW::vec bhi_w[FW::MT][FW::KSTEPS], blo_w[FW::MT][FW::KSTEPS];
-    load_afrag<NPW>(a.tab + 2 * 4096, 0, t, g, bhi_w, blo_w);
-    for (int kh = wv; kh < H; kh += kPlaneWaves) {
-      float xv[4][FW::KSTEPS][FW::KV];
+    for (int64_t p = blockIdx.x; p < n_planes; p += pstep) {
+      const PlaneId id = plane_id(a, p);
+      const bool more = p + pstep < n_planes;
+      const __amdgpu_buffer_rsrc_t rcoef =
+          make_rsrc(a.out + id.vol, static_cast<int64_t>(row_bytes) * H);
+      // ---- H axis: registers -> LDS; then fetch the next plane's columns
 #pragma unroll
-      for (int ks = 0; ks < FW::KSTEPS; ++ks)
+      for (int j = 0; j < SLW; ++j) {
+        const int w = wv + kPlaneWaves * j;
+        if (w >= W) break;
+        f32x4 acc[4][FH::MT];
+        typename FH::vec ahi[FH::MT][FH::KSTEPS], alo[FH::MT][FH::KSTEPS];
+        frag_from_lds<NPH>(s_fh, lane, ahi, alo);
+        contract4<NPH>(ahi, alo, xs[j], acc, kOne);
 #pragma unroll
-        for (int v = 0; v < FW::KV; ++v) {
-          const int w = ks * FW::KPER + FW::KV * g + v;
-          float4 q = float4{0.f, 0.f, 0.f, 0.f};
-          if (w < W) q = lds_ld4(plane + (kh * W + w) * 64 + 4 * t);
-          xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
-        }
-      f32x4 acc[4][FW::MT];
-      if constexpr (ROT) {
-        // H on the channels, then the butterflies' sign and 1/8 after the
-        // (channel-wise) W contraction
-        rotate_frag<NPW>(xv, wl);
-        contract4<NPW>(bhi_w, blo_w, xv, acc, post_w);
-      } else {
-        contract4<NPW>(bhi_w, blo_w, xv, acc, kOne);
-      }
-      if constexpr (MODE == MODE_STATS) {
-        // partial sums of bin (s, kh, kw, head): kw steps kv_heads * parts
-        float* vrow = a.var_part + u * a.var_stride + bin_of3(kh, 0) * a.parts + half;
-        const int kw_step = a.kv_heads * a.parts;
-#pragma unroll
-        for (int m = 0; m < FW::MT; ++m)
+        for (int m = 0; m < FH::MT; ++m)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
-            float sq = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sq = fmaf(acc[i][m][rr], acc[i][m][rr], sq);
-            sq = row_sum16(sq);
-            const int kw = 16 * m + 4 * g + rr;
-            if (t == 0 && kw < W) vrow[kw * kw_step] = sq;
-          }
-      } else {
-        // stage the coefficients bin-major in this wave's own plane row
-        // (row kh is read only by this wave), then one bin at a time
-        float* zt = plane + static_cast<int64_t>(kh) * W * 64;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int m = 0; m < FW::MT; ++m)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int kw = 16 * m + 4 * g + rr;
-            if (kw < W)
-              lds_st4(zt + kw * 64 + 4 * t,
+            const int kh = 16 * m + 4 * g + rr;
+            if (kh < H)
+              lds_st4(plane + (kh * W + w) * 64 + 4 * t,
                       float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
           }
+        if (more) fetch_cols(p + pstep, j);
+      }
+      __syncthreads();
+      // ---- W axis: LDS -> epilogue; a wave owns the columns of one kh ----
+#pragma unroll
+      for (int r = 0; r < SLH; ++r) {
+        const int kh = wv + kPlaneWaves * r;
+        if (kh >= H) break;
+        float xv[4][FW::KSTEPS][FW::KV];
+#pragma unroll
+        for (int ks = 0; ks < FW::KSTEPS; ++ks)
+#pragma unroll
+          for (int v = 0; v < FW::KV; ++v) {
+            const int w = ks * FW::KPER + FW::KV * g + v;
+            float4 q = float4{0.f, 0.f, 0.f, 0.f};
+            if (w < W) q = lds_ld4(plane + (kh * W + w) * 64 + 4 * t);
+            xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
+          }
+        f32x4 acc[4][FW::MT];
+        typename FW::vec bhi_w[FW::MT][FW::KSTEPS], blo_w[FW::MT][FW::KSTEPS];
+        frag_from_lds<NPW>(s_fw, lane, bhi_w, blo_w);
+        contract4<NPW>(bhi_w, blo_w, xv, acc, kOne);
+        {
+          // partial sums of bin (s, kh, kw, head): kw steps kv_heads * parts
+          float* vrow = a.var_part + id.u * a.var_stride + bin_of3(id, kh, 0) * a.parts + id.half;
+          const int kw_step = a.kv_heads * a.parts;
+          // the final coefficients go back over this plane's input
+          const int vo = (kh * W + 4 * g) * cbytes + static_cast<int>(id.c0 + 4 * t) * 4;
+#pragma unroll
+          for (int m = 0; m < FW::MT; ++m)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              float sq = 0.f;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sq = fmaf(acc[i][m][rr], acc[i][m][rr], sq);
+              sq = row_sum16(sq);
+              const int kw = 16 * m + 4 * g + rr;
+              if (t == 0 && kw < W) vrow[kw * kw_step] = sq;
+              if (kw < W)
+                buf_st4(rcoef, vo, (16 * m + rr) * cbytes,
+                        float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
+            }
+        }
+      }
+      __syncthreads();                       // LDS free for the next plane
+    }
+  } else {
+    // side info (bits, first plane, gain) and code words of this wave's kh
+    // rows, lane = kw; fetched one plane ahead
+    int bj[SLH], pjv[SLH];
+    float gjv[SLH];
+    uint2 wd[SLH][8];
+    auto fetch_side = [&](int64_t p) {
+      const PlaneId id = plane_id(a, p);
+      const uint8_t* r = a.rec.base + id.u * a.rec.stride;
+      const uint8_t* bits = r + a.rec.off_bits;
+      const float* gains = reinterpret_cast<const float*>(r + a.rec.off_gains);
+      const uint32_t* poff = a.plane_off + id.u * a.n_bins;
+#pragma unroll
+      for (int q = 0; q < SLH; ++q) {
+        const int kh = wv + kPlaneWaves * q;
+        bj[q] = 0; pjv[q] = 0; gjv[q] = 0.f;
+        if (kh < H && lane < W) {
+          const int64_t bin = bin_of3(id, kh, lane);
+          bj[q] = bits[bin];
+          pjv[q] = static_cast<int>(poff[bin]);
+          gjv[q] = gains[bin];
+        }
+      }
+    };
+    auto fetch_words = [&](int64_t p) {
+      const PlaneId id = plane_id(a, p);
+      const uint64_t* words =
+          reinterpret_cast<const uint64_t*>(a.rec.base + id.u * a.rec.stride + a.rec.off_codes);
+#pragma unroll
+      for (int q = 0; q < SLH; ++q) {
+        int b = bj[q];
+        const int64_t pj = static_cast<uint32_t>(pjv[q]);
+        if (b > a.max_bits || pj + b > a.total_bits) b = 0;
+        bj[q] = b;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          uint64_t w = 0;
+          if (k < b) w = words[(pj + k) * wpp + id.half];
+          wd[q][k] = uint2{static_cast<uint32_t>(w), static_cast<uint32_t>(w >> 32)};
+        }
+      }
+    };
+    if (static_cast<int64_t>(blockIdx.x) < n_planes) {
+      fetch_side(blockIdx.x);
+      fetch_words(blockIdx.x);
+    }
+    for (int64_t p = blockIdx.x; p < n_planes; p += pstep) {
+      const PlaneId id = plane_id(a, p);
+      const bool more = p + pstep < n_planes;
+      // ---- inverse W: decode bins into LDS, contract; a wave owns one kh --
+#pragma unroll
+      for (int q = 0; q < SLH; ++q) {
+        const int kh = wv + kPlaneWaves * q;
+        if (kh >= H) break;
+        float* row = plane + static_cast<int64_t>(kh) * W * 64;
+        for (int kw = 0; kw < W; ++kw) {
+          const int b = __builtin_amdgcn_readlane(bj[q], kw);
+          float x = 0.f;
+          if (b > 0) {
+            int code = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              if (k < b) {
+                const uint32_t lo = __builtin_amdgcn_readlane(wd[q][k].x, kw);
+                const uint32_t hi = __builtin_amdgcn_readlane(wd[q][k].y, kw);
+                code |= static_cast<int>(((lane < 32 ? lo : hi) >> (lane & 31)) & 1u) << k;
+              }
+            }
+            x = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gjv[q]), kw)) *
+                s_cb[(1 << b) - 2 + code];
+          }
+          row[kw * 64 + lane] = x;
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        uint8_t* r = a.rec.base + u * a.rec.stride;
-        const uint8_t* bits = r + a.rec.off_bits;
-        uint64_t* words = reinterpret_cast<uint64_t*>(r + a.rec.off_codes);
-        const uint32_t* poff = a.plane_off + u * a.n_bins;
-        const float* invg = a.inv_gain + u * a.var_stride;
-        const int wpp = a.head_dim / 64;
-        int bj = 0, pjlo = 0;
-        float ij = 0.f;
-        if (lane < W) {
-          const int64_t bin = bin_of3(kh, lane);
-          bj = bits[bin];
-          const int64_t pj = poff[bin];
-          if (bj > a.max_bits || pj + bj > a.total_bits) bj = 0;
-          pjlo = static_cast<int>(pj);
-          ij = invg[bin];
-        }
-        for (int kw = 0; kw < W; ++kw) {
-          const int b = __builtin_amdgcn_readlane(bj, kw);
-          if (b == 0) continue;
-          const int64_t p0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(pjlo, kw));
-          const float inv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ij), kw));
-          const int code = cell_index_lds(s_cb, zt[kw * 64 + lane] * inv, b);
-          for (int q = 0; q < b; ++q) {
-            const uint64_t word = __ballot((code >> q) & 1);
-            if (lane == 0) words[(p0 + q) * wpp + half] = word;
+        float xv[4][FW::KSTEPS][FW::KV];
+#pragma unroll
+        for (int ks = 0; ks < FW::KSTEPS; ++ks)
+#pragma unroll
+          for (int v = 0; v < FW::KV; ++v) {
+            const int kw = ks * FW::KPER + FW::KV * g + v;
+            float4 qv = float4{0.f, 0.f, 0.f, 0.f};
+            if (kw < W) qv = lds_ld4(row + kw * 64 + 4 * t);
+            xv[0][ks][v] = qv.x; xv[1][ks][v] = qv.y; xv[2][ks][v] = qv.z; xv[3][ks][v] = qv.w;
           }
+        f32x4 acc[4][FW::MT];
+        typename FW::vec ahi_w[FW::MT][FW::KSTEPS], alo_w[FW::MT][FW::KSTEPS];
+        frag_from_lds<NPW>(s_fw, lane, ahi_w, alo_w);
+        if constexpr (ROT) {
+          // R^T = diag(s) H / 8: H on the decoded channels, the signs and 1/8
+          // after the (channel-wise) W contraction
+          rotate_frag<NPW>(xv, wl);
+          contract4<NPW>(ahi_w, alo_w, xv, acc, post_w);
+        } else {
+          contract4<NPW>(ahi_w, alo_w, xv, acc, kOne);
         }
-      }
-    }
-  } else {
-    // ---- inverse W: decode bins into LDS, contract; a wave owns one kh ----
-    __syncthreads();                         // codebook in LDS
-    typename FW::vec ahi_w[FW::MT][FW::KSTEPS], alo_w[FW::MT][FW::KSTEPS];
-    load_afrag<NPW>(a.tab + 2 * 4096, 1, t, g, ahi_w, alo_w);
-    const uint8_t* r = a.rec.base + u * a.rec.stride;
-    const uint8_t* bits = r + a.rec.off_bits;
-    const float* gains = reinterpret_cast<const float*>(r + a.rec.off_gains);
-    const uint64_t* words = reinterpret_cast<const uint64_t*>(r + a.rec.off_codes);
-    const uint32_t* poff = a.plane_off + u * a.n_bins;
-    const int wpp = a.head_dim / 64;
-    for (int kh = wv; kh < H; kh += kPlaneWaves) {
-      float* row = plane + static_cast<int64_t>(kh) * W * 64;
-      int bj = 0;
-      float gj = 0.f;
-      uint32_t wlo[8], whi[8];
-      {
-        int64_t pj = 0;
-        if (lane < W) {
-          const int64_t bin = bin_of3(kh, lane);
-          bj = bits[bin];
-          pj = poff[bin];
-          gj = gains[bin];
-          if (bj > a.max_bits || pj + bj > a.total_bits) bj = 0;
-        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          uint64_t w = 0;
-          if (q < bj) w = words[(pj + q) * wpp + half];
-          wlo[q] = static_cast<uint32_t>(w);
-          whi[q] = static_cast<uint32_t>(w >> 32);
-        }
-      }
-      for (int kw = 0; kw < W; ++kw) {
-        const int b = __builtin_amdgcn_readlane(bj, kw);
-        float x = 0.f;
-        if (b > 0) {
-          int code = 0;
+        for (int m = 0; m < FW::MT; ++m)
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            if (q < b) {
-              const uint32_t lo = __builtin_amdgcn_readlane(wlo[q], kw);
-              const uint32_t hi = __builtin_amdgcn_readlane(whi[q], kw);
-              code |= static_cast<int>(((lane < 32 ? lo : hi) >> (lane & 31)) & 1u) << q;
-            }
+          for (int rr = 0; rr < 4; ++rr) {
+            const int w = 16 * m + 4 * g + rr;
+            if (w < W)
+              lds_st4(row + w * 64 + 4 * t,
+                      float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
           }
-          x = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gj), kw)) *
-              s_cb[(1 << b) - 2 + code];
-        }
-        row[kw * 64 + lane] = x;
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      float xv[4][FW::KSTEPS][FW::KV];
+      // the next plane's side info, in flight during the inverse H pass
+      if (more) fetch_side(p + pstep);
+      __syncthreads();
+      // ---- inverse H: LDS -> global; a wave owns the columns of one w -----
+      const __amdgpu_buffer_rsrc_t rout =
+          make_rsrc(a.out + id.vol, static_cast<int64_t>(row_bytes) * H);
 #pragma unroll
-      for (int ks = 0; ks < FW::KSTEPS; ++ks)
+      for (int j = 0; j < SLW; ++j) {
+        const int w = wv + kPlaneWaves * j;
+        if (w >= W) break;
+        float xv[4][FH::KSTEPS][FH::KV];
 #pragma unroll
-        for (int v = 0; v < FW::KV; ++v) {
-          const int kw = ks * FW::KPER + FW::KV * g + v;
-          float4 q = float4{0.f, 0.f, 0.f, 0.f};
-          if (kw < W) q = lds_ld4(row + kw * 64 + 4 * t);
-          xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
-        }
-      f32x4 acc[4][FW::MT];
-      if constexpr (ROT) {
-        // R^T = diag(s) H / 8: H on the decoded channels, the signs and 1/8
-        // after the (channel-wise) W contraction
-        rotate_frag<NPW>(xv, wl);
-        contract4<NPW>(ahi_w, alo_w, xv, acc, post_w);
-      } else {
-        contract4<NPW>(ahi_w, alo_w, xv, acc, kOne);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
+        for (int ks = 0; ks < FH::KSTEPS; ++ks)
 #pragma unroll
-      for (int m = 0; m < FW::MT; ++m)
+          for (int v = 0; v < FH::KV; ++v) {
+            const int kh = ks * FH::KPER + FH::KV * g + v;
+            float4 qv = float4{0.f, 0.f, 0.f, 0.f};
+            if (kh < H) qv = lds_ld4(plane + (kh * W + w) * 64 + 4 * t);
+            xv[0][ks][v] = qv.x; xv[1][ks][v] = qv.y; xv[2][ks][v] = qv.z; xv[3][ks][v] = qv.w;
+          }
+        f32x4 acc[4][FH::MT];
+        typename FH::vec ahi_h[FH::MT][FH::KSTEPS], alo_h[FH::MT][FH::KSTEPS];
+        frag_from_lds<NPH>(s_fh, lane, ahi_h, alo_h);
+        contract4<NPH>(ahi_h, alo_h, xv, acc, kOne);
+        // rows h >= H fall past the buffer's range and are dropped
+        const int voff = (4 * g * W + w) * cbytes + static_cast<int>(id.c0 + 4 * t) * 4;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int w = 16 * m + 4 * g + rr;
-          if (w < W)
-            lds_st4(row + w * 64 + 4 * t,
+        for (int m = 0; m < FH::MT; ++m)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            buf_st4(rout, voff, (16 * m + rr) * row_bytes,
                     float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
-        }
-    }
-    __syncthreads();
-    // ---- inverse H: LDS -> global; a wave owns the columns of one w -------
-    const __amdgpu_buffer_rsrc_t rout = make_rsrc(a.out + vol, static_cast<int64_t>(row_bytes) * H);
-    typename FH::vec ahi_h[FH::MT][FH::KSTEPS], alo_h[FH::MT][FH::KSTEPS];
-    load_afrag<NPH>(a.tab + 1 * 4096, 1, t, g, ahi_h, alo_h);
-    for (int w = wv; w < W; w += kPlaneWaves) {
-      float xv[4][FH::KSTEPS][FH::KV];
-#pragma unroll
-      for (int ks = 0; ks < FH::KSTEPS; ++ks)
-#pragma unroll
-        for (int v = 0; v < FH::KV; ++v) {
-          const int kh = ks * FH::KPER + FH::KV * g + v;
-          float4 q = float4{0.f, 0.f, 0.f, 0.f};
-          if (kh < H) q = lds_ld4(plane + (kh * W + w) * 64 + 4 * t);
-          xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
-        }
-      f32x4 acc[4][FH::MT];
-      contract4<NPH>(ahi_h, alo_h, xv, acc, kOne);
-      // rows h >= H fall past the buffer's range and are dropped
-      const int voff = (4 * g * W + w) * cbytes + lane_col;
-#pragma unroll
-      for (int m = 0; m < FH::MT; ++m)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          buf_st4(rout, voff, (16 * m + rr) * row_bytes,
-                  float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
+        // after the first column, the next plane's code words (their side
+        // info has arrived by now)
+        if (j == 0 && more) fetch_words(p + pstep);
+      }
+      if (W <= wv && more) fetch_words(p + pstep);
+      __syncthreads();                       // LDS free for the next plane
     }
   }
 }
@@ -1489,6 +1568,21 @@ void launch_axis(const Geometry& g, int64_t n_units, int axis, int inverse, int 
 }
 
 
+// Blocks of a persistent launch: the device's resident capacity for this
+// kernel (compute units x blocks per unit), at most `work`, at least 1.
+static int64_t persistent_blocks(const void* fn, int threads, size_t lds, int64_t work) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  int64_t n = static_cast<int64_t>(cus) * per_cu;
+  if (n > work) n = work;
+  return n < 1 ? 1 : n;
+}
+
 bool plane_supported(const Geometry& g) {
   return (g.axes & 6) == 6 && g.H <= 32 && g.W <= 32 &&
          static_cast<int64_t>(g.H) * g.W * 64 * 4 <= 150 * 1024;
@@ -1496,7 +1590,7 @@ bool plane_supported(const Geometry& g) {
 
 void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in, float* out,
                   int64_t ustride, const float* tab, float* var_part, int64_t var_stride,
-                  const float* inv_gain, RecordView rec, const uint32_t* plane_off, hipStream_t s) {
+                  RecordView rec, const uint32_t* plane_off, hipStream_t s) {
   PlaneArgs a;
   a.in = in;
   a.out = out;
@@ -1514,35 +1608,43 @@ void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in,
   a.var_part = var_part;
   a.parts = g.head_dim / 64;
   a.var_stride = var_stride;
-  a.inv_gain = inv_gain;
   a.rec = rec;
   a.plane_off = plane_off;
-  const dim3 grid(static_cast<unsigned>(a.C / 64), static_cast<unsigned>(g.S),
-                  static_cast<unsigned>(n_units));
+  a.n_units = n_units;
+  const int64_t n_planes = n_units * g.S * (a.C / 64);
   const dim3 block(64 * kPlaneWaves);
   const size_t lds = static_cast<size_t>(g.H) * g.W * 64 * sizeof(float);
   const bool h16 = g.H <= 16, w16 = g.W <= 16;
   const bool rot = g.rotation == TACT_ROTATION_HADAMARD;
   // the plane needs more dynamic LDS than the default limit
-#define TACT_PLANE_ONE(NH, NW, M, R)                                                            \
+  // persistent grid: as many blocks as the device holds at once
+#define TACT_PLANE_ONE(NH, NW, M, R, SL)                                                        \
   do {                                                                                          \
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_plane<NH, NW, M, R>),             \
-                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));     \
-    hipLaunchKernelGGL((k_plane<NH, NW, M, R>), grid, block, lds, s, a);                        \
+    const void* fn = reinterpret_cast<const void*>(&k_plane<NH, NW, M, R, SL>);                 \
+    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,                   \
+                              static_cast<int>(lds));                                           \
+    const dim3 grid(static_cast<unsigned>(persistent_blocks(fn, 64 * kPlaneWaves, lds, n_planes))); \
+    hipLaunchKernelGGL((k_plane<NH, NW, M, R, SL>), grid, block, lds, s, a);                    \
+  } while (0)
+#define TACT_PLANE_SL(NH, NW, SL)                                                               \
+  do {                                                                                          \
+    if (mode == MODE_STATS) TACT_PLANE_ONE(NH, NW, MODE_STATS, false, SL);                      \
+    else if (rot) TACT_PLANE_ONE(NH, NW, MODE_DEQUANT, true, SL);                               \
+    else TACT_PLANE_ONE(NH, NW, MODE_DEQUANT, false, SL);                                       \
   } while (0)
 #define TACT_PLANE(NH, NW)                                                                      \
   do {                                                                                          \
-    if (mode == MODE_STATS) TACT_PLANE_ONE(NH, NW, MODE_STATS, false);                          \
-    else if (mode == MODE_QUANT && rot) TACT_PLANE_ONE(NH, NW, MODE_QUANT, true);               \
-    else if (mode == MODE_QUANT) TACT_PLANE_ONE(NH, NW, MODE_QUANT, false);                     \
-    else if (rot) TACT_PLANE_ONE(NH, NW, MODE_DEQUANT, true);                                   \
-    else TACT_PLANE_ONE(NH, NW, MODE_DEQUANT, false);                                           \
+    if (slots <= 2) TACT_PLANE_SL(NH, NW, 2);                                                   \
+    else if (slots == 3) TACT_PLANE_SL(NH, NW, 3);                                              \
+    else TACT_PLANE_SL(NH, NW, 4);                                                              \
   } while (0)
-  if (h16 && w16) TACT_PLANE(16, 16);
+  const int slots = ((g.H > g.W ? g.H : g.W) + kPlaneWaves - 1) / kPlaneWaves;
+  if (h16 && w16) TACT_PLANE_SL(16, 16, 2);
   else if (h16) TACT_PLANE(16, 32);
   else if (w16) TACT_PLANE(32, 16);
   else TACT_PLANE(32, 32);
 #undef TACT_PLANE
+#undef TACT_PLANE_SL
 #undef TACT_PLANE_ONE
 }
 
