@@ -262,8 +262,10 @@ void decompress_chunk(const Geometry& g, int64_t cn, const uint8_t* recs, void* 
   launch_plane_offsets(g, cn, rv, w.poff, s);
   if (g.axes == TACT_AXES_ALL && plane_supported(g)) {
     launch_plane(g, cn, 2, nullptr, w.coef, g.n_entries, w.tab, nullptr, 0, rv, w.poff, s);
+    // the inverse S axis also undoes the quantizer's rotation (it acts on
+    // the channels, so it commutes with the transform)
     launch_axis(g, cn, 0, 1, AX_PRO_F32, out_epi, w.coef, g.n_entries, out, out_stride, w.tab,
-                nullptr, nullptr, 0, rv, w.poff, s);
+                nullptr, nullptr, 0, rv, w.poff, s, /*rot_in=*/true);
     return;
   }
   int ax[3];

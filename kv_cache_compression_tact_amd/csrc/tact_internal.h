@@ -81,10 +81,13 @@ void launch_dct_tables(const Geometry& g, float* tab, hipStream_t stream);
 
 // One axis (0 = S, 1 = H, 2 = W) of the transform on the matrix cores over
 // n_units units; see tact_mfma.hip for the prologue / epilogue contracts.
+// rot_in: a plain fp32 pass also applies the inverse of the quantizer's
+// rotation (when the geometry rotates) to its input rows.
 void launch_axis(const Geometry& g, int64_t n_units, int axis, int inverse, int pro, int epi,
                  const void* in, int64_t in_stride, void* out, int64_t out_stride,
                  const float* tab, float* var, const float* inv_gain, int64_t var_stride,
-                 RecordView rec, const uint32_t* plane_off, hipStream_t stream);
+                 RecordView rec, const uint32_t* plane_off, hipStream_t stream,
+                 bool rot_in = false);
 
 // Allocation by exact radix selection; writes bits_out and/or the record
 // header, and per-bin first planes into plane_off (each may be null).

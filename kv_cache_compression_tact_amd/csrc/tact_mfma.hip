@@ -229,6 +229,8 @@ struct AxisArgs {
   RecordView rec;            // EPI_QUANT, PRO_DEQUANT
   const uint32_t* plane_off; // per-bin first plane, u * n_bins + bin
   int rotate;                // EPI_QUANT, PRO_DEQUANT: apply the shared rotation
+  int rot_in;                // PRO_F32 plain pass (4 channels per lane): apply the
+                             // inverse rotation R^T to the input rows
 };
 
 template <int NP>
@@ -297,11 +299,13 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
   const LaneWht wl(lane);
   float rpost[4] = {1.f, 1.f, 1.f, 1.f};
   const bool rot = (PRO == PRO_DEQUANT || EPI == EPI_QUANT) && a.rotate;
-  if (rot) {
+  // inverse rotation of plain fp32 rows: channel 4t + i of a 64-column word
+  const bool rot_in = INTL && PRO == PRO_F32 && TPW == 4 && a.rot_in;
+  if (rot || rot_in) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      rpost[i] = (PRO == PRO_DEQUANT) ? 0.125f * wl.parity * rotation_sign(4 * t + i)
-                                      : rotation_sign(16 * i + t);
+      rpost[i] = (PRO == PRO_DEQUANT || rot_in) ? 0.125f * wl.parity * rotation_sign(4 * t + i)
+                                                : rotation_sign(16 * i + t);
   }
 
   // A fragments (the DCT matrix scaled by 2^12, or its transpose), hi / lo
@@ -465,7 +469,23 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
             wht64(xv[0][ks][v], xv[1][ks][v], xv[2][ks][v], xv[3][ks][v], wl);
       }
     } else if constexpr (INTL) {
-      // rows come from the prefetch registers (cur), one tile at a time
+      // rows come from the prefetch registers (cur), one tile at a time;
+      // R^T = diag(s) H / 8 on fp32 rows: H here, the rest with the output
+      // scale
+      if constexpr (PRO == PRO_F32 && TPW == 4) {
+        if (rot_in) {
+#pragma unroll
+          for (int ks = 0; ks < F::KSTEPS; ++ks)
+#pragma unroll
+            for (int v = 0; v < F::KV; ++v) {
+              float y0 = __uint_as_float(cur[ks][v][0]), y1 = __uint_as_float(cur[ks][v][1]);
+              float y2 = __uint_as_float(cur[ks][v][2]), y3 = __uint_as_float(cur[ks][v][3]);
+              wht64(y0, y1, y2, y3, wl);
+              cur[ks][v] = u32x4{__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2),
+                                 __float_as_uint(y3)};
+            }
+        }
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
@@ -764,18 +784,6 @@ __device__ __forceinline__ void contract4(const typename Frag<NP>::vec (&ahi)[Fr
   }
 }
 
-// the shared rotation on the channel index 4t + i of fragment values
-// xv[i][ks][v] (the same K index across a 16-lane row)
-template <int NP>
-__device__ __forceinline__ void rotate_frag(float (&xv)[4][Frag<NP>::KSTEPS][Frag<NP>::KV],
-                                            const LaneWht& w) {
-#pragma unroll
-  for (int ks = 0; ks < Frag<NP>::KSTEPS; ++ks)
-#pragma unroll
-    for (int v = 0; v < Frag<NP>::KV; ++v)
-      wht64(xv[0][ks][v], xv[1][ks][v], xv[2][ks][v], xv[3][ks][v], w);
-}
-
 // Persistent blocks of 8 waves (256 VGPRs each): a block walks the planes
 // blockIdx.x, blockIdx.x + gridDim.x, ...  While plane p is transformed,
 // the data of plane p + gridDim.x is fetched into the registers the wave
@@ -848,9 +856,8 @@ __device__ __forceinline__ PlaneId plane_id(const PlaneArgs& a, int64_t p) {
   return id;
 }
 
-template <int NPH, int NPW, int MODE, bool ROT, int SL>
+template <int NPH, int NPW, int MODE, int SL>
 __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
-  static_assert(!ROT || MODE == MODE_DEQUANT, "the rotation is undone after dequantization");
   using FH = Frag<NPH>;
   using FW = Frag<NPW>;
   // w columns (H passes) and kh rows (W passes) per wave: SL covers
@@ -877,15 +884,6 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
   auto bin_of3 = [&](const PlaneId& id, int kh, int kw) -> int64_t {
     return ((static_cast<int64_t>(id.s) * H + kh) * W + kw) * a.kv_heads + id.head;
   };
-  // inverse rotation constants: lane butterflies, and the scale after the
-  // inverse W contraction (the butterflies' sign, 1/8 and s_j of the
-  // lane's channels 4t + i)
-  const LaneWht wl(lane);
-  float post_w[4] = {1.f, 1.f, 1.f, 1.f};
-  if constexpr (ROT) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) post_w[i] = 0.125f * wl.parity * rotation_sign(4 * t + i);
-  }
   constexpr float kOne[4] = {1.f, 1.f, 1.f, 1.f};
   const int wpp = a.head_dim / 64;
 
@@ -1077,14 +1075,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
         f32x4 acc[4][FW::MT];
         typename FW::vec ahi_w[FW::MT][FW::KSTEPS], alo_w[FW::MT][FW::KSTEPS];
         frag_from_lds<NPW>(s_fw, lane, ahi_w, alo_w);
-        if constexpr (ROT) {
-          // R^T = diag(s) H / 8: H on the decoded channels, the signs and 1/8
-          // after the (channel-wise) W contraction
-          rotate_frag<NPW>(xv, wl);
-          contract4<NPW>(ahi_w, alo_w, xv, acc, post_w);
-        } else {
-          contract4<NPW>(ahi_w, alo_w, xv, acc, kOne);
-        }
+        contract4<NPW>(ahi_w, alo_w, xv, acc, kOne);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -1539,7 +1530,7 @@ static void axis_shape(const Geometry& g, int axis, int* N, int64_t* outer, int6
 void launch_axis(const Geometry& g, int64_t n_units, int axis, int inverse, int pro, int epi,
                  const void* in, int64_t in_stride, void* out, int64_t out_stride,
                  const float* tab, float* var, const float* inv_gain, int64_t var_stride,
-                 RecordView rec, const uint32_t* plane_off, hipStream_t s) {
+                 RecordView rec, const uint32_t* plane_off, hipStream_t s, bool rot_in) {
   AxisArgs a;
   a.in = in;
   a.in_ustride = in_stride;
@@ -1561,6 +1552,7 @@ void launch_axis(const Geometry& g, int64_t n_units, int axis, int inverse, int 
   a.rec = rec;
   a.plane_off = plane_off;
   a.rotate = g.rotation == TACT_ROTATION_HADAMARD;
+  a.rot_in = rot_in && a.rotate && pro == PRO_F32 && (epi == EPI_F32 || epi == EPI_BF16);
   const int tpw = (epi == EPI_STATS || epi == EPI_QUANT) ? g.head_dim / 16 : 4;
   if (a.N <= 16) launch_axis_np<16>(a, pro, epi, tpw, s);
   else if (a.N <= 32) launch_axis_np<32>(a, pro, epi, tpw, s);
@@ -1615,22 +1607,20 @@ void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in,
   const dim3 block(64 * kPlaneWaves);
   const size_t lds = static_cast<size_t>(g.H) * g.W * 64 * sizeof(float);
   const bool h16 = g.H <= 16, w16 = g.W <= 16;
-  const bool rot = g.rotation == TACT_ROTATION_HADAMARD;
   // the plane needs more dynamic LDS than the default limit
   // persistent grid: as many blocks as the device holds at once
-#define TACT_PLANE_ONE(NH, NW, M, R, SL)                                                        \
+#define TACT_PLANE_ONE(NH, NW, M, SL)                                                           \
   do {                                                                                          \
-    const void* fn = reinterpret_cast<const void*>(&k_plane<NH, NW, M, R, SL>);                 \
+    const void* fn = reinterpret_cast<const void*>(&k_plane<NH, NW, M, SL>);                    \
     (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,                   \
                               static_cast<int>(lds));                                           \
     const dim3 grid(static_cast<unsigned>(persistent_blocks(fn, 64 * kPlaneWaves, lds, n_planes))); \
-    hipLaunchKernelGGL((k_plane<NH, NW, M, R, SL>), grid, block, lds, s, a);                    \
+    hipLaunchKernelGGL((k_plane<NH, NW, M, SL>), grid, block, lds, s, a);                       \
   } while (0)
 #define TACT_PLANE_SL(NH, NW, SL)                                                               \
   do {                                                                                          \
-    if (mode == MODE_STATS) TACT_PLANE_ONE(NH, NW, MODE_STATS, false, SL);                      \
-    else if (rot) TACT_PLANE_ONE(NH, NW, MODE_DEQUANT, true, SL);                               \
-    else TACT_PLANE_ONE(NH, NW, MODE_DEQUANT, false, SL);                                       \
+    if (mode == MODE_STATS) TACT_PLANE_ONE(NH, NW, MODE_STATS, SL);                             \
+    else TACT_PLANE_ONE(NH, NW, MODE_DEQUANT, SL);                                              \
   } while (0)
 #define TACT_PLANE(NH, NW)                                                                      \
   do {                                                                                          \
