@@ -121,31 +121,59 @@ __global__ __launch_bounds__(kWave * kQuantWaves) void k_quant(QuantArgs a) {
     cnt = 0;
   };
 
-  const int nb = (a.n_bins - b0 < kWave) ? static_cast<int>(a.n_bins - b0) : kWave;
-  for (int j = 0; j < nb; ++j) {
+  // coded bins of this wave, lowest first; the words of the next one are
+  // fetched while the current one is quantized (up to 4 per bin)
+  uint64_t todo = __ballot(bj > 0);
+  float nxt[4] = {0.f, 0.f, 0.f, 0.f};
+  auto fetch = [&](int j) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      if (h < wpp) nxt[h] = cu[j * a.head_dim + 64 * h];
+  };
+  if (todo) fetch(__builtin_ctzll(todo));
+  while (todo) {
+    const int j = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    float cur[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) cur[h] = nxt[h];
+    if (todo) fetch(__builtin_ctzll(todo));
     const int b = __builtin_amdgcn_readlane(bj, j);
-    if (b == 0) continue;
     const uint32_t p0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(pj, j));
     const float inv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ij), j));
     const float* t = s_thr + ((1 << b) - b - 1);            // 2^b - 1 sorted thresholds
-    for (int h = 0; h < wpp; ++h) {
-      float v = cu[j * a.head_dim + 64 * h];
+    // the table is symmetric: its middle threshold is 0 and the two next
+    // split points are -t2 and +t2
+    const float t2 = b > 1 ? t[(3 << (b - 2)) - 1] : 0.f;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      if (h >= wpp) break;
+      float v = cur[h];
       if (a.rotate) v = wht64_lanes(v * s_in, sg) * (inv * r_out);
       else v = v * inv;
       if (cnt + b > kWave) flush();
       // most significant bit first: step k compares with the threshold that
       // splits the remaining cells; the ballot is bit plane k's word
-      int idx = 0;
-      for (int k = b - 1; k >= 0; --k) {
-        const bool up = t[idx + (1 << k) - 1] <= v;
-        const uint64_t wd = __ballot(up);
-        if (up) idx += 1 << k;
+      auto stage = [&](uint64_t wd, int k) {
         if (lane == cnt) {
           wlo = static_cast<uint32_t>(wd);
           whi = static_cast<uint32_t>(wd >> 32);
           widx = (p0 + static_cast<uint32_t>(k)) * wpp + h;
         }
         ++cnt;
+      };
+      bool up = 0.f <= v;
+      stage(__ballot(up), b - 1);
+      int idx = up ? (1 << (b - 1)) : 0;
+      if (b > 1) {
+        up = (up ? t2 : -t2) <= v;
+        stage(__ballot(up), b - 2);
+        if (up) idx += 1 << (b - 2);
+        for (int k = b - 3; k >= 0; --k) {
+          up = t[idx + (1 << k) - 1] <= v;
+          stage(__ballot(up), k);
+          if (up) idx += 1 << k;
+        }
       }
     }
   }
