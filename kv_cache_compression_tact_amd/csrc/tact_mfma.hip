@@ -1035,49 +1035,62 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
     for (int64_t p = blockIdx.x; p < n_planes; p += pstep) {
       const PlaneId id = plane_id(a, p);
       const bool more = p + pstep < n_planes;
-      // ---- inverse W: decode bins into LDS, contract; a wave owns one kh --
+      // ---- inverse W: decode into the B fragments, contract; a wave owns one
+      // kh row.  The row's LDS area first holds its bins' bits, gains and
+      // code words (10 8-byte slots per bin); lane (t, g) then rebuilds the
+      // codes of its channels 4t..4t+3 for its K rows kw: one 64-bit word
+      // per bit plane gives a nibble, spread into one byte per channel.
 #pragma unroll
       for (int q = 0; q < SLH; ++q) {
         const int kh = wv + kPlaneWaves * q;
         if (kh >= H) break;
         float* row = plane + static_cast<int64_t>(kh) * W * 64;
-        for (int kw = 0; kw < W; ++kw) {
-          const int b = __builtin_amdgcn_readlane(bj[q], kw);
-          float x = 0.f;
-          if (b > 0) {
-            int code = 0;
+        uint2* st = reinterpret_cast<uint2*>(row);
+        if (lane < W) {
+          st[lane * 10] = uint2{static_cast<uint32_t>(bj[q]), __float_as_uint(gjv[q])};
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              if (k < b) {
-                const uint32_t lo = __builtin_amdgcn_readlane(wd[q][k].x, kw);
-                const uint32_t hi = __builtin_amdgcn_readlane(wd[q][k].y, kw);
-                code |= static_cast<int>(((lane < 32 ? lo : hi) >> (lane & 31)) & 1u) << k;
-              }
-            }
-            x = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gjv[q]), kw)) *
-                s_cb[(1 << b) - 2 + code];
-          }
-          row[kw * 64 + lane] = x;
+          for (int k = 0; k < 8; ++k) st[lane * 10 + 1 + k] = wd[q][k];
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int nib_sh = (4 * t) & 31;
+        const bool nib_hi = t >= 8;
         float xv[4][FW::KSTEPS][FW::KV];
 #pragma unroll
         for (int ks = 0; ks < FW::KSTEPS; ++ks)
 #pragma unroll
           for (int v = 0; v < FW::KV; ++v) {
             const int kw = ks * FW::KPER + FW::KV * g + v;
-            float4 qv = float4{0.f, 0.f, 0.f, 0.f};
-            if (kw < W) qv = lds_ld4(row + kw * 64 + 4 * t);
-            xv[0][ks][v] = qv.x; xv[1][ks][v] = qv.y; xv[2][ks][v] = qv.z; xv[3][ks][v] = qv.w;
+            uint2 sb = uint2{0u, 0u};
+            if (kw < W) sb = st[kw * 10];
+            const int b = static_cast<int>(sb.x);
+            // byte i of `codes` collects the bits of channel 4t + i
+            uint32_t codes = 0;
+            for (int k = 0; k < 8; ++k) {
+              if (__ballot(k < b) == 0) break;
+              if (k < b) {
+                const uint2 w = st[kw * 10 + 1 + k];
+                const uint32_t nib = __builtin_amdgcn_ubfe(nib_hi ? w.y : w.x, nib_sh, 4);
+                codes |= ((nib * 0x204081u) & 0x01010101u) << k;
+              }
+            }
+            const float gn = __uint_as_float(sb.y);
+            const int base = b > 0 ? (1 << b) - 2 : 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float lv = s_cb[base + static_cast<int>((codes >> (8 * i)) & 0xFFu)];
+              xv[i][ks][v] = b > 0 ? gn * lv : 0.f;
+            }
           }
+        // every lane has read the staging before the outputs overwrite it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         f32x4 acc[4][FW::MT];
         typename FW::vec ahi_w[FW::MT][FW::KSTEPS], alo_w[FW::MT][FW::KSTEPS];
         frag_from_lds<NPW>(s_fw, lane, ahi_w, alo_w);
         contract4<NPW>(ahi_w, alo_w, xv, acc, kOne);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int m = 0; m < FW::MT; ++m)
 #pragma unroll
