@@ -222,8 +222,11 @@ void compress_chunk(const Geometry& g, int64_t cn, const void* kv, int64_t kv_st
     // S on the matrix cores into the fp32 volume, then H and W fused in LDS
     // (the final coefficients replace the volume), the allocation, and one
     // streaming pass over the coded bins
+    // the S pass also applies the quantizer's rotation to its output (it acts
+    // on the channels, so it commutes with the H and W axes and leaves the
+    // bin variances unchanged)
     launch_axis(g, cn, 0, 0, in_pro, AX_EPI_F32, kv, kv_stride, w.coef, g.n_entries, w.tab,
-                nullptr, nullptr, 0, none, nullptr, s);
+                nullptr, nullptr, 0, none, nullptr, s, /*rot_in=*/false, /*rot_out=*/true);
     launch_plane(g, cn, 0, w.coef, w.coef, g.n_entries, w.tab, w.var, vs, none, nullptr, s);
     launch_allocate2(g, cn, w.var, vs, static_cast<int>(var_parts(g)), inv_d, nullptr,
                      view(g, recs), w.poff, w.invg, s);

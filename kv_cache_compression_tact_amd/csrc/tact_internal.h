@@ -81,13 +81,15 @@ void launch_dct_tables(const Geometry& g, float* tab, hipStream_t stream);
 
 // One axis (0 = S, 1 = H, 2 = W) of the transform on the matrix cores over
 // n_units units; see tact_mfma.hip for the prologue / epilogue contracts.
-// rot_in: a plain fp32 pass also applies the inverse of the quantizer's
-// rotation (when the geometry rotates) to its input rows.
+// When the geometry rotates: rot_in makes a plain fp32 pass apply the
+// inverse of the quantizer's rotation to its input rows, rot_out makes a
+// plain pass with fp32 output apply the rotation to its output rows (the
+// rotation acts on the channels and commutes with the transform).
 void launch_axis(const Geometry& g, int64_t n_units, int axis, int inverse, int pro, int epi,
                  const void* in, int64_t in_stride, void* out, int64_t out_stride,
                  const float* tab, float* var, const float* inv_gain, int64_t var_stride,
                  RecordView rec, const uint32_t* plane_off, hipStream_t stream,
-                 bool rot_in = false);
+                 bool rot_in = false, bool rot_out = false);
 
 // Allocation by exact radix selection; writes bits_out and/or the record
 // header, and per-bin first planes into plane_off (each may be null).
@@ -104,8 +106,8 @@ void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in,
                   RecordView rec, const uint32_t* plane_off, hipStream_t stream);
 
 // Quantize + pack the final coefficients coef ([u][bin][head_dim], unit
-// stride ustride) into the records, given 1/gain and first planes
-// (tact_quant.hip).
+// stride ustride; already rotated when the geometry rotates) into the
+// records, given 1/gain and first planes (tact_quant.hip).
 void launch_quant(const Geometry& g, int64_t n_units, const float* coef, int64_t ustride,
                   const float* inv_gain, int64_t var_stride, RecordView rec,
                   const uint32_t* plane_off, hipStream_t stream);

@@ -137,13 +137,15 @@ __device__ __forceinline__ float lane_xor8(float x) {
 // k is set; the product of the four is the sign the butterflies leave.
 struct LaneWht {
   float sg[4];
-  float parity;
+  float parity;    // (-1)^popcount(lane & 15)
+  float parity8;   // (-1)^popcount(lane & 7)
   __device__ __forceinline__ explicit LaneWht(int lane) {
     parity = 1.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       sg[k] = ((lane >> k) & 1) ? -1.f : 1.f;
       parity *= sg[k];
+      if (k == 2) parity8 = parity;
     }
   }
 };
@@ -182,9 +184,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ float4 buf_ld4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
+// A store of more than 8 bytes may read its data registers after it
+// issues; a VALU write to those registers in the very next instruction can
+// reach memory instead.  Every 128-bit store is followed by one wait state.
+__device__ __forceinline__ void store_gap() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 0");
+  __builtin_amdgcn_sched_barrier(0);
+}
 __device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, int voff, int soff, float4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint32_t __attribute__((ext_vector_type(4))), v),
                                          r, voff, soff, 0);
+  store_gap();
 }
 
 // 128-bit LDS access at a float offset that is a multiple of 4
@@ -193,6 +204,29 @@ __device__ __forceinline__ float4 lds_ld4(const float* p) {
 }
 __device__ __forceinline__ void lds_st4(float* p, float4 v) {
   *static_cast<float4*>(__builtin_assume_aligned(p, 16)) = v;
+}
+
+// The same for 8 channels per lane (channel 8 t + i): in-register
+// butterflies over the 3 register bits, then lanes ^ 1, ^ 2, ^ 4; the
+// result is parity8 * (H_64 x).
+__device__ __forceinline__ void wht64_r8(float (&y)[8], const LaneWht& w) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((i & h) == 0) {
+        const float a0 = y[i], a1 = y[i + h];
+        y[i] = a0 + a1;
+        y[i + h] = a0 - a1;
+      }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    float x = y[q];
+    x = fmaf(lane_xor1(x), w.sg[0], x);
+    x = fmaf(lane_xor2(x), w.sg[1], x);
+    x = fmaf(lane_xor4(x), w.sg[2], x);
+    y[q] = x;
+  }
 }
 
 // Number of the 2^b - 1 ascending thresholds (LDS copy) that are <= u.
@@ -231,6 +265,8 @@ struct AxisArgs {
   int rotate;                // EPI_QUANT, PRO_DEQUANT: apply the shared rotation
   int rot_in;                // PRO_F32 plain pass (4 channels per lane): apply the
                              // inverse rotation R^T to the input rows
+  int rot_out;               // EPI_F32 plain pass: apply the rotation R to the
+                             // output rows
 };
 
 template <int NP>
@@ -297,15 +333,25 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
   // the shared rotation: lane butterflies and per-tile post factors
   // (dequantize: channel 4t + i; quantize: channel 16 (i % 4) + t)
   const LaneWht wl(lane);
-  float rpost[4] = {1.f, 1.f, 1.f, 1.f};
+  // per-tile output factors of the rotation: signs s_j and 1/8 folded into
+  // the output scale
+  float rpost[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) rpost[i] = 1.f;
   const bool rot = (PRO == PRO_DEQUANT || EPI == EPI_QUANT) && a.rotate;
   // inverse rotation of plain fp32 rows: channel 4t + i of a 64-column word
   const bool rot_in = INTL && PRO == PRO_F32 && TPW == 4 && a.rot_in;
+  // rotation of plain fp32 output rows, channel TPW t + i: R = H diag(s) / 8
+  // with s on the input side (commutes with the contraction), H after it
+  const bool rot_out = INTL && EPI == EPI_F32 && a.rot_out;
   if (rot || rot_in) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      rpost[i] = (PRO == PRO_DEQUANT || rot_in) ? 0.125f * wl.parity * rotation_sign(4 * t + i)
-                                                : rotation_sign(16 * i + t);
+    for (int i = 0; i < TPW; ++i)
+      rpost[i] = (PRO == PRO_DEQUANT || rot_in) ? 0.125f * wl.parity * rotation_sign(4 * t + (i % 4))
+                                                : rotation_sign(16 * (i % 4) + t);
+  } else if (rot_out) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) rpost[i] = rotation_sign((TPW * t + i) % 64);
   }
 
   // A fragments (the DCT matrix scaled by 2^12, or its transpose), hi / lo
@@ -536,7 +582,7 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
       int e = 0;
       if (mx > 0.f) frexpf(mx, &e);
       const float sc = ldexpf(1.0f, 14 - e);
-      const float unscale = ldexpf(1.0f, e - 26) * rpost[i % 4];
+      const float unscale = ldexpf(1.0f, e - 26) * rpost[i];
 #pragma unroll
       for (int ks = 0; ks < F::KSTEPS; ++ks) {
         vec bhi, blo;
@@ -561,6 +607,33 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
     }
 
     // ---- epilogues ---------------------------------------------------------
+    if constexpr (EPI == EPI_F32 && INTL) {
+      if (rot_out) {
+        // H_64 on channel TPW t + i: 4 channels per lane -> 2 register bits
+        // and 4 lane bits; 8 per lane -> 3 register bits and 3 lane bits
+        const float post = 0.125f * (TPW == 8 ? wl.parity8 : wl.parity);
+#pragma unroll
+        for (int m = 0; m < F::MT; ++m)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            if constexpr (TPW == 8) {
+              float y[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) y[i] = acc[i][m][rr];
+              wht64_r8(y, wl);
+#pragma unroll
+              for (int i = 0; i < 8; ++i) acc[i][m][rr] = y[i] * post;
+            } else {
+              float y0 = acc[0][m][rr], y1 = acc[1][m][rr], y2 = acc[2][m][rr], y3 = acc[3][m][rr];
+              wht64(y0, y1, y2, y3, wl);
+              acc[0][m][rr] = y0 * post;
+              acc[1][m][rr] = y1 * post;
+              acc[2][m][rr] = y2 * post;
+              acc[3][m][rr] = y3 * post;
+            }
+          }
+      }
+    }
     if constexpr (EPI == EPI_F32 || EPI == EPI_BF16) {
       // output row k = 16 m + 4 g + rr; rows k >= N fall past the buffer
       const int vo = 4 * g * row_out + static_cast<int>(c0 + TPW * t) * ES_OUT;
@@ -580,9 +653,10 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
             for (int i = 0; i < TPW; i += 2)
               w[i / 2] = bf16_rne_bits(acc[i][m][rr]) |
                          (static_cast<uint32_t>(bf16_rne_bits(acc[i + 1][m][rr])) << 16);
-            if constexpr (TPW == 8)
+            if constexpr (TPW == 8) {
               __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, rout, vo, so, 0);
-            else
+              store_gap();
+            } else
               __builtin_amdgcn_raw_buffer_store_b64(
                   __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))), uint2{w[0], w[1]}),
                   rout, vo, so, 0);
@@ -1543,7 +1617,8 @@ static void axis_shape(const Geometry& g, int axis, int* N, int64_t* outer, int6
 void launch_axis(const Geometry& g, int64_t n_units, int axis, int inverse, int pro, int epi,
                  const void* in, int64_t in_stride, void* out, int64_t out_stride,
                  const float* tab, float* var, const float* inv_gain, int64_t var_stride,
-                 RecordView rec, const uint32_t* plane_off, hipStream_t s, bool rot_in) {
+                 RecordView rec, const uint32_t* plane_off, hipStream_t s, bool rot_in,
+                 bool rot_out) {
   AxisArgs a;
   a.in = in;
   a.in_ustride = in_stride;
@@ -1566,6 +1641,7 @@ void launch_axis(const Geometry& g, int64_t n_units, int axis, int inverse, int 
   a.plane_off = plane_off;
   a.rotate = g.rotation == TACT_ROTATION_HADAMARD;
   a.rot_in = rot_in && a.rotate && pro == PRO_F32 && (epi == EPI_F32 || epi == EPI_BF16);
+  a.rot_out = rot_out && a.rotate && pro != PRO_DEQUANT && epi == EPI_F32;
   const int tpw = (epi == EPI_STATS || epi == EPI_QUANT) ? g.head_dim / 16 : 4;
   if (a.N <= 16) launch_axis_np<16>(a, pro, epi, tpw, s);
   else if (a.N <= 32) launch_axis_np<32>(a, pro, epi, tpw, s);

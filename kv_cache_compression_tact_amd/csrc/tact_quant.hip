@@ -4,7 +4,9 @@
 // quantization of the final DCT coefficients and bit-plane packing.
 //
 // k_quant streams the coefficient volume once, reading only bins that were
-// given bits.  One wave owns 64 consecutive bins of a unit (lane j holds
+// given bits.  The coefficients arrive already rotated by the quantizer's
+// shared rotation when the geometry asks for it (the forward S pass applies
+// it), so the value quantized here is coefficient / gain.  One wave owns 64 consecutive bins of a unit (lane j holds
 // bin j's bit width, first plane and 1/gain) and walks them one at a time:
 // lane c is channel c of a 64-channel word, so a bin's codes for one bit
 // plane are one ballot.  The cell index is found most significant bit
@@ -25,43 +27,6 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kQuantWaves = 4;
 
-// ---- the shared rotation, lane = channel ------------------------------------
-// R = H_64 diag(s) / 8 with Sylvester's H_64 (H[j][j'] = (-1)^popcount(j&j'))
-// and s_j = -1 where the top bit of SplitMix64(0x54414354 + j) is set.
-constexpr uint64_t kRotationSeed = 0x54414354ull;
-
-__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
-  uint64_t z = x + 0x9E3779B97F4A7C15ull;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  return z ^ (z >> 31);
-}
-
-// Butterfly on lane bit k: y = x + sg_k * x[lane ^ 2^k], where sg_k = -1
-// on lanes whose bit k is set.  On those lanes that is the negated
-// Sylvester value, and both lanes of a pair carry the same sign history,
-// so after the six stages y = (-1)^popcount(lane) (H_64 x)[lane].
-__device__ __forceinline__ float wht64_lanes(float x, const float (&sg)[6]) {
-  const int xi = __float_as_int(x);
-  x = fmaf(__int_as_float(__builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, true)), sg[0], x);
-  x = fmaf(__int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true)), sg[1], x);
-  x = fmaf(__int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F)), sg[2], x);
-  x = fmaf(__int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true)), sg[3], x);
-  // lanes l and l ^ 16 (l ^ 32) by a permlane swap of two copies: the first
-  // result holds the even (lower) partner, the second the odd (upper) one
-  {
-    const uint32_t u = __float_as_uint(x);
-    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    x = fmaf(__uint_as_float(r[0]), sg[4], __uint_as_float(r[1]));
-  }
-  {
-    const uint32_t u = __float_as_uint(x);
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    x = fmaf(__uint_as_float(r[0]), sg[5], __uint_as_float(r[1]));
-  }
-  return x;
-}
-
 struct QuantArgs {
   const float* coef;         // final DCT coefficients, [u][bin][head_dim]
   int64_t ustride;           // elements between units
@@ -71,7 +36,6 @@ struct QuantArgs {
   int64_t var_stride;        // floats per unit in inv_gain
   const uint32_t* plane_off; // first bit plane of each bin, [u][bin]
   RecordView rec;
-  int rotate;
 };
 
 __global__ __launch_bounds__(kWave * kQuantWaves) void k_quant(QuantArgs a) {
@@ -94,21 +58,6 @@ __global__ __launch_bounds__(kWave * kQuantWaves) void k_quant(QuantArgs a) {
     pj = static_cast<int>(a.plane_off[u * a.n_bins + bin]);
     ij = a.inv_gain[u * a.var_stride + bin];
     if (bj > a.max_bits || static_cast<int64_t>(static_cast<uint32_t>(pj)) + bj > a.total_bits) bj = 0;
-  }
-
-  // rotation constants of lane (channel) c: the butterfly signs, s_c, and
-  // the output factor (-1)^popcount(c) / 8
-  float sg[6];
-  float s_in = 1.f, r_out = 1.f;
-  if (a.rotate) {
-    float par = 1.f;
-#pragma unroll
-    for (int k = 0; k < 6; ++k) {
-      sg[k] = ((lane >> k) & 1) ? -1.f : 1.f;
-      par *= sg[k];
-    }
-    s_in = (splitmix64(kRotationSeed + static_cast<uint64_t>(lane)) >> 63) ? -1.f : 1.f;
-    r_out = 0.125f * par;
   }
 
   const float* cu = a.coef + u * a.ustride + b0 * a.head_dim + lane;
@@ -148,9 +97,7 @@ __global__ __launch_bounds__(kWave * kQuantWaves) void k_quant(QuantArgs a) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       if (h >= wpp) break;
-      float v = cur[h];
-      if (a.rotate) v = wht64_lanes(v * s_in, sg) * (inv * r_out);
-      else v = v * inv;
+      const float v = cur[h] * inv;
       if (cnt + b > kWave) flush();
       // most significant bit first: step k compares with the threshold that
       // splits the remaining cells; the ballot is bit plane k's word
@@ -196,7 +143,6 @@ void launch_quant(const Geometry& g, int64_t n_units, const float* coef, int64_t
   a.var_stride = var_stride;
   a.plane_off = plane_off;
   a.rec = rec;
-  a.rotate = g.rotation == TACT_ROTATION_HADAMARD;
   const int64_t per_block = static_cast<int64_t>(kWave) * kQuantWaves;
   const dim3 grid(static_cast<unsigned>((g.n_bins + per_block - 1) / per_block),
                   static_cast<unsigned>(n_units));

@@ -395,6 +395,25 @@ def test_strided_units_and_empty_batch():
     assert tact.compress(empty, 1).shape[0] == 0
 
 
+def test_batched_units_match_single_unit_calls():
+    """A unit's result does not depend on the batch around it: a full ct4b
+    launch (68 units, memory system under load) against single-unit calls,
+    bit for bit, for the transform and for the whole codec."""
+    wl = WORKLOADS["ct4b"]
+    say("batched vs single, ct4b units", wl.n_units)
+    x = generate_units(wl, device="cuda")
+    g = tact.Geometry(*wl.unit_shape, budget_bits=1, max_bits=wl.max_bits, dtype=wl.dtype)
+    c_all = tact.dbg_dct3(x, g)
+    out_all, rec_all = tact.roundtrip(x, 1, wl.max_bits)
+    for u in (0, 33, wl.n_units - 1):
+        assert torch.equal(c_all[u], tact.dbg_dct3(x[u:u + 1], g)[0]), u
+        out_u, rec_u = tact.roundtrip(x[u:u + 1].contiguous(), 1, wl.max_bits)
+        assert torch.equal(rec_all[u], rec_u[0]), u
+        assert torch.equal(out_all[u], out_u[0]), u
+    del x, c_all, out_all, rec_all
+    torch.cuda.empty_cache()
+
+
 FULL = [("ct4b", 1), ("ct4b", 4), ("ct7b", 1), ("ct32b", 1), ("video", 1), ("video", 2)]
 
 
