@@ -44,6 +44,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // scale of the DCT matrix before splitting (keeps C_lo out of fp16
 // subnormals); undone on output
 constexpr float kMatScale = 4096.0f;
+// the same for the Lloyd-Max levels used as a matrix operand
+constexpr float kLevelScale = 2048.0f;
 
 // ---------------------------------------------------------------------------
 // DCT-II matrices of the three axes, fp32, zero padded to 64 x 64:
@@ -64,8 +66,13 @@ __global__ void k_dct_tables(float* __restrict__ tab, int n0, int n1, int n2) {
 }
 
 // fp32 -> (hi, lo) fp16 pair with hi = RNE(x), lo = RNE(x - hi); x must be
-// below 2^15 in magnitude (callers scale first).
+// below 2^15 in magnitude (callers scale first).  The same hi must serve
+// as the operand and in lo's subtraction: an x formed by an inexact product
+// is passed through a register barrier first (the compiler would otherwise
+// form hi from the fused exact product in one place and from the rounded
+// product in the other).
 __device__ __forceinline__ void split2(float x, _Float16& hi, _Float16& lo) {
+#pragma clang fp contract(off)
   hi = static_cast<_Float16>(x);
   lo = static_cast<_Float16>(x - static_cast<float>(hi));
 }
@@ -942,15 +949,12 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
   // 128-bit LDS operations (a 16-lane group then covers all 64 banks once)
   extern __shared__ float4 plane_v4[];
   float* plane = reinterpret_cast<float*>(plane_v4);
-  __shared__ float s_cb[(MODE == MODE_DEQUANT) ? TACT_CODEBOOK_LEVELS : 1];
   const int lane = threadIdx.x % kWave;
   const int wv = threadIdx.x / kWave;
   const int t = lane % 16, g = lane / 16;
   const int H = a.H, W = a.W;
   const int64_t n_planes = a.n_units * a.S * (a.C / 64);
   const int64_t pstep = gridDim.x;
-  if constexpr (MODE == MODE_DEQUANT)
-    for (int j = threadIdx.x; j < TACT_CODEBOOK_LEVELS; j += blockDim.x) s_cb[j] = c_levels[j];
   // byte strides of a slice: one w step, one h row; this lane's columns
   const int cbytes = static_cast<int>(a.C) * 4;
   const int row_bytes = W * cbytes;
@@ -962,12 +966,51 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
   const int wpp = a.head_dim / 64;
 
   __shared__ FragLds<NPH> s_fh;
-  __shared__ FragLds<NPW> s_fw;
+  // W axis: forward, split fragments (FragLds<NPW>); inverse, the fp32
+  // matrix values per lane, [m][ks][v][lane], scaled per row by the bins'
+  // gains, and the levels as (hi, lo) fp16 pairs with a zero entry first
+  constexpr int kAwFloats = FW::MT * FW::KSTEPS * FW::KV * kWave;
+  constexpr int kWBufWords = (MODE == MODE_DEQUANT)
+                                 ? kAwFloats + TACT_CODEBOOK_LEVELS + 1
+                                 : static_cast<int>(sizeof(FragLds<NPW>) / 4);
+  __shared__ __attribute__((aligned(16))) uint32_t s_wbuf[kWBufWords];
+  FragLds<NPW>& s_fw = *reinterpret_cast<FragLds<NPW>*>(s_wbuf);
+  float* s_aw = reinterpret_cast<float*>(s_wbuf);
+  uint32_t* s_lp = s_wbuf + kAwFloats;
   if (wv == 0) {
     frag_to_lds<NPH>(s_fh, a.tab + 1 * 4096, MODE == MODE_DEQUANT, lane);
-    frag_to_lds<NPW>(s_fw, a.tab + 2 * 4096, MODE == MODE_DEQUANT, lane);
+    if constexpr (MODE == MODE_DEQUANT) {
+      const float* tw = a.tab + 2 * 4096;
+#pragma unroll
+      for (int m = 0; m < FW::MT; ++m)
+#pragma unroll
+        for (int ks = 0; ks < FW::KSTEPS; ++ks)
+#pragma unroll
+          for (int v = 0; v < FW::KV; ++v) {
+            const int row = 16 * m + t;                       // output w
+            const int col = ks * FW::KPER + FW::KV * g + v;   // input kw
+            s_aw[((m * FW::KSTEPS + ks) * FW::KV + v) * kWave + lane] = kMatScale * tw[col * 64 + row];
+          }
+    } else {
+      frag_to_lds<NPW>(s_fw, a.tab + 2 * 4096, 0, lane);
+    }
   }
-  __syncthreads();                           // fragments and codebook in LDS
+  if constexpr (MODE == MODE_DEQUANT) {
+    for (int j = threadIdx.x; j <= TACT_CODEBOOK_LEVELS; j += blockDim.x) {
+      uint32_t pr = 0;
+      if (j > 0) {
+        // scaled by 2^11 so that the low half of the smallest level (about
+        // 0.01 at 8 bits) stays a normal fp16 number; |2^11 L| < 2^14
+        const float lv = kLevelScale * c_levels[j - 1];
+        _Float16 h, l;
+        split2(lv, h, l);
+        pr = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h)) |
+             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l)) << 16);
+      }
+      s_lp[j] = pr;
+    }
+  }
+  __syncthreads();                           // fragments and tables in LDS
 
   if constexpr (MODE != MODE_DEQUANT) {
     // the H columns (all h, 64 channels) of this wave's w = wv + 8 j
@@ -1130,7 +1173,9 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const int nib_sh = (4 * t) & 31;
         const bool nib_hi = t >= 8;
-        float xv[4][FW::KSTEPS][FW::KV];
+        // B = the levels as (hi, lo) fp16 pairs; the gains go into A
+        uint32_t bp[4][FW::KSTEPS][FW::KV];
+        float gv[FW::KSTEPS][FW::KV];
 #pragma unroll
         for (int ks = 0; ks < FW::KSTEPS; ++ks)
 #pragma unroll
@@ -1149,22 +1194,70 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
                 codes |= ((nib * 0x204081u) & 0x01010101u) << k;
               }
             }
-            const float gn = __uint_as_float(sb.y);
-            const int base = b > 0 ? (1 << b) - 2 : 0;
+            gv[ks][v] = b > 0 ? __uint_as_float(sb.y) : 0.f;
+            const int base = b > 0 ? (1 << b) - 1 : 0;        // s_lp[0] = 0
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float lv = s_cb[base + static_cast<int>((codes >> (8 * i)) & 0xFFu)];
-              xv[i][ks][v] = b > 0 ? gn * lv : 0.f;
-            }
+            for (int i = 0; i < 4; ++i) bp[i][ks][v] = s_lp[base + static_cast<int>((codes >> (8 * i)) & 0xFFu)];
           }
         // every lane has read the staging before the outputs overwrite it
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        f32x4 acc[4][FW::MT];
+        // A' = (2^12 C^T) diag(g) 2^(2 - e), with 2^e above the row's largest
+        // gain, so |A'| < 2^14; split into fp16 hi / lo.  Output scale:
+        // 2^-12 (matrix) 2^(e - 2) (gains) 2^-11 (levels)
+        float gm = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < FW::KSTEPS; ++ks)
+#pragma unroll
+          for (int v = 0; v < FW::KV; ++v) gm = fmaxf(gm, gv[ks][v]);
+        gm = column_max(gm);
+        int e = 0;
+        if (gm > 0.f) frexpf(gm, &e);
+        const float gsc = ldexpf(1.0f, 2 - e);
+        const float unscale = ldexpf(1.0f, e - 25);
         typename FW::vec ahi_w[FW::MT][FW::KSTEPS], alo_w[FW::MT][FW::KSTEPS];
-        frag_from_lds<NPW>(s_fw, lane, ahi_w, alo_w);
-        contract4<NPW>(ahi_w, alo_w, xv, acc, kOne);
+        const int la = opaque(lane);
+#pragma unroll
+        for (int m = 0; m < FW::MT; ++m)
+#pragma unroll
+          for (int ks = 0; ks < FW::KSTEPS; ++ks)
+#pragma unroll
+            for (int v = 0; v < FW::KV; ++v) {
+              // the product is rounded to fp32 and hidden from the optimizer
+              // before the split: otherwise hi is formed once from the exact
+              // product (fused) and once from the rounded one, and lo pairs
+              // with a hi that differs from the operand hi
+              float ap = s_aw[((m * FW::KSTEPS + ks) * FW::KV + v) * kWave + la] * (gv[ks][v] * gsc);
+              asm volatile("" : "+v"(ap));
+              _Float16 h, l;
+              split2(ap, h, l);
+              ahi_w[m][ks][v] = h;
+              alo_w[m][ks][v] = l;
+            }
+        f32x4 acc[4][FW::MT];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int m = 0; m < FW::MT; ++m) acc[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < FW::KSTEPS; ++ks) {
+            typename FW::vec bhi, blo;
+#pragma unroll
+            for (int v = 0; v < FW::KV; ++v) {
+              bhi[v] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(bp[i][ks][v] & 0xFFFFu));
+              blo[v] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(bp[i][ks][v] >> 16));
+            }
+#pragma unroll
+            for (int m = 0; m < FW::MT; ++m) {
+              acc[i][m] = mfma<NPW>(ahi_w[m][ks], bhi, acc[i][m]);
+              acc[i][m] = mfma<NPW>(alo_w[m][ks], bhi, acc[i][m]);
+              acc[i][m] = mfma<NPW>(ahi_w[m][ks], blo, acc[i][m]);
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < FW::MT; ++m) acc[i][m] *= unscale;
+        }
 #pragma unroll
         for (int m = 0; m < FW::MT; ++m)
 #pragma unroll

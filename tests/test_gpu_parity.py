@@ -9,8 +9,9 @@ seeded synthetic inputs and compares with the oracle on the same inputs:
                             and bits (both sides decide in fp32; the stage
                             entry points quantize without the rotation)
   * unpack:                 byte-exact; dequantize within 1 fp32 rounding
-  * decompress:             bf16 outputs equal except 1-ulp differences on
-                            <= 0.1% of entries (rounding of a ~1e-6 error)
+  * decompress:             bf16 outputs equal except where the exact value
+                            lies within the transform's error bound (1e-5 of
+                            the RMS) of a bf16 rounding boundary
   * end to end:             bits equal except at the cut, codes >= 99.99%
                             equal with mismatches next to a threshold (of
                             the rotated value when the rotation is on), and
@@ -224,15 +225,27 @@ def test_decompress_from_oracle_records(geo, rot):
             ref = O.round_to_bf16(exact)
             a, b = O.bf16_bits(out[u]), O.bf16_bits(ref)
             diff = a != b
-            assert diff.mean() <= 1e-3
-            # a mismatch is a rounding-boundary case: the GPU value is within
-            # half a bf16 ulp of the exact value, up to the transform's
-            # per-element error (bounded by 1e-5 of the unit's RMS; it
-            # dominates near zero)
+            rms = math.sqrt(np.mean(exact ** 2))
+            tol = 1e-5 * rms                     # the transform's error bound
+            # an entry may round differently only where its exact value lies
+            # within the error bound of a bf16 rounding boundary: half an ulp
+            # above |ref|, half an ulp below it (the smaller ulp when |ref| is
+            # a power of two)
+            mag_r = np.maximum(np.abs(ref), np.finfo(np.float32).tiny)
+            e = np.floor(np.log2(mag_r))
+            ulp_up = np.ldexp(1.0, (e - 7).astype(int))
+            ulp_dn = np.where(mag_r == np.ldexp(1.0, e.astype(int)), 0.5 * ulp_up, ulp_up)
+            ax = np.abs(exact)
+            dist = np.minimum(mag_r + 0.5 * ulp_up - ax, ax - (mag_r - 0.5 * ulp_dn))
+            near = dist <= tol
+            assert np.all(near[diff]), np.argwhere(diff & ~near)[:4]
+            # and it is then a rounding-boundary case: the GPU value is within
+            # half a bf16 ulp of the exact value, up to the error bound
             mag = np.maximum(np.abs(exact[diff]), np.abs(out[u][diff]))
             ulp = np.ldexp(1.0, (np.floor(np.log2(mag)) - 7).astype(int))
-            rms = math.sqrt(np.mean(exact ** 2))
-            assert np.all(np.abs(out[u][diff] - exact[diff]) <= 0.5 * ulp + 1e-5 * rms)
+            assert np.all(np.abs(out[u][diff] - exact[diff]) <= 0.5 * ulp + tol)
+            say(f"  unit {u}: bf16 mismatches {diff.mean():.2e} of entries, "
+                f"near a boundary {near.mean():.2e}")
         else:
             ref = O.decompress(recs[u], op, None, rotation=_orot(g))
             assert _rel(out[u], ref) <= 1e-5
