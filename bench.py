@@ -41,7 +41,23 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=2,
                     help="units in the oracle's timed sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (3 times): the "
+                         "reference for scaling the HBM byte counters of a profile")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """Three copies of exactly 1 GiB between device buffers, nothing else."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                      "repeats": 3}), flush=True)
 
 
 def cpu_baseline(wl, budget, n_units):
@@ -110,6 +126,9 @@ def main():
               "per layer, per sequence and needs no exchange between GPUs; run one process "
               "per GPU on its own share of the units.", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import kv_cache_compression_tact_amd as tact
     from tact_inputs import WORKLOADS, generate_units
