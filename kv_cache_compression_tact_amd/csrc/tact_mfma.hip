@@ -865,12 +865,34 @@ __device__ __forceinline__ void contract4(const typename Frag<NP>::vec (&ahi)[Fr
   }
 }
 
-// Persistent blocks of 8 waves (256 VGPRs each): a block walks the planes
-// blockIdx.x, blockIdx.x + gridDim.x, ...  While plane p is transformed,
-// the data of plane p + gridDim.x is fetched into the registers the wave
-// has just consumed (forward: the H columns of its w; inverse: the record
-// words and side info of its kh rows), so memory and compute overlap.
+// Persistent blocks of 8 waves (256 VGPRs each), each walking a list of
+// planes.  While one plane is transformed, the data of the block's next
+// plane is fetched into the registers the wave has just consumed (forward:
+// the H columns of its w; inverse: the record words and side info of its kh
+// rows), so memory and compute overlap.
 constexpr int kPlaneWaves = 8;
+
+// The decoding walk is XCD-aware.  Workgroups are dispatched to the 8 XCDs
+// round robin (block b runs on XCD b % 8) and every XCD has its own L2.  The
+// 64-channel slabs of one slice read the same record lines (side info and
+// code words of bins of consecutive heads are adjacent); spread over XCDs,
+// every L2 would fetch them all.  So in decoding an XCD takes whole slices:
+// XCD x walks slices x, x + 8, x + 16, ... slab by slab, and its blocks take
+// the planes of that list in turn (the grid holds at least 8 blocks).  The
+// forward walk shares no input lines between slabs and keeps the plain order
+// (one group: block b takes planes b, b + grid, ...).
+constexpr int kXcds = 8;
+
+template <int GROUPS>
+struct PlaneWalk {
+  int64_t n_slabs, n_slices, per_group;
+  int group;
+  // plane of position k in this block's group list, or -1 past its end
+  __device__ __forceinline__ int64_t at(int64_t k) const {
+    const int64_t slice = (k / n_slabs) * GROUPS + group;
+    return slice < n_slices ? slice * n_slabs + k % n_slabs : -1;
+  }
+};
 
 // DCT fragments of one contraction (hi / lo per lane) kept in LDS: built
 // once per block, read back right before each contraction
@@ -953,8 +975,13 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
   const int wv = threadIdx.x / kWave;
   const int t = lane % 16, g = lane / 16;
   const int H = a.H, W = a.W;
-  const int64_t n_planes = a.n_units * a.S * (a.C / 64);
-  const int64_t pstep = gridDim.x;
+  constexpr int kGroups = MODE == MODE_DEQUANT ? kXcds : 1;
+  PlaneWalk<kGroups> walk;
+  walk.n_slabs = a.C / 64;
+  walk.n_slices = a.n_units * a.S;
+  walk.group = static_cast<int>(blockIdx.x % kGroups);
+  walk.per_group = (static_cast<int64_t>(gridDim.x) - walk.group + kGroups - 1) / kGroups;
+  const int64_t k0 = blockIdx.x / kGroups;
   // byte strides of a slice: one w step, one h row; this lane's columns
   const int cbytes = static_cast<int>(a.C) * 4;
   const int row_bytes = W * cbytes;
@@ -1029,14 +1056,16 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
           xs[j][0][ks][v] = q.x; xs[j][1][ks][v] = q.y; xs[j][2][ks][v] = q.z; xs[j][3][ks][v] = q.w;
         }
     };
-    if (static_cast<int64_t>(blockIdx.x) < n_planes) {
+    int64_t p = walk.at(k0);
+    if (p >= 0) {
 #pragma unroll
       for (int j = 0; j < SLW; ++j)
-        if (wv + kPlaneWaves * j < W) fetch_cols(blockIdx.x, j);
+        if (wv + kPlaneWaves * j < W) fetch_cols(p, j);
     }
-    for (int64_t p = blockIdx.x; p < n_planes; p += pstep) {
+    for (int64_t k = k0; p >= 0; k += walk.per_group) {
       const PlaneId id = plane_id(a, p);
-      const bool more = p + pstep < n_planes;
+      const int64_t pn = walk.at(k + walk.per_group);
+      const bool more = pn >= 0;
       const __amdgpu_buffer_rsrc_t rcoef =
           make_rsrc(a.out + id.vol, static_cast<int64_t>(row_bytes) * H);
       // ---- H axis: registers -> LDS; then fetch the next plane's columns
@@ -1057,7 +1086,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
               lds_st4(plane + (kh * W + w) * 64 + 4 * t,
                       float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
           }
-        if (more) fetch_cols(p + pstep, j);
+        if (more) fetch_cols(pn, j);
       }
       __syncthreads();
       // ---- W axis: LDS -> epilogue; a wave owns the columns of one kh ----
@@ -1102,6 +1131,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
         }
       }
       __syncthreads();                       // LDS free for the next plane
+      p = pn;
     }
   } else {
     // side info (bits, first plane, gain) and code words of this wave's kh
@@ -1145,13 +1175,15 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
         }
       }
     };
-    if (static_cast<int64_t>(blockIdx.x) < n_planes) {
-      fetch_side(blockIdx.x);
-      fetch_words(blockIdx.x);
+    int64_t p = walk.at(k0);
+    if (p >= 0) {
+      fetch_side(p);
+      fetch_words(p);
     }
-    for (int64_t p = blockIdx.x; p < n_planes; p += pstep) {
+    for (int64_t k = k0; p >= 0; k += walk.per_group) {
       const PlaneId id = plane_id(a, p);
-      const bool more = p + pstep < n_planes;
+      const int64_t pn = walk.at(k + walk.per_group);
+      const bool more = pn >= 0;
       // ---- inverse W: decode into the B fragments, contract; a wave owns one
       // kh row.  The row's LDS area first holds its bins' bits, gains and
       // code words (10 8-byte slots per bin); lane (t, g) then rebuilds the
@@ -1269,7 +1301,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
           }
       }
       // the next plane's side info, in flight during the inverse H pass
-      if (more) fetch_side(p + pstep);
+      if (more) fetch_side(pn);
       __syncthreads();
       // ---- inverse H: LDS -> global; a wave owns the columns of one w -----
       const __amdgpu_buffer_rsrc_t rout =
@@ -1302,10 +1334,11 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
                     float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
         // after the first column, the next plane's code words (their side
         // info has arrived by now)
-        if (j == 0 && more) fetch_words(p + pstep);
+        if (j == 0 && more) fetch_words(pn);
       }
-      if (W <= wv && more) fetch_words(p + pstep);
+      if (W <= wv && more) fetch_words(pn);
       __syncthreads();                       // LDS free for the next plane
+      p = pn;
     }
   }
 }
@@ -1757,6 +1790,12 @@ static int64_t persistent_blocks(const void* fn, int threads, size_t lds, int64_
   return n < 1 ? 1 : n;
 }
 
+// Grid of the XCD-aware plane walk: a whole number of XCD rounds, at least
+// one block per XCD (blocks whose list is empty exit at once).
+static int64_t xcd_grid(int64_t n) {
+  return n < kXcds ? kXcds : n / kXcds * kXcds;
+}
+
 bool plane_supported(const Geometry& g) {
   return (g.axes & 6) == 6 && g.H <= 32 && g.W <= 32 &&
          static_cast<int64_t>(g.H) * g.W * 64 * 4 <= 150 * 1024;
@@ -1796,7 +1835,7 @@ void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in,
     const void* fn = reinterpret_cast<const void*>(&k_plane<NH, NW, M, SL>);                    \
     (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,                   \
                               static_cast<int>(lds));                                           \
-    const dim3 grid(static_cast<unsigned>(persistent_blocks(fn, 64 * kPlaneWaves, lds, n_planes))); \
+    const dim3 grid(static_cast<unsigned>(xcd_grid(persistent_blocks(fn, 64 * kPlaneWaves, lds, n_planes)))); \
     hipLaunchKernelGGL((k_plane<NH, NW, M, SL>), grid, block, lds, s, a);                       \
   } while (0)
 #define TACT_PLANE_SL(NH, NW, SL)                                                               \
