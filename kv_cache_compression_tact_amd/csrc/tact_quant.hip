@@ -11,9 +11,10 @@
 // lane c is channel c of a 64-channel word, so a bin's codes for one bit
 // plane are one ballot.  The cell index is found most significant bit
 // first (binary search over the sorted thresholds), and the ballot of each
-// step is directly the word of that bit plane.  Words are gathered into
-// lanes (word k in lane k) with their record offsets and written up to 64
-// at a time.
+// step is directly the word of that bit plane.  The coded bins of a wave
+// own one contiguous run of record words (bin by bin, plane by plane, word
+// of the plane fastest), so the words are gathered into lanes by their
+// position in that run and written up to 64 at a time.
 #include <hip/hip_runtime.h>
 
 #include "tact_internal.h"
@@ -21,6 +22,10 @@
 namespace tact {
 
 #include "codebook_device.h"
+
+// v_writelane_b32 (the compiler's intrinsic): lane `lane` of `old` takes the
+// uniform value `v`
+__device__ int tact_writelane(int v, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
 
 namespace {
 
@@ -31,13 +36,54 @@ struct QuantArgs {
   const float* coef;         // final DCT coefficients, [u][bin][head_dim]
   int64_t ustride;           // elements between units
   int64_t n_bins, total_bits;
-  int head_dim, max_bits;
+  int max_bits;
   const float* inv_gain;     // fp32 1/gain per bin (0 for gain 0)
   int64_t var_stride;        // floats per unit in inv_gain
   const uint32_t* plane_off; // first bit plane of each bin, [u][bin]
   RecordView rec;
 };
 
+// Codes of one bin of B bits (B >= 1) for its WPP words of 64 channels:
+// lane c holds v = coefficient c / gain of each word.  The ballot of step k
+// (bit plane k, most significant first) goes to lane base + k * WPP + h of
+// the gathered words, which is its place in the record after `base` words.
+template <int WPP, int B>
+__device__ __forceinline__ void code_bin(const float (&v)[4], const float* __restrict__ s_thr,
+                                         int base, int& wlo, int& whi) {
+  // the 2^B - 1 sorted thresholds of B bits; the table is symmetric: its
+  // middle threshold is 0 and the two next split points are -t2 and +t2
+  const float* t = s_thr + ((1 << B) - B - 1);
+  float t2 = 0.f;
+  if constexpr (B > 1) t2 = t[(3 << (B - 2)) - 1];
+  auto stage = [&](bool up, int slot) {
+    const uint64_t wd = __ballot(up);
+    wlo = tact_writelane(static_cast<int>(static_cast<uint32_t>(wd)), slot, wlo);
+    whi = tact_writelane(static_cast<int>(static_cast<uint32_t>(wd >> 32)), slot, whi);
+  };
+#pragma unroll
+  for (int h = 0; h < WPP; ++h) {
+    bool up = 0.f <= v[h];
+    stage(up, base + (B - 1) * WPP + h);
+    if constexpr (B > 1) {
+      int idx = up ? (1 << (B - 1)) : 0;
+      up = (up ? t2 : -t2) <= v[h];
+      stage(up, base + (B - 2) * WPP + h);
+      if (up) idx += 1 << (B - 2);
+      // q points at threshold idx - 1, the last one known to be <= v
+      const float* q = t + idx - 1;
+#pragma unroll
+      for (int k = B - 3; k >= 0; --k) {
+        const float* c = q + (1 << k);
+        up = *c <= v[h];
+        stage(up, base + k * WPP + h);
+        if (up) q = c;
+      }
+    }
+  }
+}
+
+// WPP = head_dim / 64 words per bit plane of a bin
+template <int WPP>
 __global__ __launch_bounds__(kWave * kQuantWaves) void k_quant(QuantArgs a) {
   __shared__ float s_thr[TACT_CODEBOOK_THRESHOLDS];
   for (int j = threadIdx.x; j < TACT_CODEBOOK_THRESHOLDS; j += blockDim.x) s_thr[j] = c_thresholds[j];
@@ -46,7 +92,7 @@ __global__ __launch_bounds__(kWave * kQuantWaves) void k_quant(QuantArgs a) {
   const int64_t u = blockIdx.y;
   const int64_t b0 = (static_cast<int64_t>(blockIdx.x) * kQuantWaves + threadIdx.x / kWave) * kWave;
   if (b0 >= a.n_bins) return;
-  const int wpp = a.head_dim / 64;
+  constexpr int kHeadDim = 64 * WPP;
 
   // side info of bin b0 + lane
   int bj = 0, pj = 0;
@@ -60,69 +106,55 @@ __global__ __launch_bounds__(kWave * kQuantWaves) void k_quant(QuantArgs a) {
     if (bj > a.max_bits || static_cast<int64_t>(static_cast<uint32_t>(pj)) + bj > a.total_bits) bj = 0;
   }
 
-  const float* cu = a.coef + u * a.ustride + b0 * a.head_dim + lane;
+  const float* cu = a.coef + u * a.ustride + b0 * kHeadDim + lane;
   uint64_t* words = reinterpret_cast<uint64_t*>(a.rec.base + u * a.rec.stride + a.rec.off_codes);
-  // gathered words: lane k holds word k and its index in the record
-  uint32_t wlo = 0, whi = 0, widx = 0;
+  // gathered words: lane k holds word first + k of the record
+  int wlo = 0, whi = 0;
   int cnt = 0;
+  int64_t first = 0;
   auto flush = [&]() {
-    if (lane < cnt) words[widx] = (static_cast<uint64_t>(whi) << 32) | wlo;
+    if (lane < cnt)
+      words[first + lane] = (static_cast<uint64_t>(static_cast<uint32_t>(whi)) << 32) |
+                            static_cast<uint32_t>(wlo);
     cnt = 0;
   };
 
-  // coded bins of this wave, lowest first; the words of the next one are
-  // fetched while the current one is quantized (up to 4 per bin)
+  // coded bins of this wave, lowest first; the coefficients of the next one
+  // are in flight while the current one is coded
   uint64_t todo = __ballot(bj > 0);
   float nxt[4] = {0.f, 0.f, 0.f, 0.f};
   auto fetch = [&](int j) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
-      if (h < wpp) nxt[h] = cu[j * a.head_dim + 64 * h];
+    for (int h = 0; h < WPP; ++h) nxt[h] = cu[j * kHeadDim + 64 * h];
   };
   if (todo) fetch(__builtin_ctzll(todo));
   while (todo) {
     const int j = __builtin_ctzll(todo);
     todo &= todo - 1;
-    float cur[4];
+    float v[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) cur[h] = nxt[h];
+    for (int h = 0; h < 4; ++h) v[h] = nxt[h];
     if (todo) fetch(__builtin_ctzll(todo));
     const int b = __builtin_amdgcn_readlane(bj, j);
-    const uint32_t p0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(pj, j));
+    const int64_t w0 = static_cast<int64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(pj, j))) * WPP;
     const float inv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ij), j));
-    const float* t = s_thr + ((1 << b) - b - 1);            // 2^b - 1 sorted thresholds
-    // the table is symmetric: its middle threshold is 0 and the two next
-    // split points are -t2 and +t2
-    const float t2 = b > 1 ? t[(3 << (b - 2)) - 1] : 0.f;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      if (h >= wpp) break;
-      const float v = cur[h] * inv;
-      if (cnt + b > kWave) flush();
-      // most significant bit first: step k compares with the threshold that
-      // splits the remaining cells; the ballot is bit plane k's word
-      auto stage = [&](uint64_t wd, int k) {
-        if (lane == cnt) {
-          wlo = static_cast<uint32_t>(wd);
-          whi = static_cast<uint32_t>(wd >> 32);
-          widx = (p0 + static_cast<uint32_t>(k)) * wpp + h;
-        }
-        ++cnt;
-      };
-      bool up = 0.f <= v;
-      stage(__ballot(up), b - 1);
-      int idx = up ? (1 << (b - 1)) : 0;
-      if (b > 1) {
-        up = (up ? t2 : -t2) <= v;
-        stage(__ballot(up), b - 2);
-        if (up) idx += 1 << (b - 2);
-        for (int k = b - 3; k >= 0; --k) {
-          up = t[idx + (1 << k) - 1] <= v;
-          stage(__ballot(up), k);
-          if (up) idx += 1 << k;
-        }
-      }
+    for (int h = 0; h < WPP; ++h) v[h] *= inv;
+    // this bin's b * WPP words must follow the gathered ones in the record
+    // and fit beside them
+    if (cnt > 0 && (w0 != first + cnt || cnt + b * WPP > kWave)) flush();
+    if (cnt == 0) first = w0;
+    switch (b) {
+      case 1: code_bin<WPP, 1>(v, s_thr, cnt, wlo, whi); break;
+      case 2: code_bin<WPP, 2>(v, s_thr, cnt, wlo, whi); break;
+      case 3: code_bin<WPP, 3>(v, s_thr, cnt, wlo, whi); break;
+      case 4: code_bin<WPP, 4>(v, s_thr, cnt, wlo, whi); break;
+      case 5: code_bin<WPP, 5>(v, s_thr, cnt, wlo, whi); break;
+      case 6: code_bin<WPP, 6>(v, s_thr, cnt, wlo, whi); break;
+      case 7: code_bin<WPP, 7>(v, s_thr, cnt, wlo, whi); break;
+      default: code_bin<WPP, 8>(v, s_thr, cnt, wlo, whi); break;
     }
+    cnt += b * WPP;
   }
   flush();
 }
@@ -137,7 +169,6 @@ void launch_quant(const Geometry& g, int64_t n_units, const float* coef, int64_t
   a.ustride = ustride;
   a.n_bins = g.n_bins;
   a.total_bits = g.total_bits;
-  a.head_dim = g.head_dim;
   a.max_bits = g.max_bits;
   a.inv_gain = inv_gain;
   a.var_stride = var_stride;
@@ -146,7 +177,10 @@ void launch_quant(const Geometry& g, int64_t n_units, const float* coef, int64_t
   const int64_t per_block = static_cast<int64_t>(kWave) * kQuantWaves;
   const dim3 grid(static_cast<unsigned>((g.n_bins + per_block - 1) / per_block),
                   static_cast<unsigned>(n_units));
-  hipLaunchKernelGGL(k_quant, grid, dim3(kWave * kQuantWaves), 0, s, a);
+  const dim3 block(kWave * kQuantWaves);
+  if (g.head_dim == 64) hipLaunchKernelGGL(k_quant<1>, grid, block, 0, s, a);
+  else if (g.head_dim == 128) hipLaunchKernelGGL(k_quant<2>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_quant<4>, grid, block, 0, s, a);
 }
 
 }  // namespace tact

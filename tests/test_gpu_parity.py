@@ -71,6 +71,12 @@ GEOMS = [
     (2, 5, 3, 2, 256, 4, 8, torch.bfloat16),
     (33, 3, 2, 1, 128, 3, 5, torch.bfloat16),       # S beyond 32
     (64, 2, 3, 1, 64, 1, 8, torch.float32),
+    # wider planes: each H / W contraction size and both decoding kernels
+    # (32-channel half planes up to ~600 positions, 64-channel planes above)
+    (3, 17, 23, 2, 128, 2, 8, torch.bfloat16),
+    (2, 10, 21, 1, 64, 1, 8, torch.float32),
+    (2, 20, 12, 2, 64, 3, 8, torch.bfloat16),
+    (2, 26, 30, 1, 128, 1, 8, torch.bfloat16),
 ]
 
 
