@@ -1139,39 +1139,43 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
     int bj[SLH], pjv[SLH];
     float gjv[SLH];
     uint2 wd[SLH][8];
+    // record reads through buffer descriptors (32-bit offsets per lane)
     auto fetch_side = [&](int64_t p) {
       const PlaneId id = plane_id(a, p);
       const uint8_t* r = a.rec.base + id.u * a.rec.stride;
-      const uint8_t* bits = r + a.rec.off_bits;
-      const float* gains = reinterpret_cast<const float*>(r + a.rec.off_gains);
-      const uint32_t* poff = a.plane_off + id.u * a.n_bins;
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(r + a.rec.off_bits, a.n_bins);
+      const __amdgpu_buffer_rsrc_t rg = make_rsrc(r + a.rec.off_gains, 4 * a.n_bins);
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.plane_off + id.u * a.n_bins, 4 * a.n_bins);
 #pragma unroll
       for (int q = 0; q < SLH; ++q) {
         const int kh = wv + kPlaneWaves * q;
         bj[q] = 0; pjv[q] = 0; gjv[q] = 0.f;
         if (kh < H && lane < W) {
-          const int64_t bin = bin_of3(id, kh, lane);
-          bj[q] = bits[bin];
-          pjv[q] = static_cast<int>(poff[bin]);
-          gjv[q] = gains[bin];
+          const int bin = static_cast<int>(bin_of3(id, kh, lane));
+          bj[q] = __builtin_amdgcn_raw_buffer_load_b8(rb, bin, 0, 0);
+          pjv[q] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(ro, 4 * bin, 0, 0));
+          gjv[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, 4 * bin, 0, 0));
         }
       }
     };
     auto fetch_words = [&](int64_t p) {
       const PlaneId id = plane_id(a, p);
-      const uint64_t* words =
-          reinterpret_cast<const uint64_t*>(a.rec.base + id.u * a.rec.stride + a.rec.off_codes);
+      // the plane words of this slab: 64-bit word (plane * wpp + half)
+      const __amdgpu_buffer_rsrc_t rw =
+          make_rsrc(a.rec.base + id.u * a.rec.stride + a.rec.off_codes, a.total_bits * wpp * 8);
 #pragma unroll
       for (int q = 0; q < SLH; ++q) {
         int b = bj[q];
         const int64_t pj = static_cast<uint32_t>(pjv[q]);
         if (b > a.max_bits || pj + b > a.total_bits) b = 0;
         bj[q] = b;
+        const int base = 8 * (static_cast<int>(pj) * wpp + id.half);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          uint64_t w = 0;
-          if (k < b) w = words[(pj + k) * wpp + id.half];
-          wd[q][k] = uint2{static_cast<uint32_t>(w), static_cast<uint32_t>(w >> 32)};
+          uint2 w = uint2{0u, 0u};
+          if (k < b)
+            w = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rw, base + 8 * wpp * k, 0, 0));
+          wd[q][k] = w;
         }
       }
     };
@@ -1185,26 +1189,31 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
       const int64_t pn = walk.at(k + walk.per_group);
       const bool more = pn >= 0;
       // ---- inverse W: decode into the B fragments, contract; a wave owns one
-      // kh row.  The row's LDS area first holds its bins' bits, gains and
-      // code words (10 8-byte slots per bin); lane (t, g) then rebuilds the
-      // codes of its channels 4t..4t+3 for its K rows kw: one 64-bit word
-      // per bit plane gives a nibble, spread into one byte per channel.
+      // kh row.  The row's LDS area first holds its bins' side info and code
+      // words, 80 bytes per bin: {bits, gain, 0, 0}, the low 32-bit halves of
+      // the 8 plane words, then their high halves (planes at or above the
+      // bin's bit width are 0).  Lane (t, g) then rebuilds the codes of its
+      // channels 4t..4t+3 for its K rows kw: it reads the 8 halves that hold
+      // its channels at once, and each plane gives a nibble, spread into one
+      // byte per channel.
 #pragma unroll
       for (int q = 0; q < SLH; ++q) {
         const int kh = wv + kPlaneWaves * q;
         if (kh >= H) break;
         float* row = plane + static_cast<int64_t>(kh) * W * 64;
-        uint2* st = reinterpret_cast<uint2*>(row);
+        uint4* st = reinterpret_cast<uint4*>(row);
         if (lane < W) {
-          st[lane * 10] = uint2{static_cast<uint32_t>(bj[q]), __float_as_uint(gjv[q])};
-#pragma unroll
-          for (int k = 0; k < 8; ++k) st[lane * 10 + 1 + k] = wd[q][k];
+          st[lane * 5] = uint4{static_cast<uint32_t>(bj[q]), __float_as_uint(gjv[q]), 0u, 0u};
+          st[lane * 5 + 1] = uint4{wd[q][0].x, wd[q][1].x, wd[q][2].x, wd[q][3].x};
+          st[lane * 5 + 2] = uint4{wd[q][4].x, wd[q][5].x, wd[q][6].x, wd[q][7].x};
+          st[lane * 5 + 3] = uint4{wd[q][0].y, wd[q][1].y, wd[q][2].y, wd[q][3].y};
+          st[lane * 5 + 4] = uint4{wd[q][4].y, wd[q][5].y, wd[q][6].y, wd[q][7].y};
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const int nib_sh = (4 * t) & 31;
-        const bool nib_hi = t >= 8;
+        const int half = t >= 8 ? 3 : 1;     // the halves holding channels 4t..4t+3
         // B = the levels as (hi, lo) fp16 pairs; the gains go into A
         uint32_t bp[4][FW::KSTEPS][FW::KV];
         float gv[FW::KSTEPS][FW::KV];
@@ -1213,18 +1222,21 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
 #pragma unroll
           for (int v = 0; v < FW::KV; ++v) {
             const int kw = ks * FW::KPER + FW::KV * g + v;
-            uint2 sb = uint2{0u, 0u};
-            if (kw < W) sb = st[kw * 10];
+            uint4 sb = uint4{0u, 0u, 0u, 0u}, w03 = sb, w47 = sb;
+            if (kw < W) {
+              sb = st[kw * 5];
+              w03 = st[kw * 5 + half];
+              w47 = st[kw * 5 + half + 1];
+            }
+            const uint32_t wk[8] = {w03.x, w03.y, w03.z, w03.w, w47.x, w47.y, w47.z, w47.w};
             const int b = static_cast<int>(sb.x);
             // byte i of `codes` collects the bits of channel 4t + i
             uint32_t codes = 0;
+#pragma unroll
             for (int k = 0; k < 8; ++k) {
               if (__ballot(k < b) == 0) break;
-              if (k < b) {
-                const uint2 w = st[kw * 10 + 1 + k];
-                const uint32_t nib = __builtin_amdgcn_ubfe(nib_hi ? w.y : w.x, nib_sh, 4);
-                codes |= ((nib * 0x204081u) & 0x01010101u) << k;
-              }
+              const uint32_t nib = __builtin_amdgcn_ubfe(wk[k], nib_sh, 4);
+              codes |= ((nib * 0x204081u) & 0x01010101u) << k;
             }
             gv[ks][v] = b > 0 ? __uint_as_float(sb.y) : 0.f;
             const int base = b > 0 ? (1 << b) - 1 : 0;        // s_lp[0] = 0
