@@ -884,13 +884,16 @@ constexpr int kPlaneWaves = 8;
 constexpr int kXcds = 8;
 
 template <int GROUPS>
+// Plane indices fit in 32 bits: a launch covers at most one workspace chunk
+// of units (24 GiB of fp32 volume, under 2^28 planes of >= 64 entries), so
+// the index arithmetic runs in 32-bit unsigned integers.
 struct PlaneWalk {
-  int64_t n_slabs, n_slices, per_group;
+  uint32_t n_slabs, n_slices, per_group;
   int group;
   // plane of position k in this block's group list, or -1 past its end
-  __device__ __forceinline__ int64_t at(int64_t k) const {
-    const int64_t slice = (k / n_slabs) * GROUPS + group;
-    return slice < n_slices ? slice * n_slabs + k % n_slabs : -1;
+  __device__ __forceinline__ int64_t at(uint32_t k) const {
+    const uint32_t slice = (k / n_slabs) * GROUPS + group;
+    return slice < n_slices ? static_cast<int64_t>(slice * n_slabs + k % n_slabs) : -1;
   }
 };
 
@@ -945,14 +948,15 @@ struct PlaneId {
   int64_t vol;     // element offset of (u, s, 0, 0, 0)
 };
 
-__device__ __forceinline__ PlaneId plane_id(const PlaneArgs& a, int64_t p) {
-  const int64_t n_slabs = a.C / 64;
+__device__ __forceinline__ PlaneId plane_id(const PlaneArgs& a, int64_t p64) {
+  const uint32_t p = static_cast<uint32_t>(p64);
+  const uint32_t n_slabs = static_cast<uint32_t>(a.C / 64);
   PlaneId id;
-  const int64_t slab = p % n_slabs;
-  const int64_t rest = p / n_slabs;
-  id.s = static_cast<int>(rest % a.S);
-  id.u = rest / a.S;
-  id.c0 = slab * 64;
+  const uint32_t slab = p % n_slabs;
+  const uint32_t rest = p / n_slabs;
+  id.s = static_cast<int>(rest % static_cast<uint32_t>(a.S));
+  id.u = rest / static_cast<uint32_t>(a.S);
+  id.c0 = static_cast<int64_t>(slab) * 64;
   id.head = id.c0 / a.head_dim;
   id.half = static_cast<int>((id.c0 % a.head_dim) / 64);
   id.vol = id.u * a.ustride + static_cast<int64_t>(id.s) * a.H * a.W * a.C;
@@ -977,11 +981,11 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
   const int H = a.H, W = a.W;
   constexpr int kGroups = MODE == MODE_DEQUANT ? kXcds : 1;
   PlaneWalk<kGroups> walk;
-  walk.n_slabs = a.C / 64;
-  walk.n_slices = a.n_units * a.S;
+  walk.n_slabs = static_cast<uint32_t>(a.C / 64);
+  walk.n_slices = static_cast<uint32_t>(a.n_units * a.S);
   walk.group = static_cast<int>(blockIdx.x % kGroups);
-  walk.per_group = (static_cast<int64_t>(gridDim.x) - walk.group + kGroups - 1) / kGroups;
-  const int64_t k0 = blockIdx.x / kGroups;
+  walk.per_group = (gridDim.x - walk.group + kGroups - 1) / kGroups;
+  const uint32_t k0 = blockIdx.x / kGroups;
   // byte strides of a slice: one w step, one h row; this lane's columns
   const int cbytes = static_cast<int>(a.C) * 4;
   const int row_bytes = W * cbytes;
@@ -1062,7 +1066,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
       for (int j = 0; j < SLW; ++j)
         if (wv + kPlaneWaves * j < W) fetch_cols(p, j);
     }
-    for (int64_t k = k0; p >= 0; k += walk.per_group) {
+    for (uint32_t k = k0; p >= 0; k += walk.per_group) {
       const PlaneId id = plane_id(a, p);
       const int64_t pn = walk.at(k + walk.per_group);
       const bool more = pn >= 0;
@@ -1184,7 +1188,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
       fetch_side(p);
       fetch_words(p);
     }
-    for (int64_t k = k0; p >= 0; k += walk.per_group) {
+    for (uint32_t k = k0; p >= 0; k += walk.per_group) {
       const PlaneId id = plane_id(a, p);
       const int64_t pn = walk.at(k + walk.per_group);
       const bool more = pn >= 0;
