@@ -185,6 +185,8 @@ __device__ __forceinline__ void wht64(float& a0, float& a1, float& a2, float& a3
 // the descriptor's byte range return 0 and stores past it are dropped, so
 // padded rows need no branch.  voff is per lane, soff uniform.
 constexpr int kBufWord3 = 0x00020000;
+// a lane offset past every buffer the kernels address (all under 2^31 bytes)
+constexpr int kPastBuffer = 0x7FFFFFF0;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufWord3);
 }
@@ -1143,7 +1145,11 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
     int bj[SLH], pjv[SLH];
     float gjv[SLH];
     uint2 wd[SLH][8];
-    // record reads through buffer descriptors (32-bit offsets per lane)
+    // Record reads through buffer descriptors (32-bit offsets per lane).
+    // Every call issues the same loads: lanes with nothing to read take an
+    // offset past the buffer and read 0.  With fixed load and store counts
+    // the compiler's waits count the stores issued after a load instead of
+    // waiting for all memory operations.
     auto fetch_side = [&](int64_t p) {
       const PlaneId id = plane_id(a, p);
       const uint8_t* r = a.rec.base + id.u * a.rec.stride;
@@ -1153,13 +1159,12 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
 #pragma unroll
       for (int q = 0; q < SLH; ++q) {
         const int kh = wv + kPlaneWaves * q;
-        bj[q] = 0; pjv[q] = 0; gjv[q] = 0.f;
-        if (kh < H && lane < W) {
-          const int bin = static_cast<int>(bin_of3(id, kh, lane));
-          bj[q] = __builtin_amdgcn_raw_buffer_load_b8(rb, bin, 0, 0);
-          pjv[q] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(ro, 4 * bin, 0, 0));
-          gjv[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, 4 * bin, 0, 0));
-        }
+        const bool ok = kh < H && lane < W;
+        const int bin = static_cast<int>(bin_of3(id, kh, lane));
+        const int vb = ok ? bin : kPastBuffer, vw = ok ? 4 * bin : kPastBuffer;
+        bj[q] = __builtin_amdgcn_raw_buffer_load_b8(rb, vb, 0, 0);
+        pjv[q] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(ro, vw, 0, 0));
+        gjv[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, vw, 0, 0));
       }
     };
     auto fetch_words = [&](int64_t p) {
@@ -1175,12 +1180,9 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
         bj[q] = b;
         const int base = 8 * (static_cast<int>(pj) * wpp + id.half);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          uint2 w = uint2{0u, 0u};
-          if (k < b)
-            w = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rw, base + 8 * wpp * k, 0, 0));
-          wd[q][k] = w;
-        }
+        for (int k = 0; k < 8; ++k)
+          wd[q][k] = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_raw_buffer_load_b64(rw, k < b ? base + 8 * wpp * k : kPastBuffer, 0, 0));
       }
     };
     int64_t p = walk.at(k0);
@@ -1200,12 +1202,16 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
       // channels 4t..4t+3 for its K rows kw: it reads the 8 halves that hold
       // its channels at once, and each plane gives a nibble, spread into one
       // byte per channel.
+      //   All rows are staged first.  The next plane's side info is then
+      // fetched, and its code words at the end of this W stage: both before
+      // this plane's stores.  Vector memory operations complete in issue
+      // order, so waiting for those loads never waits for the stores, which
+      // drain during the next W stage.
 #pragma unroll
       for (int q = 0; q < SLH; ++q) {
         const int kh = wv + kPlaneWaves * q;
         if (kh >= H) break;
-        float* row = plane + static_cast<int64_t>(kh) * W * 64;
-        uint4* st = reinterpret_cast<uint4*>(row);
+        uint4* st = reinterpret_cast<uint4*>(plane + static_cast<int64_t>(kh) * W * 64);
         if (lane < W) {
           st[lane * 5] = uint4{static_cast<uint32_t>(bj[q]), __float_as_uint(gjv[q]), 0u, 0u};
           st[lane * 5 + 1] = uint4{wd[q][0].x, wd[q][1].x, wd[q][2].x, wd[q][3].x};
@@ -1213,9 +1219,19 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
           st[lane * 5 + 3] = uint4{wd[q][0].y, wd[q][1].y, wd[q][2].y, wd[q][3].y};
           st[lane * 5 + 4] = uint4{wd[q][4].y, wd[q][5].y, wd[q][6].y, wd[q][7].y};
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+      // (the last plane of the walk fetches itself again: same loads, unused)
+      const int64_t pf = more ? pn : p;
+      fetch_side(pf);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int q = 0; q < SLH; ++q) {
+        const int kh = wv + kPlaneWaves * q;
+        if (kh >= H) break;
+        float* row = plane + static_cast<int64_t>(kh) * W * 64;
+        const uint4* st = reinterpret_cast<const uint4*>(row);
         const int nib_sh = (4 * t) & 31;
         const int half = t >= 8 ? 3 : 1;     // the halves holding channels 4t..4t+3
         // B = the levels as (hi, lo) fp16 pairs; the gains go into A
@@ -1316,16 +1332,17 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
                       float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
           }
       }
-      // the next plane's side info, in flight during the inverse H pass
-      if (more) fetch_side(pn);
+      fetch_words(pf);
       __syncthreads();
       // ---- inverse H: LDS -> global; a wave owns the columns of one w -----
-      const __amdgpu_buffer_rsrc_t rout =
-          make_rsrc(a.out + id.vol, static_cast<int64_t>(row_bytes) * H);
+      // Every wave issues the same stores: a column past W is computed from
+      // column W - 1 and stored through an empty buffer (dropped).
 #pragma unroll
       for (int j = 0; j < SLW; ++j) {
-        const int w = wv + kPlaneWaves * j;
-        if (w >= W) break;
+        const bool wok = wv + kPlaneWaves * j < W;
+        const int w = wok ? wv + kPlaneWaves * j : W - 1;
+        const __amdgpu_buffer_rsrc_t rout =
+            make_rsrc(a.out + id.vol, wok ? static_cast<int64_t>(row_bytes) * H : 0);
         float xv[4][FH::KSTEPS][FH::KV];
 #pragma unroll
         for (int ks = 0; ks < FH::KSTEPS; ++ks)
@@ -1348,11 +1365,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
           for (int rr = 0; rr < 4; ++rr)
             buf_st4(rout, voff, (16 * m + rr) * row_bytes,
                     float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
-        // after the first column, the next plane's code words (their side
-        // info has arrived by now)
-        if (j == 0 && more) fetch_words(pn);
       }
-      if (W <= wv && more) fetch_words(pn);
       __syncthreads();                       // LDS free for the next plane
       p = pn;
     }
