@@ -17,6 +17,7 @@ the docstrings use these short forms:
   [Method/dec]    the decoding paragraph that follows stage 4
   [Contrib/k]     "Key Contributions", item k
   [Findings/SQ]   "Main Findings", bullet on gain-shape scalar quantization
+  [Findings/batch] "Main Findings", bullet on batch and throughput at equal HBM
   [Abstract]      "Authors' abstract"
 
 Where the page leaves a step open, the plain reading taken here is stated in
@@ -54,7 +55,7 @@ __all__ = [
     "splitmix64", "rotation_signs", "rotate", "unrotate", "ROTATION_SEED",
     "record_layout", "pack_record", "unpack_record", "round_to_bf16",
     "bf16_bits", "compress", "decompress", "roundtrip", "mse",
-    "spectral_flatness", "occupancy_bits", "absmax_to_std",
+    "spectral_flatness", "occupancy_bits", "absmax_to_std", "capacity_model",
 ]
 
 
@@ -690,3 +691,30 @@ def absmax_to_std(coef: np.ndarray) -> np.ndarray:
     am = np.max(np.abs(c), axis=-1)
     keep = rms > 0
     return am[keep] / rms[keep]
+
+
+# --------------------------------------------------------------------------
+# O13: serving capacity at equal HBM          [Findings/batch], [Method/1]
+# --------------------------------------------------------------------------
+def capacity_model(p: Params, layers: int, text_tokens: int, hbm_bytes: int,
+                   weight_bytes: int, window_layers: int = 0,
+                   reserve_bytes: int = 0) -> dict:
+    """Per-request cache and maximum decoding batch, bf16 against coded.
+
+    [Findings/batch] ("Main Findings", the bullet on batch and throughput at
+    equal HBM): the per-request cache shrinks and the largest batch that fits
+    beside the weights grows.  [Method/1]: text keys and values stay bf16.
+    READING: a request is one sequence; each layer holds its text KV
+    (text_tokens x K,V x kv_heads x head_dim bf16) and its visual K and V
+    volumes, either bf16 or one record each; layers with sliding-window
+    attention ("Future Directions") keep bf16 visual KV; the batch is the
+    number of whole requests in the HBM left after the weights and a reserve.
+    """
+    text = text_tokens * layers * 2 * p.kv_heads * p.head_dim * 2
+    unit_bf16 = p.n_entries * 2
+    rec = record_layout(p)["size"]
+    bf16 = text + layers * 2 * unit_bf16
+    coded = text + (layers - window_layers) * 2 * rec + window_layers * 2 * unit_bf16
+    free = max(hbm_bytes - weight_bytes - reserve_bytes, 0)
+    return dict(request_bytes_bf16=bf16, request_bytes_coded=coded,
+                batch_bf16=free // bf16, batch_coded=free // coded)
