@@ -55,7 +55,7 @@ __all__ = [
     "splitmix64", "rotation_signs", "rotate", "unrotate", "ROTATION_SEED",
     "record_layout", "pack_record", "unpack_record", "round_to_bf16",
     "bf16_bits", "compress", "decompress", "roundtrip", "mse",
-    "spectral_flatness", "occupancy_bits", "absmax_to_std", "capacity_model",
+    "spectral_flatness", "occupancy_bits", "absmax_to_std", "capacity_model", "attend",
 ]
 
 
@@ -718,3 +718,41 @@ def capacity_model(p: Params, layers: int, text_tokens: int, hbm_bytes: int,
     free = max(hbm_bytes - weight_bytes - reserve_bytes, 0)
     return dict(request_bytes_bf16=bf16, request_bytes_coded=coded,
                 batch_bf16=free // bf16, batch_coded=free // coded)
+
+
+# --------------------------------------------------------------------------
+# O14: attention over the decoded visual cache                 [Method/dec]
+# --------------------------------------------------------------------------
+def attend(k_rec: np.ndarray, v_rec: np.ndarray, p: Params, q: np.ndarray,
+           scale: float, axes=(0, 1, 2), rotation: str = "hadamard"):
+    """One decoding step of attention over one unit pair's visual tokens.
+
+    [Method/dec]: decoding reverses the codec and can be fused into the
+    attention kernel, so that the reconstructed cache is never materialized.
+    This is the plain definition of what such a kernel returns, written on
+    the decoded cache itself (fp64, no output rounding).
+    READING: q holds one query per query head, shape (q_heads, head_dim),
+    with grouped heads: query head r reads kv head r // (q_heads / kv_heads).
+    The result is the softmax attention of each query over the S*H*W visual
+    tokens of its kv head, out[r] = sum_t p_t v_t with
+    p_t = exp(scale q_r . k_t - lse_r), and lse_r = log sum_t exp(scale q_r . k_t),
+    which is what a caller needs to merge it with attention over the text
+    tokens.
+    """
+    K = decompress(k_rec, p, None, axes, rotation)
+    V = decompress(v_rec, p, None, axes, rotation)
+    q = np.asarray(q, dtype=np.float64)
+    qh = q.shape[0]
+    rep = qh // p.kv_heads
+    n = p.S * p.H * p.W
+    out = np.zeros((qh, p.head_dim))
+    lse = np.zeros(qh)
+    for r in range(qh):
+        h = r // rep
+        k = K[:, :, :, h, :].reshape(n, p.head_dim)
+        v = V[:, :, :, h, :].reshape(n, p.head_dim)
+        s = scale * (k @ q[r])
+        m = s.max()
+        lse[r] = m + np.log(np.sum(np.exp(s - m)))
+        out[r] = np.exp(s - lse[r]) @ v
+    return out, lse
