@@ -144,6 +144,36 @@ tact_status tact_roundtrip(const tact_params* p, int64_t n_units,
                            void* records, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Decoding fused into attention --------------------------------------
+ * The page's decoding paragraph ("Methodology in Plain English") notes that
+ * decoding can be fused into the attention kernel, so that the reconstructed
+ * cache is never materialized.  tact_attend runs one decoding step of
+ * attention over the visual tokens of n_pairs unit pairs -- the K record and
+ * the V record of one layer and sequence, both coded with *p -- reading only
+ * the records:
+ *   k_records, v_records  device, n_pairs records each, tact_record_bytes(p)
+ *            apart (as tact_compress writes them), 256-byte aligned;
+ *   q        device float32 [n_pairs][q_heads][head_dim]; query head r reads
+ *            kv head r / (q_heads / kv_heads) (grouped heads);
+ *   out      device float32 [n_pairs][q_heads][head_dim]:
+ *            out = sum_t p_t v_t over the S*H*W visual tokens t, with
+ *            p_t = exp(scale * q . k_t - lse) (the softmax over those tokens);
+ *   lse      device float32 [n_pairs][q_heads]: log sum_t exp(scale * q . k_t),
+ *            which merges the result with attention over the text tokens;
+ * where k_t, v_t are the decoded cache: the values tact_decompress
+ * reconstructs, before the output rounding.  The inverse DCT is linear, so
+ * the scores are the inverse 3-D DCT of the per-bin projections q . c_f and
+ * the output is the sum over coded V bins of DCT3(p)_f c_f; only coded bins
+ * are read.  Limits (TACT_ERR_UNSUPPORTED otherwise): q_heads a multiple of
+ * kv_heads with at most 16 query heads per kv head, S*H*W <= 40000.  q, out
+ * and lse are 4-byte aligned and must not overlap; n_pairs == 0 is a no-op.
+ * Precision: fp32 throughout (see the tests for the bound). */
+size_t tact_attend_workspace_bytes(const tact_params* p, int64_t n_pairs, int32_t q_heads);
+tact_status tact_attend(const tact_params* p, int64_t n_pairs, int32_t q_heads,
+                        const void* k_records, const void* v_records, const float* q,
+                        float scale, float* out, float* lse, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* tact_status_string(tact_status s);
 

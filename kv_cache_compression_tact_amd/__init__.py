@@ -15,6 +15,7 @@ without it raises ImportError (build it with
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from dataclasses import dataclass
 
@@ -54,6 +55,8 @@ def _load():
         "tact_status_string": (ctypes.c_char_p, [i32]),
         "tact_last_error": (ctypes.c_char_p, []),
         "tact_codebook": (i32, [i32, vp, vp]),
+        "tact_attend_workspace_bytes": (sz, [P, i64, i32]),
+        "tact_attend": (i32, [P, i64, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]),
         "tact_dbg_workspace_bytes": (sz, [P, i64]),
         "tact_dbg_dct3": (i32, [P, i64, i32, vp, vp, vp, sz, vp]),
         "tact_dbg_bin_variance": (i32, [P, i64, vp, vp, vp]),
@@ -73,6 +76,7 @@ _lib = _load()
 EXPORTED = ("tact_params_init", "tact_record_bytes", "tact_workspace_bytes",
             "tact_compress", "tact_decompress", "tact_roundtrip",
             "tact_status_string", "tact_last_error", "tact_codebook",
+            "tact_attend_workspace_bytes", "tact_attend",
             "tact_dbg_workspace_bytes", "tact_dbg_dct3", "tact_dbg_bin_variance",
             "tact_dbg_allocate", "tact_dbg_quantize", "tact_dbg_unpack",
             "tact_dbg_dequantize")
@@ -232,6 +236,38 @@ def roundtrip(kv: torch.Tensor, budget_bits: int, max_bits: int = 8, *,
                                _unit_stride(out), _ptr(records), _ptr(ws), ws.numel(),
                                _stream()), "tact_roundtrip")
     return out, records
+
+
+def attend(k_records: torch.Tensor, v_records: torch.Tensor, geom: Geometry,
+           q: torch.Tensor, scale: float | None = None, *, ws: torch.Tensor | None = None):
+    """One decoding step of attention over the visual tokens of unit pairs,
+    read straight from the K and V records (decoding fused into attention).
+
+    k_records, v_records: uint8 (P, record_bytes) coded with geom; q: float32
+    (P, q_heads, head_dim).  Returns (out, lse): out float32 (P, q_heads,
+    head_dim), the softmax-weighted sum of the decoded V over the S*H*W
+    tokens; lse float32 (P, q_heads), the log-sum-exp of the scaled scores.
+    """
+    P, qh, d = q.shape
+    if d != geom.head_dim or k_records.shape[0] != P or v_records.shape[0] != P:
+        raise ValueError("q must be (pairs, q_heads, head_dim) with one K and V record per pair")
+    if q.dtype != torch.float32 or not q.is_contiguous():
+        raise TypeError("q must be contiguous float32")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    p = geom.params()
+    out = torch.empty_like(q)
+    lse = torch.empty((P, qh), dtype=torch.float32, device=q.device)
+    if ws is None:
+        n = _lib.tact_attend_workspace_bytes(ctypes.byref(p), P, qh)
+        if n == 0:
+            _check(_lib.tact_attend(ctypes.byref(p), P, qh, None, None, None, 0.0, None, None,
+                                    None, 0, None), "tact_attend")
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+    _check(_lib.tact_attend(ctypes.byref(p), P, qh, _ptr(k_records), _ptr(v_records), _ptr(q),
+                            float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream()),
+           "tact_attend")
+    return out, lse
 
 
 def codebook(bits: int):

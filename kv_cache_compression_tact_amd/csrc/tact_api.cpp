@@ -2,6 +2,7 @@
 // workspace layout, chunking of large batches, launch sequencing and status
 // reporting.  All compute runs in the kernels of tact_kernels.hip; this file
 // never touches cache data.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -287,6 +288,65 @@ void decompress_chunk(const Geometry& g, int64_t cn, const uint8_t* recs, void* 
 }  // namespace
 }  // namespace tact
 
+// ---- decoding fused into attention ---------------------------------------
+namespace tact {
+namespace {
+
+constexpr int kMaxAttendRep = 16;
+constexpr int64_t kMaxAttendField = 40000;   // S*H*W fp32 held in LDS (160 KB)
+
+struct AttendWs {
+  float* tab;
+  float* tabT;
+  uint32_t* kpoff;
+  uint32_t* vpoff;
+  float* qrot;
+  float* field;
+  float* partial;
+};
+
+int64_t attend_ws_bytes(const Geometry& g, int64_t n_pairs, int q_heads, AttendWs* w,
+                        void* base) {
+  uint8_t* b = static_cast<uint8_t*>(base);
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    uint8_t* ptr = b ? b + off : nullptr;
+    off += align256(bytes);
+    return ptr;
+  };
+  const int64_t shw = static_cast<int64_t>(g.S) * g.H * g.W;
+  const int rep = q_heads / g.kv_heads;
+  AttendWs x;
+  x.tab = reinterpret_cast<float*>(take(4 * kDctTableFloats));
+  x.tabT = reinterpret_cast<float*>(take(4 * kDctTableFloats));
+  x.kpoff = reinterpret_cast<uint32_t*>(take(4 * n_pairs * g.n_bins));
+  x.vpoff = reinterpret_cast<uint32_t*>(take(4 * n_pairs * g.n_bins));
+  x.qrot = reinterpret_cast<float*>(take(4 * n_pairs * q_heads * g.head_dim));
+  x.field = reinterpret_cast<float*>(take(4 * n_pairs * q_heads * shw));
+  x.partial = reinterpret_cast<float*>(
+      take(4 * n_pairs * g.kv_heads * attend_chunks(g) * rep * g.head_dim));
+  if (w) *w = x;
+  return off;
+}
+
+tact_status check_attend(const Geometry& g, int64_t n_pairs, int32_t q_heads) {
+  if (n_pairs < 0 || n_pairs > 65535)
+    return fail(TACT_ERR_INVALID_ARGUMENT, "n_pairs=%lld: must be in 0..65535", (long long)n_pairs);
+  if (q_heads < g.kv_heads || q_heads % g.kv_heads != 0)
+    return fail(TACT_ERR_UNSUPPORTED, "q_heads=%d: must be a multiple of kv_heads=%d", q_heads,
+                g.kv_heads);
+  if (q_heads / g.kv_heads > kMaxAttendRep)
+    return fail(TACT_ERR_UNSUPPORTED, "%d query heads per kv head: at most %d",
+                q_heads / g.kv_heads, kMaxAttendRep);
+  if (static_cast<int64_t>(g.S) * g.H * g.W > kMaxAttendField)
+    return fail(TACT_ERR_UNSUPPORTED, "S*H*W=%lld: at most %lld for attention",
+                static_cast<long long>(g.S) * g.H * g.W, (long long)kMaxAttendField);
+  return TACT_OK;
+}
+
+}  // namespace
+}  // namespace tact
+
 using namespace tact;
 
 extern "C" {
@@ -401,6 +461,58 @@ tact_status tact_roundtrip(const tact_params* p, int64_t n_units, const void* kv
                      out_unit_stride, w, stream);
   }
   return after_launch("tact_roundtrip");
+}
+
+size_t tact_attend_workspace_bytes(const tact_params* p, int64_t n_pairs, int32_t q_heads) {
+  Geometry g;
+  if (make_geometry(p, &g) != TACT_OK || check_attend(g, n_pairs, q_heads) != TACT_OK) return 0;
+  return static_cast<size_t>(attend_ws_bytes(g, n_pairs, q_heads, nullptr, nullptr));
+}
+
+tact_status tact_attend(const tact_params* p, int64_t n_pairs, int32_t q_heads,
+                        const void* k_records, const void* v_records, const float* q,
+                        float scale, float* out, float* lse, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  Geometry g;
+  tact_status st;
+  if ((st = make_geometry(p, &g)) != TACT_OK) return st;
+  if ((st = check_attend(g, n_pairs, q_heads)) != TACT_OK) return st;
+  if (n_pairs == 0) return ok();
+  if ((st = check_buffer(k_records, "k_records", 256)) != TACT_OK) return st;
+  if ((st = check_buffer(v_records, "v_records", 256)) != TACT_OK) return st;
+  if ((st = check_buffer(q, "q", 4)) != TACT_OK) return st;
+  if ((st = check_buffer(out, "out", 4)) != TACT_OK) return st;
+  if ((st = check_buffer(lse, "lse", 4)) != TACT_OK) return st;
+  if (!std::isfinite(scale)) return fail(TACT_ERR_INVALID_ARGUMENT, "scale is not finite");
+  const int64_t need = attend_ws_bytes(g, n_pairs, q_heads, nullptr, nullptr);
+  if (!workspace)
+    return fail(TACT_ERR_WORKSPACE, "workspace is NULL (%lld bytes needed)", (long long)need);
+  if (!aligned(workspace, 256)) return fail(TACT_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  if (static_cast<int64_t>(workspace_bytes) < need)
+    return fail(TACT_ERR_WORKSPACE, "workspace of %zu bytes, %lld needed", workspace_bytes,
+                (long long)need);
+  {
+    // out and lse may not overlap q or each other
+    const uint8_t* a0 = reinterpret_cast<const uint8_t*>(q);
+    const uint8_t* b0 = reinterpret_cast<const uint8_t*>(out);
+    const uint8_t* c0 = reinterpret_cast<const uint8_t*>(lse);
+    const int64_t nq = 4 * n_pairs * q_heads * g.head_dim, nl = 4 * n_pairs * q_heads;
+    auto over = [](const uint8_t* x, int64_t nx, const uint8_t* y, int64_t ny) {
+      return x < y + ny && y < x + nx;
+    };
+    if (over(a0, nq, b0, nq) || over(a0, nq, c0, nl) || over(b0, nq, c0, nl))
+      return fail(TACT_ERR_INVALID_ARGUMENT, "q, out and lse overlap");
+  }
+  AttendWs w;
+  attend_ws_bytes(g, n_pairs, q_heads, &w, workspace);
+  const RecordView kv = view(g, const_cast<void*>(k_records));
+  const RecordView vv = view(g, const_cast<void*>(v_records));
+  launch_dct_tables(g, w.tab, stream);
+  launch_plane_offsets(g, n_pairs, kv, w.kpoff, stream);
+  launch_plane_offsets(g, n_pairs, vv, w.vpoff, stream);
+  launch_attend(g, n_pairs, q_heads, kv, vv, w.kpoff, w.vpoff, q, scale, w.qrot, w.field,
+                w.partial, out, lse, w.tab, w.tabT, stream);
+  return after_launch("tact_attend");
 }
 
 const char* tact_status_string(tact_status s) {

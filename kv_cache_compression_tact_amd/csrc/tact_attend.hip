@@ -1,0 +1,390 @@
+// Decoding fused into attention (page "TACT-KV: Tri-Axis Cosine Transform
+// for Compressing Volumetric KV Caches in Medical VLMs", "Methodology in Plain
+// English", the decoding paragraph): one decoding query per query head
+// attends over the visual tokens of a unit pair (the K and the V record of one
+// layer and sequence) without reconstructing K or V.
+//
+// The inverse 3-D DCT is linear and orthonormal.  With c_f the decoded
+// (unrotated) coefficient vector of frequency bin f of a head and B the
+// inverse transform, token t holds k_t = sum_f B[t, f] c_f, so
+//   scores:  q . k_t = IDCT3(s)[t],   s_f = q . c_f = (R q) . c'_f,
+//   output:  sum_t p_t v_t = sum_f DCT3(p)[f] c_f = R^T sum_f DCT3(p)[f] c'_f,
+// where c'_f = g_f * level(code) is the decoded vector in the rotated frame
+// (R is the quantizer's rotation).  Only coded bins contribute.  Per unit
+// pair, kv head and query head the kernels compute
+//   k_att_qrot   q' = scale * R q;
+//   k_att_proj   s_f = g_f * sum_j level_j * q'_j over the K record's bins
+//                (lane = bin, the codes read straight from the bit planes);
+//   k_att_field  scores = IDCT3(s) in LDS, the softmax, lse, P = DCT3(p);
+//   k_att_out    partial sums of P_f * level * g over the V record's bins
+//                (lane = channel), per chunk of bins;
+//   k_att_final  the sum over chunks and R^T, into the output.
+// The field of one query head (S * H * W fp32) lives in LDS, so S * H * W is
+// capped (the host checks it).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tact_internal.h"
+
+namespace tact {
+
+#include "codebook_device.h"
+#include "tact_rotation.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kMaxRep = 16;       // query heads per kv head
+constexpr int kChunk = 256;       // bins per wave in k_att_out
+constexpr int kFieldThreads = 512;
+
+struct AttArgs {
+  RecordView krec, vrec;
+  const uint32_t* kpoff;          // first plane of each bin, [pair][bin]
+  const uint32_t* vpoff;
+  const float* q;                 // [pair][q_heads][head_dim]
+  float scale;
+  float* qrot;                    // [pair][q_heads][head_dim]
+  float* field;                   // [pair][q_heads][S*H*W]
+  float* partial;                 // [pair][kv_heads][chunk][rep][head_dim]
+  float* out;                     // [pair][q_heads][head_dim]
+  float* lse;                     // [pair][q_heads]
+  const float* tab;               // DCT-II matrices [3][64][64]
+  float* tabT;                    // their transposes
+  int S, H, W, kv_heads, head_dim, q_heads, rep;
+  int rotate, axes, max_bits;
+  int64_t n_bins, total_bits;
+  int shw, n_chunks;
+};
+
+// q' = scale * R q (R per 64-channel block) or scale * q
+__global__ void k_att_qrot(AttArgs a) {
+  const int64_t row = static_cast<int64_t>(blockIdx.y) * a.q_heads + blockIdx.x;
+  const float* q = a.q + row * a.head_dim;
+  for (int i = threadIdx.x; i < a.head_dim; i += blockDim.x) {
+    float v = q[i];
+    if (a.rotate) {
+      const int b0 = i & ~63;
+      v = 0.f;
+      for (int j = 0; j < 64; ++j) v = fmaf(hadamard64(i & 63, j) * rotation_sign(j), q[b0 + j], v);
+      v *= 0.125f;
+    }
+    a.qrot[row * a.head_dim + i] = a.scale * v;
+  }
+}
+
+// Bin side info of a record, validated: bits 0 for a bin whose planes would
+// fall outside the record.
+__device__ __forceinline__ void bin_side(const RecordView& rv, const uint32_t* poff, int64_t pair,
+                                         int64_t bin, const AttArgs& a, int& b, int64_t& p0, float& g) {
+  const uint8_t* r = rv.base + pair * rv.stride;
+  b = r[rv.off_bits + bin];
+  p0 = poff[pair * a.n_bins + bin];
+  g = reinterpret_cast<const float*>(r + rv.off_gains)[bin];
+  if (b > a.max_bits || p0 + b > a.total_bits) b = 0;
+}
+
+// ---- projections: lane = bin f of kv head h --------------------------------
+template <int WPP>
+__global__ __launch_bounds__(256) void k_att_proj(AttArgs a) {
+  __shared__ float s_lv[TACT_CODEBOOK_LEVELS + 1];   // s_lv[0] = 0; b bits at (1 << b) - 1
+  for (int j = threadIdx.x; j <= TACT_CODEBOOK_LEVELS; j += blockDim.x)
+    s_lv[j] = j ? c_levels[j - 1] : 0.f;
+  __syncthreads();
+  const int h = blockIdx.y;
+  const int64_t pair = blockIdx.z;
+  const int f = blockIdx.x * blockDim.x + threadIdx.x;
+  const bool live = f < a.shw;
+  int b = 0;
+  int64_t p0 = 0;
+  float g = 0.f;
+  if (live) bin_side(a.krec, a.kpoff, pair, static_cast<int64_t>(f) * a.kv_heads + h, a, b, p0, g);
+  const uint64_t* words = reinterpret_cast<const uint64_t*>(
+      a.krec.base + pair * a.krec.stride + a.krec.off_codes);
+  // the query heads of this kv head, rotated and scaled: uniform operands
+  const float* qr = a.qrot + (pair * a.q_heads + static_cast<int64_t>(h) * a.rep) * (64 * WPP);
+  const int base = b > 0 ? (1 << b) - 1 : 0;
+  // the largest bit width in the wave bounds the planes read per channel
+  int bw = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (__ballot(k < b)) bw = k + 1;
+  float acc[kMaxRep];
+#pragma unroll
+  for (int r = 0; r < kMaxRep; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int hw = 0; hw < WPP; ++hw) {
+    uint64_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = k < b ? words[(p0 + k) * WPP + hw] : 0ull;
+    for (int jj = 0; jj < 64; ++jj) {
+      uint32_t code = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k < bw) code |= static_cast<uint32_t>((w[k] >> jj) & 1ull) << k;
+      const float val = s_lv[base + static_cast<int>(code)];
+      const float* qc = qr + 64 * hw + jj;
+#pragma unroll
+      for (int r = 0; r < kMaxRep; ++r)
+        if (r < a.rep) acc[r] = fmaf(val, qc[r * 64 * WPP], acc[r]);
+    }
+  }
+  if (!live) return;
+#pragma unroll
+  for (int r = 0; r < kMaxRep; ++r)
+    if (r < a.rep)
+      a.field[(pair * a.q_heads + static_cast<int64_t>(h) * a.rep + r) * a.shw + f] = g * acc[r];
+}
+
+// ---- the field of one query head: IDCT3, softmax, DCT3 ---------------------
+// One axis of the field in LDS: each thread transforms whole lines, the line
+// in registers (NP >= N, zero padded), y[n] = sum_k M[n][k] x[k] with M the
+// DCT-II matrix (forward) or its transpose (inverse), rows of 64 floats,
+// zero padded; the rows are uniform operands.
+template <int NP>
+__device__ void line_pass(float* fld, int n_lines, int N, int inner, const float* __restrict__ M) {
+  for (int l = threadIdx.x; l < n_lines; l += blockDim.x) {
+    // lines are (outer, inner) pairs with elements `inner` apart; the
+    // innermost axis (inner == 1) has contiguous lines
+    const int o = l / inner, in = l % inner;
+    float* p = fld + static_cast<int64_t>(o) * inner * N + in;
+    float x[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) x[k] = k < N ? p[k * inner] : 0.f;
+    for (int n = 0; n < N; ++n) {
+      const float* m = M + n * 64;
+      float v = 0.f;
+#pragma unroll
+      for (int k = 0; k < NP; ++k) v = fmaf(m[k], x[k], v);
+      p[n * inner] = v;
+    }
+  }
+}
+
+__device__ void axis_pass(float* fld, const AttArgs& a, int axis, const float* M) {
+  // field [S][H][W]; axis 0: lines over (h, w), elements H*W apart; axis 1:
+  // lines over (s, w), W apart; axis 2: lines over (s, h), contiguous
+  const int N = axis == 0 ? a.S : (axis == 1 ? a.H : a.W);
+  const int n_lines = a.shw / N;
+  const int inner = axis == 0 ? a.H * a.W : (axis == 1 ? a.W : 1);
+  M += axis * 4096;
+  if (N <= 16) line_pass<16>(fld, n_lines, N, inner, M);
+  else if (N <= 32) line_pass<32>(fld, n_lines, N, inner, M);
+  else line_pass<64>(fld, n_lines, N, inner, M);
+}
+
+// the transposed DCT matrices, tabT[a][n][k] = tab[a][k][n]
+__global__ void k_att_transpose(AttArgs a) {
+  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < 3 * 4096; e += gridDim.x * blockDim.x) {
+    const int ax = e / 4096, k = (e / 64) % 64, n = e % 64;
+    a.tabT[ax * 4096 + n * 64 + k] = a.tab[e];
+  }
+}
+
+__device__ float block_reduce(float v, bool is_max, float* red) {
+  // wave reduction, then across the waves of the block through LDS
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float u = __shfl_xor(v, o, kWave);
+    v = is_max ? fmaxf(v, u) : v + u;
+  }
+  const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+  __syncthreads();
+  if (lane == 0) red[wv] = v;
+  __syncthreads();
+  v = red[0];
+  for (int j = 1; j < static_cast<int>(blockDim.x / kWave); ++j) v = is_max ? fmaxf(v, red[j]) : v + red[j];
+  return v;
+}
+
+__global__ __launch_bounds__(kFieldThreads) void k_att_field(AttArgs a) {
+  extern __shared__ float4 fld_v4[];
+  float* fld = reinterpret_cast<float*>(fld_v4);
+  __shared__ float red[kFieldThreads / kWave];
+  const int64_t row = static_cast<int64_t>(blockIdx.y) * a.q_heads + blockIdx.x;
+  float* gf = a.field + row * a.shw;
+  for (int e = threadIdx.x; e < a.shw; e += blockDim.x) fld[e] = gf[e];
+  __syncthreads();
+  for (int axis = 2; axis >= 0; --axis)
+    if (a.axes & (1 << axis)) {
+      axis_pass(fld, a, axis, a.tabT);
+      __syncthreads();
+    }
+  float m = -INFINITY;
+  for (int e = threadIdx.x; e < a.shw; e += blockDim.x) m = fmaxf(m, fld[e]);
+  m = block_reduce(m, true, red);
+  float l = 0.f;
+  for (int e = threadIdx.x; e < a.shw; e += blockDim.x) l += expf(fld[e] - m);
+  l = block_reduce(l, false, red);
+  const float lse = m + logf(l);
+  for (int e = threadIdx.x; e < a.shw; e += blockDim.x) fld[e] = expf(fld[e] - lse);
+  __syncthreads();
+  for (int axis = 0; axis < 3; ++axis)
+    if (a.axes & (1 << axis)) {
+      axis_pass(fld, a, axis, a.tab);
+      __syncthreads();
+    }
+  for (int e = threadIdx.x; e < a.shw; e += blockDim.x) gf[e] = fld[e];
+  if (threadIdx.x == 0) a.lse[row] = lse;
+}
+
+// ---- output partial sums: lane = channel, one wave per chunk of bins ------
+template <int WPP>
+__global__ __launch_bounds__(kWave) void k_att_out(AttArgs a) {
+  __shared__ float s_lv[TACT_CODEBOOK_LEVELS + 1];
+  for (int j = threadIdx.x; j <= TACT_CODEBOOK_LEVELS; j += blockDim.x)
+    s_lv[j] = j ? c_levels[j - 1] : 0.f;
+  __syncthreads();
+  const int lane = threadIdx.x;
+  const int chunk = blockIdx.x, h = blockIdx.y;
+  const int64_t pair = blockIdx.z;
+  const uint64_t* words = reinterpret_cast<const uint64_t*>(
+      a.vrec.base + pair * a.vrec.stride + a.vrec.off_codes);
+  const float* P = a.field + (pair * a.q_heads + static_cast<int64_t>(h) * a.rep) * a.shw;
+  float acc[kMaxRep][WPP];
+#pragma unroll
+  for (int r = 0; r < kMaxRep; ++r)
+#pragma unroll
+    for (int hw = 0; hw < WPP; ++hw) acc[r][hw] = 0.f;
+  const int f_end = min(a.shw, (chunk + 1) * kChunk);
+  for (int f0 = chunk * kChunk; f0 < f_end; f0 += kWave) {
+    // side info and probabilities of bins f0 + lane
+    const int f = f0 + lane;
+    int bj = 0;
+    int64_t pj = 0;
+    float gj = 0.f;
+    float pr[kMaxRep];
+#pragma unroll
+    for (int r = 0; r < kMaxRep; ++r) pr[r] = 0.f;
+    if (f < f_end) {
+      bin_side(a.vrec, a.vpoff, pair, static_cast<int64_t>(f) * a.kv_heads + h, a, bj, pj, gj);
+#pragma unroll
+      for (int r = 0; r < kMaxRep; ++r)
+        if (r < a.rep) pr[r] = P[static_cast<int64_t>(r) * a.shw + f];
+    }
+    uint64_t todo = __ballot(bj > 0);
+    while (todo) {
+      const int j = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const int b = __builtin_amdgcn_readlane(bj, j);
+      const int64_t p0 = static_cast<int64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(pj), j)));
+      const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gj), j));
+      const int base = (1 << b) - 1;
+#pragma unroll
+      for (int hw = 0; hw < WPP; ++hw) {
+        uint32_t code = 0;
+        for (int k = 0; k < b; ++k) {
+          const uint64_t w = words[(p0 + k) * WPP + hw];
+          code |= static_cast<uint32_t>((w >> lane) & 1ull) << k;
+        }
+        const float val = g * s_lv[base + static_cast<int>(code)];
+#pragma unroll
+        for (int r = 0; r < kMaxRep; ++r)
+          if (r < a.rep)
+            acc[r][hw] = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[r]), j)),
+                              val, acc[r][hw]);
+      }
+    }
+  }
+  float* dst = a.partial + ((pair * a.kv_heads + h) * a.n_chunks + chunk) * a.rep * (64 * WPP);
+#pragma unroll
+  for (int r = 0; r < kMaxRep; ++r)
+    if (r < a.rep)
+#pragma unroll
+      for (int hw = 0; hw < WPP; ++hw) dst[r * 64 * WPP + 64 * hw + lane] = acc[r][hw];
+}
+
+// ---- sum over chunks, undo the rotation ----------------------------------
+__global__ void k_att_final(AttArgs a) {
+  extern __shared__ float s_o[];
+  const int qh = blockIdx.x;
+  const int64_t pair = blockIdx.y;
+  const int h = qh / a.rep, r = qh % a.rep;
+  const int d = a.head_dim;
+  const float* src = a.partial + (pair * a.kv_heads + h) * a.n_chunks * a.rep * d;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    float v = 0.f;
+    for (int c = 0; c < a.n_chunks; ++c) v += src[(static_cast<int64_t>(c) * a.rep + r) * d + i];
+    s_o[i] = v;
+  }
+  __syncthreads();
+  float* o = a.out + (pair * a.q_heads + qh) * d;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    float v = s_o[i];
+    if (a.rotate) {
+      // (R^T v)_j = s_j / 8 * sum_i H[j][i] v_i within the 64-block
+      const int b0 = i & ~63;
+      v = 0.f;
+      for (int k = 0; k < 64; ++k) v = fmaf(hadamard64(i & 63, k), s_o[b0 + k], v);
+      v *= 0.125f * rotation_sign(i & 63);
+    }
+    o[i] = v;
+  }
+}
+
+}  // namespace
+
+int attend_chunks(const Geometry& g) {
+  const int shw = g.S * g.H * g.W;
+  return (shw + kChunk - 1) / kChunk;
+}
+
+void launch_attend(const Geometry& g, int64_t n_pairs, int q_heads, RecordView krec,
+                   RecordView vrec, const uint32_t* kpoff, const uint32_t* vpoff, const float* q,
+                   float scale, float* qrot, float* field, float* partial, float* out, float* lse,
+                   const float* tab, float* tabT, hipStream_t s) {
+  AttArgs a;
+  a.krec = krec;
+  a.vrec = vrec;
+  a.kpoff = kpoff;
+  a.vpoff = vpoff;
+  a.q = q;
+  a.scale = scale;
+  a.qrot = qrot;
+  a.field = field;
+  a.partial = partial;
+  a.out = out;
+  a.lse = lse;
+  a.tab = tab;
+  a.tabT = tabT;
+  a.S = g.S;
+  a.H = g.H;
+  a.W = g.W;
+  a.kv_heads = g.kv_heads;
+  a.head_dim = g.head_dim;
+  a.q_heads = q_heads;
+  a.rep = q_heads / g.kv_heads;
+  a.rotate = g.rotation == TACT_ROTATION_HADAMARD;
+  a.axes = g.axes;
+  a.max_bits = g.max_bits;
+  a.n_bins = g.n_bins;
+  a.total_bits = g.total_bits;
+  a.shw = g.S * g.H * g.W;
+  a.n_chunks = attend_chunks(g);
+  const unsigned np = static_cast<unsigned>(n_pairs);
+  hipLaunchKernelGGL(k_att_transpose, dim3(12), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_att_qrot, dim3(q_heads, np), dim3(g.head_dim), 0, s, a);
+  const dim3 gp((a.shw + 255) / 256, g.kv_heads, np), go(a.n_chunks, g.kv_heads, np);
+  if (g.head_dim == 64) {
+    hipLaunchKernelGGL(k_att_proj<1>, gp, dim3(256), 0, s, a);
+  } else if (g.head_dim == 128) {
+    hipLaunchKernelGGL(k_att_proj<2>, gp, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(k_att_proj<4>, gp, dim3(256), 0, s, a);
+  }
+  const size_t lds = static_cast<size_t>(a.shw) * sizeof(float);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_att_field),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  hipLaunchKernelGGL(k_att_field, dim3(q_heads, np), dim3(kFieldThreads), lds, s, a);
+  if (g.head_dim == 64) {
+    hipLaunchKernelGGL(k_att_out<1>, go, dim3(kWave), 0, s, a);
+  } else if (g.head_dim == 128) {
+    hipLaunchKernelGGL(k_att_out<2>, go, dim3(kWave), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(k_att_out<4>, go, dim3(kWave), 0, s, a);
+  }
+  hipLaunchKernelGGL(k_att_final, dim3(q_heads, np), dim3(g.head_dim),
+                     g.head_dim * sizeof(float), s, a);
+}
+
+}  // namespace tact

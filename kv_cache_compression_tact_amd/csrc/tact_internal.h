@@ -116,6 +116,18 @@ void launch_quant(const Geometry& g, int64_t n_units, const float* coef, int64_t
 void launch_plane_offsets(const Geometry& g, int64_t n_units, RecordView rec,
                           uint32_t* plane_off, hipStream_t stream);
 
+// Decoding fused into attention (tact_attend.hip): per unit pair the
+// projections, the field transforms and softmax, the output partial sums per
+// chunk of bins, and the final sum and inverse rotation.  Workspace: tab
+// (DCT tables, filled by launch_dct_tables), tabT (3 x 64 x 64 fp32), the
+// per-bin first planes of both record arrays, qrot [pairs][q_heads][d],
+// field [pairs][q_heads][S*H*W], partial [pairs][kv_heads][chunks][rep][d].
+int attend_chunks(const Geometry& g);
+void launch_attend(const Geometry& g, int64_t n_pairs, int q_heads, RecordView krec,
+                   RecordView vrec, const uint32_t* kpoff, const uint32_t* vpoff, const float* q,
+                   float scale, float* qrot, float* field, float* partial, float* out, float* lse,
+                   const float* tab, float* tabT, hipStream_t stream);
+
 // Host copy of the fp32 codebooks.
 extern const float kHostLevels[];
 extern const float kHostThresholds[];

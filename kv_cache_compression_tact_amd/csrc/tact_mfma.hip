@@ -105,25 +105,12 @@ __device__ __forceinline__ uint16_t bf16_rne_bits(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// The shared rotation of the quantizer (stage 4): R = H_64 diag(s) / 8 on
-// every 64-channel block of a bin, H_64 Sylvester's Hadamard matrix
-// (H[j][j'] = (-1)^popcount(j & j')), s_j the top bit of SplitMix64(seed+j)
-// mapped to +1 / -1.  In the fragments the 6 channel bits split into 4 lane
-// bits (lanes of a 16-lane row) and 2 register bits (4 values per lane).
+// The shared rotation of the quantizer (stage 4), R = H_64 diag(s) / 8 on
+// every 64-channel block of a bin (tact_rotation.h).  In the fragments the 6
+// channel bits split into 4 lane bits (lanes of a 16-lane row) and 2
+// register bits (4 values per lane).
 // ---------------------------------------------------------------------------
-constexpr uint64_t kRotationSeed = 0x54414354ull;
-
-// SplitMix64 (Steele, Lea and Flood, OOPSLA 2014), one output per counter.
-__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
-  uint64_t z = x + 0x9E3779B97F4A7C15ull;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  return z ^ (z >> 31);
-}
-
-__device__ __forceinline__ float rotation_sign(int j) {
-  return (splitmix64(kRotationSeed + static_cast<uint64_t>(j)) >> 63) ? -1.0f : 1.0f;
-}
+#include "tact_rotation.h"
 
 // Partner values across the lanes of a 16-lane row: lane ^ 1, ^ 2 (quad
 // permutes), ^ 4 (swizzle, bit mask mode), ^ 8 (row rotate by 8).

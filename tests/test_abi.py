@@ -148,3 +148,37 @@ def test_valid_call_without_device_reports_hip_error():
     st = lib().tact_compress(ctypes.byref(p), 1, fake, 32768, fake, fake, ws, None)
     assert st == 4
     assert b"tact_compress" in lib().tact_last_error()
+
+
+def test_attend_validation():
+    L = lib()
+    p = _params()                      # 4x8x8, 2 kv heads of 64
+    fake = ctypes.c_void_p(1 << 20)
+    ws = L.tact_attend_workspace_bytes(ctypes.byref(p), 3, 4)
+    assert ws > 0
+    # q_heads: a multiple of kv_heads, at most 16 per kv head
+    assert L.tact_attend_workspace_bytes(ctypes.byref(p), 3, 3) == 0
+    assert L.tact_attend_workspace_bytes(ctypes.byref(p), 3, 34) == 0
+    assert L.tact_attend(ctypes.byref(p), 3, 3, fake, fake, fake, 1.0, fake, fake, fake, ws,
+                         None) == 2
+    assert L.tact_attend(ctypes.byref(p), 3, 34, fake, fake, fake, 1.0, fake, fake, fake, ws,
+                         None) == 2
+    # the field of S*H*W tokens must fit in LDS
+    big = _params(S=64, H=32, W=32)
+    assert L.tact_attend_workspace_bytes(ctypes.byref(big), 1, 2) == 0
+    assert b"S*H*W" in (L.tact_attend(ctypes.byref(big), 1, 2, fake, fake, fake, 1.0, fake,
+                                      fake, fake, 1 << 30, None) == 2 and L.tact_last_error())
+    # pointers, alignment, scale, workspace, overlap, pair count
+    args = [fake, fake, fake, 1.0, ctypes.c_void_p((1 << 20) + 65536),
+            ctypes.c_void_p((1 << 20) + 131072), fake, ws]
+    assert L.tact_attend(ctypes.byref(p), 3, 4, None, *args[1:], None) == 1
+    assert L.tact_attend(ctypes.byref(p), 3, 4, ctypes.c_void_p((1 << 20) + 16), *args[1:],
+                         None) == 1
+    assert L.tact_attend(ctypes.byref(p), 3, 4, *args[:3], float("nan"), *args[4:], None) == 1
+    assert L.tact_attend(ctypes.byref(p), 3, 4, *args[:6], None, ws, None) == 3
+    assert L.tact_attend(ctypes.byref(p), 3, 4, *args[:7], ws - 1, None) == 3
+    assert L.tact_attend(ctypes.byref(p), 3, 4, *args[:3], 1.0, fake, args[5], fake, ws,
+                         None) == 1     # out overlaps q
+    assert L.tact_attend(ctypes.byref(p), -1, 4, *args, None) == 1
+    assert L.tact_attend(ctypes.byref(p), 0, 4, None, None, None, 1.0, None, None, None, 0,
+                         None) == 0
