@@ -41,6 +41,11 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=2,
                     help="units in the oracle's timed sample")
+    ap.add_argument("--attend", action="store_true",
+                    help="time decoding fused into attention (tact_attend) over every "
+                         "layer and sequence of the workload instead of the codec")
+    ap.add_argument("--q-per-kv", type=int, default=4,
+                    help="query heads per kv head for --attend")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times): the "
                          "reference for scaling the HBM byte counters of a profile")
@@ -119,6 +124,67 @@ def measured_traffic(workload: str):
     return rec
 
 
+def bench_attend(args, tact, wl, budget, g, x):
+    """One decoding step of attention over the visual KV of every layer and
+    sequence of the workload (one query per query head), read straight from
+    the K and V records by tact_attend.  For reference the same records are
+    decompressed to the bf16 cache with tact_decompress, which a path that
+    materializes the cache must do before its attention reads it."""
+    dev = x.device
+    U = wl.n_units
+    pairs = U // 2
+    rec = tact.compress(x, budget, wl.max_bits)
+    krec, vrec = rec[0::2].contiguous(), rec[1::2].contiguous()
+    del x
+    qh = args.q_per_kv * wl.kv_heads
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    q = torch.randn((pairs, qh, wl.head_dim), generator=gen, device=dev, dtype=torch.float32)
+    ws = tact.attend_workspace(g, pairs, qh, dev)
+    out_cache = torch.empty((U,) + g.unit_shape, dtype=g.dtype, device=dev)
+    dws = tact.workspace(g, U, dev)
+    stream = torch.cuda.current_stream()
+    scale = 1.0 / wl.head_dim ** 0.5
+
+    def timed(fn, n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    att = lambda: tact.attend(krec, vrec, g, q, scale, ws=ws)
+    dec = lambda: tact.decompress(rec, g, out=out_cache, ws=dws)
+    for _ in range(args.warmup):
+        att()
+        dec()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_att = timed(att, args.steps)
+    elapsed = time.perf_counter() - t0
+    t_dec = timed(dec, args.steps)
+    ms_att = sum(t_att) / len(t_att)
+    ms_dec = sum(t_dec) / len(t_dec)
+    read = 2 * pairs * g.record_bytes()
+    line = {
+        "metric": "decode-attention step over the coded visual KV (tact_attend), ms",
+        "value": round(ms_att, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "pairs": pairs, "q_heads": qh,
+                   "unit_shape": list(wl.unit_shape), "budget_bits": budget},
+        "record_bytes_read": read,
+        "record_read_GBs": round(read / (ms_att * 1e-3) / 1e9, 2),
+        "ms_decompress_same_records": round(ms_dec, 4),
+        "speedup_vs_decompress": round(ms_dec / ms_att, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -143,6 +209,9 @@ def main():
     g = tact.Geometry(*wl.unit_shape, budget_bits=budget, max_bits=wl.max_bits,
                       dtype=wl.dtype)
     U = wl.n_units
+    if args.attend:
+        bench_attend(args, tact, wl, budget, g, x)
+        return
     rec = torch.empty((U, g.record_bytes()), dtype=torch.uint8, device=dev)
     out = torch.empty_like(x)
     ws = tact.workspace(g, U, dev)

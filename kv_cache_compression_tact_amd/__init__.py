@@ -238,6 +238,15 @@ def roundtrip(kv: torch.Tensor, budget_bits: int, max_bits: int = 8, *,
     return out, records
 
 
+def attend_workspace(geom: Geometry, n_pairs: int, q_heads: int, device=None) -> torch.Tensor:
+    p = geom.params()
+    n = _lib.tact_attend_workspace_bytes(ctypes.byref(p), n_pairs, q_heads)
+    if n == 0:
+        _check(_lib.tact_attend(ctypes.byref(p), n_pairs, q_heads, None, None, None, 0.0, None,
+                                None, None, 0, None), "tact_attend_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
 def attend(k_records: torch.Tensor, v_records: torch.Tensor, geom: Geometry,
            q: torch.Tensor, scale: float | None = None, *, ws: torch.Tensor | None = None):
     """One decoding step of attention over the visual tokens of unit pairs,
@@ -259,11 +268,7 @@ def attend(k_records: torch.Tensor, v_records: torch.Tensor, geom: Geometry,
     out = torch.empty_like(q)
     lse = torch.empty((P, qh), dtype=torch.float32, device=q.device)
     if ws is None:
-        n = _lib.tact_attend_workspace_bytes(ctypes.byref(p), P, qh)
-        if n == 0:
-            _check(_lib.tact_attend(ctypes.byref(p), P, qh, None, None, None, 0.0, None, None,
-                                    None, 0, None), "tact_attend")
-        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+        ws = attend_workspace(geom, P, qh, q.device)
     _check(_lib.tact_attend(ctypes.byref(p), P, qh, _ptr(k_records), _ptr(v_records), _ptr(q),
                             float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream()),
            "tact_attend")
