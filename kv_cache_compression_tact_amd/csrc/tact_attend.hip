@@ -85,14 +85,24 @@ __device__ __forceinline__ void bin_side(const RecordView& rv, const uint32_t* p
 }
 
 // ---- projections: lane = bin f of kv head h --------------------------------
+// The rotated, scaled queries of the kv head are staged in LDS transposed
+// (channel-major, the query heads of a channel adjacent), so one broadcast
+// read serves every lane.
 template <int WPP>
 __global__ __launch_bounds__(256) void k_att_proj(AttArgs a) {
+  constexpr int D = 64 * WPP;
   __shared__ float s_lv[TACT_CODEBOOK_LEVELS + 1];   // s_lv[0] = 0; b bits at (1 << b) - 1
-  for (int j = threadIdx.x; j <= TACT_CODEBOOK_LEVELS; j += blockDim.x)
-    s_lv[j] = j ? c_levels[j - 1] : 0.f;
-  __syncthreads();
+  __shared__ __attribute__((aligned(16))) float s_qt[D * kMaxRep];   // [channel][r]
   const int h = blockIdx.y;
   const int64_t pair = blockIdx.z;
+  for (int j = threadIdx.x; j <= TACT_CODEBOOK_LEVELS; j += blockDim.x)
+    s_lv[j] = j ? c_levels[j - 1] : 0.f;
+  const float* qr = a.qrot + (pair * a.q_heads + static_cast<int64_t>(h) * a.rep) * D;
+  for (int e = threadIdx.x; e < D * kMaxRep; e += blockDim.x) {
+    const int c = e / kMaxRep, r = e % kMaxRep;
+    s_qt[e] = r < a.rep ? qr[r * D + c] : 0.f;
+  }
+  __syncthreads();
   const int f = blockIdx.x * blockDim.x + threadIdx.x;
   const bool live = f < a.shw;
   int b = 0;
@@ -101,32 +111,43 @@ __global__ __launch_bounds__(256) void k_att_proj(AttArgs a) {
   if (live) bin_side(a.krec, a.kpoff, pair, static_cast<int64_t>(f) * a.kv_heads + h, a, b, p0, g);
   const uint64_t* words = reinterpret_cast<const uint64_t*>(
       a.krec.base + pair * a.krec.stride + a.krec.off_codes);
-  // the query heads of this kv head, rotated and scaled: uniform operands
-  const float* qr = a.qrot + (pair * a.q_heads + static_cast<int64_t>(h) * a.rep) * (64 * WPP);
   const int base = b > 0 ? (1 << b) - 1 : 0;
   // the largest bit width in the wave bounds the planes read per channel
   int bw = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k)
     if (__ballot(k < b)) bw = k + 1;
+  // query heads in groups of 4 (one 128-bit LDS read per channel and group)
+  const int n4 = (a.rep + 3) / 4;
   float acc[kMaxRep];
 #pragma unroll
   for (int r = 0; r < kMaxRep; ++r) acc[r] = 0.f;
 #pragma unroll
   for (int hw = 0; hw < WPP; ++hw) {
-    uint64_t w[8];
+    uint32_t wl[8], wh[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) w[k] = k < b ? words[(p0 + k) * WPP + hw] : 0ull;
+    for (int k = 0; k < 8; ++k) {
+      const uint64_t w = k < b ? words[(p0 + k) * WPP + hw] : 0ull;
+      wl[k] = static_cast<uint32_t>(w);
+      wh[k] = static_cast<uint32_t>(w >> 32);
+    }
+#pragma unroll 8
     for (int jj = 0; jj < 64; ++jj) {
       uint32_t code = 0;
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (k < bw) code |= static_cast<uint32_t>((w[k] >> jj) & 1ull) << k;
+        if (k < bw) code |= __builtin_amdgcn_ubfe(jj < 32 ? wl[k] : wh[k], jj & 31, 1) << k;
       const float val = s_lv[base + static_cast<int>(code)];
-      const float* qc = qr + 64 * hw + jj;
+      const float4* qc = reinterpret_cast<const float4*>(s_qt + (64 * hw + jj) * kMaxRep);
 #pragma unroll
-      for (int r = 0; r < kMaxRep; ++r)
-        if (r < a.rep) acc[r] = fmaf(val, qc[r * 64 * WPP], acc[r]);
+      for (int r4 = 0; r4 < kMaxRep / 4; ++r4) {
+        if (r4 >= n4) break;
+        const float4 qv = qc[r4];
+        acc[4 * r4 + 0] = fmaf(val, qv.x, acc[4 * r4 + 0]);
+        acc[4 * r4 + 1] = fmaf(val, qv.y, acc[4 * r4 + 1]);
+        acc[4 * r4 + 2] = fmaf(val, qv.z, acc[4 * r4 + 2]);
+        acc[4 * r4 + 3] = fmaf(val, qv.w, acc[4 * r4 + 3]);
+      }
     }
   }
   if (!live) return;
@@ -229,9 +250,13 @@ __global__ __launch_bounds__(kFieldThreads) void k_att_field(AttArgs a) {
 }
 
 // ---- output partial sums: lane = channel, one wave per chunk of bins ------
+// Bins are taken 64 at a time: lane j loads bin j's side info, its query
+// heads' probabilities and its plane words (into LDS, 8 planes x WPP words
+// per bin), then the wave walks the coded bins with every operand on chip.
 template <int WPP>
 __global__ __launch_bounds__(kWave) void k_att_out(AttArgs a) {
   __shared__ float s_lv[TACT_CODEBOOK_LEVELS + 1];
+  __shared__ uint2 s_w[kWave][8 * WPP];        // [bin][plane * WPP + word] as (lo, hi)
   for (int j = threadIdx.x; j <= TACT_CODEBOOK_LEVELS; j += blockDim.x)
     s_lv[j] = j ? c_levels[j - 1] : 0.f;
   __syncthreads();
@@ -241,6 +266,8 @@ __global__ __launch_bounds__(kWave) void k_att_out(AttArgs a) {
   const uint64_t* words = reinterpret_cast<const uint64_t*>(
       a.vrec.base + pair * a.vrec.stride + a.vrec.off_codes);
   const float* P = a.field + (pair * a.q_heads + static_cast<int64_t>(h) * a.rep) * a.shw;
+  const int sh = lane & 31;
+  const bool hi = lane >= 32;
   float acc[kMaxRep][WPP];
 #pragma unroll
   for (int r = 0; r < kMaxRep; ++r)
@@ -248,7 +275,7 @@ __global__ __launch_bounds__(kWave) void k_att_out(AttArgs a) {
     for (int hw = 0; hw < WPP; ++hw) acc[r][hw] = 0.f;
   const int f_end = min(a.shw, (chunk + 1) * kChunk);
   for (int f0 = chunk * kChunk; f0 < f_end; f0 += kWave) {
-    // side info and probabilities of bins f0 + lane
+    // side info, probabilities and plane words of bins f0 + lane
     const int f = f0 + lane;
     int bj = 0;
     int64_t pj = 0;
@@ -262,20 +289,31 @@ __global__ __launch_bounds__(kWave) void k_att_out(AttArgs a) {
       for (int r = 0; r < kMaxRep; ++r)
         if (r < a.rep) pr[r] = P[static_cast<int64_t>(r) * a.shw + f];
     }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int hw = 0; hw < WPP; ++hw) {
+        const uint64_t w = k < bj ? words[(pj + k) * WPP + hw] : 0ull;
+        s_w[lane][k * WPP + hw] = uint2{static_cast<uint32_t>(w), static_cast<uint32_t>(w >> 32)};
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     uint64_t todo = __ballot(bj > 0);
     while (todo) {
       const int j = __builtin_ctzll(todo);
       todo &= todo - 1;
       const int b = __builtin_amdgcn_readlane(bj, j);
-      const int64_t p0 = static_cast<int64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(pj), j)));
       const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gj), j));
       const int base = (1 << b) - 1;
 #pragma unroll
       for (int hw = 0; hw < WPP; ++hw) {
         uint32_t code = 0;
-        for (int k = 0; k < b; ++k) {
-          const uint64_t w = words[(p0 + k) * WPP + hw];
-          code |= static_cast<uint32_t>((w >> lane) & 1ull) << k;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (k >= b) break;
+          const uint2 w = s_w[j][k * WPP + hw];
+          code |= __builtin_amdgcn_ubfe(hi ? w.y : w.x, sh, 1) << k;
         }
         const float val = g * s_lv[base + static_cast<int>(code)];
 #pragma unroll
@@ -285,6 +323,10 @@ __global__ __launch_bounds__(kWave) void k_att_out(AttArgs a) {
                               val, acc[r][hw]);
       }
     }
+    // every lane has read the words before the next group overwrites them
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   float* dst = a.partial + ((pair * a.kv_heads + h) * a.n_chunks + chunk) * a.rep * (64 * WPP);
 #pragma unroll
