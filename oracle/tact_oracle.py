@@ -45,13 +45,14 @@ import math
 from dataclasses import dataclass
 
 import numpy as np
-from scipy.special import erfc
+from scipy.special import erfc, ndtri
 
 __all__ = [
     "Params", "dct2_matrix", "dct3_forward", "dct3_inverse", "bin_variance",
     "total_bits", "waterfill_theta", "waterfill_rates", "round_bits",
     "greedy_correct", "allocate_bits", "allocate_bits_by_sorting", "allocate_uniform",
     "lloyd_max", "codebook_f32", "gains_f32", "quantize", "dequantize",
+    "QUANTIZERS", "uniform_levels", "nf_levels", "codebook", "gains_absmax_f32",
     "splitmix64", "rotation_signs", "rotate", "unrotate", "ROTATION_SEED",
     "record_layout", "pack_record", "unpack_record", "round_to_bf16",
     "bf16_bits", "compress", "decompress", "roundtrip", "mse",
@@ -385,9 +386,53 @@ def lloyd_max(bits: int):
     return _LM_CACHE[bits]
 
 
-def codebook_f32(bits: int):
-    """The Lloyd-Max table rounded to float32, as the kernel uses it."""
-    levels, thresholds, _ = lloyd_max(bits)
+# The scalar quantizers compared in [Findings/SQ]: the gain-shape Lloyd-Max
+# table of the method, a symmetric uniform quantizer and NormalFloat.
+QUANTIZERS = ("lloyd_max", "uniform", "nf")
+
+
+def uniform_levels(bits: int) -> np.ndarray:
+    """Symmetric uniform quantizer of [-1, 1] with 2^bits cells.
+
+    READING: [Findings/SQ] names the backend without its construction; the
+    plain one is 2^b equal cells tiling [-1, 1] with the level at each cell
+    centre (mid-rise: no level at 0, so 1 bit is +-1/2), the values scaled by
+    the bin's absolute maximum.
+    """
+    n = 2 ** bits
+    return (2.0 * np.arange(n) + 1.0 - n) / n
+
+
+def nf_levels(bits: int) -> np.ndarray:
+    """NormalFloat levels: standard normal quantiles at the centres of 2^b
+    equal-probability slices, (k + 1/2) / 2^b, normalized so that the
+    outermost levels are +-1.
+
+    READING: [Findings/SQ] names NormalFloat without its construction; this
+    is the symmetric form (equal-probability quantiles, absmax scaling).
+    """
+    n = 2 ** bits
+    q = ndtri((np.arange(n) + 0.5) / n)
+    return q / q[-1]
+
+
+def codebook(bits: int, kind: str = "lloyd_max"):
+    """(levels, thresholds) of a quantizer, ascending, float64; thresholds
+    are the midpoints of adjacent levels for every kind."""
+    if kind == "lloyd_max":
+        levels, thresholds, _ = lloyd_max(bits)
+        return levels, thresholds
+    if not 1 <= bits <= 8:
+        raise ValueError("bits must be in 1..8")
+    levels = uniform_levels(bits) if kind == "uniform" else nf_levels(bits)
+    if kind not in QUANTIZERS:
+        raise ValueError(f"unknown quantizer {kind}")
+    return levels, 0.5 * (levels[:-1] + levels[1:])
+
+
+def codebook_f32(bits: int, kind: str = "lloyd_max"):
+    """The table rounded to float32, as the kernel uses it."""
+    levels, thresholds = codebook(bits, kind)
     return levels.astype(np.float32), thresholds.astype(np.float32)
 
 
@@ -456,8 +501,19 @@ def gains_f32(var: np.ndarray) -> np.ndarray:
     return np.sqrt(np.asarray(var, dtype=np.float64)).astype(np.float32)
 
 
+def gains_absmax_f32(coef: np.ndarray, rotation: str = "none") -> np.ndarray:
+    """Per-bin gain of the uniform and NormalFloat quantizers: the largest
+    |value| of the bin vector (after the rotation when it is on), rounded to
+    fp32, so the scaled values lie in [-1, 1].  READING: both quantizers
+    scale by the absolute maximum, as those formats are defined."""
+    c = np.asarray(coef, dtype=np.float64)
+    if rotation == "hadamard":
+        c = rotate(c)
+    return np.max(np.abs(c), axis=-1).astype(np.float32)
+
+
 def quantize(coef: np.ndarray, gains: np.ndarray, bits: np.ndarray,
-             rotation: str = "none") -> np.ndarray:
+             rotation: str = "none", kind: str = "lloyd_max") -> np.ndarray:
     """Cell index of every coefficient at its bin's bit width [Method/4].
 
     Decided in float32 (the kernel's precision): r = 1/g (0 when g == 0),
@@ -481,13 +537,13 @@ def quantize(coef: np.ndarray, gains: np.ndarray, bits: np.ndarray,
         sel = b == nb
         if not sel.any():
             continue
-        _, thr = codebook_f32(nb)
+        _, thr = codebook_f32(nb, kind)
         codes[sel] = np.searchsorted(thr, u[sel], side="right").astype(np.uint8)
     return codes
 
 
 def dequantize(codes: np.ndarray, gains: np.ndarray, bits: np.ndarray,
-               rotation: str = "none") -> np.ndarray:
+               rotation: str = "none", kind: str = "lloyd_max") -> np.ndarray:
     """c_hat = g * R^T level_b[code] (R = I without rotation); 0-bit bins
     reconstruct to exactly 0 [Method/dec]."""
     codes = np.asarray(codes)
@@ -498,7 +554,7 @@ def dequantize(codes: np.ndarray, gains: np.ndarray, bits: np.ndarray,
         sel = b == nb
         if not sel.any():
             continue
-        levels, _, _ = lloyd_max(nb)
+        levels, _ = codebook(nb, kind)
         lv = levels[codes[sel].astype(np.int64)]
         if rotation == "hadamard":
             lv = unrotate(lv)
@@ -619,13 +675,16 @@ def allocate_uniform(var: np.ndarray, budget_bits: int) -> np.ndarray:
 
 
 def compress(x: np.ndarray, p: Params, axes=(0, 1, 2), alloc: str = "waterfill",
-             rotation: str = "hadamard") -> np.ndarray:
+             rotation: str = "hadamard", quantizer: str = "lloyd_max") -> np.ndarray:
     """One unit: transform, variances, allocation, quantization, record.
 
     ``axes`` and ``alloc`` ("waterfill" or "uniform") select the page's
     ablations; the method is all three axes with water-filling.
     ``rotation`` is "hadamard" (the page's shared rotation, the method)
-    or "none" (the identity, an ablation).
+    or "none" (the identity, an ablation).  ``quantizer`` is "lloyd_max"
+    (the method: RMS gain, Gaussian Lloyd-Max table) or one of the
+    backends of [Findings/SQ], "uniform" or "nf" (absmax gain of every bin,
+    the allocation unchanged).
     """
     x = np.asarray(x, dtype=np.float64).reshape(p.shape)
     coef = dct3_forward(x, axes)
@@ -634,20 +693,21 @@ def compress(x: np.ndarray, p: Params, axes=(0, 1, 2), alloc: str = "waterfill",
         bits = allocate_uniform(var, p.budget_bits).reshape(var.shape)
     else:
         bits = allocate_bits(var, total_bits(p), p.max_bits).reshape(var.shape)
-    g = gains_f32(var)
-    codes = quantize(coef, g, bits, rotation)
+    g = gains_f32(var) if quantizer == "lloyd_max" else gains_absmax_f32(coef, rotation)
+    codes = quantize(coef, g, bits, rotation, quantizer)
     return pack_record(codes, g, bits, p)
 
 
 def decompress(rec: np.ndarray, p: Params, out_dtype="bf16",
-               axes=(0, 1, 2), rotation: str = "hadamard") -> np.ndarray:
+               axes=(0, 1, 2), rotation: str = "hadamard",
+               quantizer: str = "lloyd_max") -> np.ndarray:
     """Unpack, dequantize, inverse transform, round [Method/dec].
 
     READING: the output is rounded to bfloat16 (nearest even) for a bf16
     cache, or to float32 for a float32 cache.
     """
     codes, g, b = unpack_record(rec, p)
-    xr = dct3_inverse(dequantize(codes, g, b, rotation), axes)
+    xr = dct3_inverse(dequantize(codes, g, b, rotation, quantizer), axes)
     if out_dtype == "bf16":
         return round_to_bf16(xr)
     if out_dtype == "f32":
@@ -656,9 +716,10 @@ def decompress(rec: np.ndarray, p: Params, out_dtype="bf16",
 
 
 def roundtrip(x: np.ndarray, p: Params, out_dtype="bf16", axes=(0, 1, 2),
-              alloc: str = "waterfill", rotation: str = "hadamard"):
-    rec = compress(x, p, axes, alloc, rotation)
-    return decompress(rec, p, out_dtype, axes, rotation), rec
+              alloc: str = "waterfill", rotation: str = "hadamard",
+              quantizer: str = "lloyd_max"):
+    rec = compress(x, p, axes, alloc, rotation, quantizer)
+    return decompress(rec, p, out_dtype, axes, rotation, quantizer), rec
 
 
 # --------------------------------------------------------------------------
@@ -724,7 +785,8 @@ def capacity_model(p: Params, layers: int, text_tokens: int, hbm_bytes: int,
 # O14: attention over the decoded visual cache                 [Method/dec]
 # --------------------------------------------------------------------------
 def attend(k_rec: np.ndarray, v_rec: np.ndarray, p: Params, q: np.ndarray,
-           scale: float, axes=(0, 1, 2), rotation: str = "hadamard"):
+           scale: float, axes=(0, 1, 2), rotation: str = "hadamard",
+           quantizer: str = "lloyd_max"):
     """One decoding step of attention over one unit pair's visual tokens.
 
     [Method/dec]: decoding reverses the codec and can be fused into the
@@ -739,8 +801,8 @@ def attend(k_rec: np.ndarray, v_rec: np.ndarray, p: Params, q: np.ndarray,
     which is what a caller needs to merge it with attention over the text
     tokens.
     """
-    K = decompress(k_rec, p, None, axes, rotation)
-    V = decompress(v_rec, p, None, axes, rotation)
+    K = decompress(k_rec, p, None, axes, rotation, quantizer)
+    V = decompress(v_rec, p, None, axes, rotation, quantizer)
     q = np.asarray(q, dtype=np.float64)
     qh = q.shape[0]
     rep = qh // p.kv_heads

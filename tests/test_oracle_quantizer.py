@@ -159,3 +159,96 @@ def test_rotation_flattens_a_spike():
     x[5] = 8.0
     v = rotate(x)
     assert np.allclose(np.abs(v[:64]), 1.0) and np.all(v[64:] == 0.0)
+
+
+# ---- the other quantizer backends of the page's comparison ----------------
+def _normal_table():
+    rows = {}
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "normal_quantiles.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        p, z = line.split()
+        rows[float(p)] = float(z)
+    return rows
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+def test_uniform_quantizer_mse_on_uniform_input(bits):
+    # a uniform quantizer with step D on U(-1, 1) has MSE D^2 / 12 (classic
+    # result); checked by quantizing a fine grid of the interval
+    from oracle import codebook
+    lv, th = codebook(bits, "uniform")
+    x = (np.arange(200000) + 0.5) / 100000.0 - 1.0
+    y = lv[np.searchsorted(th, x, side="right")]
+    step = 2.0 / 2 ** bits
+    assert abs(np.mean((x - y) ** 2) / (step * step / 12.0) - 1) < 1e-3
+    np.testing.assert_array_equal(lv, -lv[::-1])
+
+
+def test_nf_levels_match_the_normal_table():
+    from oracle import nf_levels
+    z = _normal_table()
+    for bits in (2, 3):
+        n = 2 ** bits
+        zmax = z[(n - 0.5) / n]
+        upper = nf_levels(bits)[n // 2:]
+        ref = [z[(k + 0.5) / n] / zmax for k in range(n // 2, n)]
+        np.testing.assert_allclose(upper, ref, atol=2e-4)
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+def test_nf_levels_sit_at_equal_probability_centres(bits):
+    # Phi(level * z_max) = (k + 1/2) / 2^b, with Phi from the oracle's own
+    # complementary error function (independent of the quantile routine)
+    from oracle import nf_levels
+    from oracle.tact_oracle import _upper_tail
+    n = 2 ** bits
+    lv = nf_levels(bits)
+    # z_max is the quantile at (n - 1/2) / n: solve it by bisection on erfc
+    lo, hi = 0.0, 10.0
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        if 1.0 - _upper_tail(mid) < (n - 0.5) / n:
+            lo = mid
+        else:
+            hi = mid
+    zmax = 0.5 * (lo + hi)
+    cdf = 1.0 - _upper_tail(lv * zmax)
+    np.testing.assert_allclose(cdf, (np.arange(n) + 0.5) / n, atol=1e-12)
+
+
+def test_lloyd_max_beats_the_other_backends_at_low_rate():
+    # at 1-3 bits the Gaussian Lloyd-Max table with the RMS gain beats both
+    # absmax-scaled grids on Gaussian bins (their outer levels sit at the
+    # bin's extreme value, far in the tail); from 4 bits on, NormalFloat's
+    # per-vector range catches up, so the comparison stops at 3
+    from oracle import gains_absmax_f32
+    rng = np.random.default_rng(11)
+    c = rng.standard_normal((2000, 128))
+    g_rms = gains_f32(np.mean(c ** 2, axis=1))
+    g_abs = gains_absmax_f32(c)
+    for b in (1, 2, 3):
+        bits = np.full(2000, b)
+        e = {}
+        for kind, g in (("lloyd_max", g_rms), ("uniform", g_abs), ("nf", g_abs)):
+            r = dequantize(quantize(c, g, bits, kind=kind), g, bits, kind=kind)
+            e[kind] = np.mean((r - c) ** 2)
+        assert e["lloyd_max"] < e["uniform"] and e["lloyd_max"] < e["nf"], (b, e)
+
+
+def test_heavy_tails_hurt_absmax_backends_most():
+    # the page's explanation of its quantizer comparison: with heavy-tailed
+    # coefficients (Student-t, 3 degrees of freedom) the absmax-scaled grids
+    # waste their range, while gain-shape SQ with the rotation keeps its
+    # distortion near the Gaussian value
+    from oracle import gains_absmax_f32
+    rng = np.random.default_rng(12)
+    c = rng.standard_t(3, size=(2000, 128))
+    bits = np.full(2000, 1)
+    g_rms = gains_f32(np.mean(c ** 2, axis=1))
+    r = dequantize(quantize(c, g_rms, bits, "hadamard"), g_rms, bits, "hadamard")
+    e_lm = np.mean((r - c) ** 2) / np.mean(c ** 2)
+    for kind in ("uniform", "nf"):
+        g = gains_absmax_f32(c)
+        r = dequantize(quantize(c, g, bits, kind=kind), g, bits, kind=kind)
+        assert np.mean((r - c) ** 2) / np.mean(c ** 2) > 1.2 * e_lm
