@@ -412,8 +412,11 @@ def nf_levels(bits: int) -> np.ndarray:
     is the symmetric form (equal-probability quantiles, absmax scaling).
     """
     n = 2 ** bits
-    q = ndtri((np.arange(n) + 0.5) / n)
-    return q / q[-1]
+    # the quantiles at (k + 1/2) / 2^b mirror about 1/2: the upper half,
+    # mirrored, keeps the table exactly symmetric (the middle threshold 0)
+    up = ndtri((np.arange(n // 2, n) + 0.5) / n)
+    up = up / up[-1]
+    return np.concatenate([-up[::-1], up])
 
 
 def codebook(bits: int, kind: str = "lloyd_max"):
