@@ -93,6 +93,16 @@ enum { TACT_ALLOC_WATERFILL = 0, TACT_ALLOC_UNIFORM = 1 };
  * normalized coefficients themselves (an ablation). */
 enum { TACT_ROTATION_NONE = 0, TACT_ROTATION_HADAMARD = 1 };
 
+/* Scalar quantizer of the coded bins ("Main Findings", the comparison of
+ * quantizer backends).  TACT_QUANT_LLOYD_MAX (the method): gain = RMS of the
+ * bin, Gaussian Lloyd-Max table.  TACT_QUANT_UNIFORM: gain = largest |value|
+ * of the (rotated) bin vector, 2^b equal cells of [-1, 1] with levels at the
+ * cell centres.  TACT_QUANT_NF: the same gain, NormalFloat levels (normal
+ * quantiles at (k + 1/2) / 2^b, outermost levels +-1).  Thresholds are the
+ * midpoints of adjacent levels; the allocation is the same for all three.
+ * The two comparison backends run on the per-axis kernels. */
+enum { TACT_QUANT_LLOYD_MAX = 0, TACT_QUANT_UNIFORM = 1, TACT_QUANT_NF = 2 };
+
 typedef struct {
   /* A unit (S * H * W * kv_heads * head_dim entries) holds at most 2^29
    * entries; larger units are TACT_ERR_UNSUPPORTED. */
@@ -105,10 +115,12 @@ typedef struct {
   int32_t axes;         /* TACT_AXES_ALL, or a non-empty subset              */
   int32_t alloc_mode;   /* TACT_ALLOC_WATERFILL or TACT_ALLOC_UNIFORM        */
   int32_t rotation;     /* TACT_ROTATION_HADAMARD or TACT_ROTATION_NONE      */
+  int32_t quantizer;    /* TACT_QUANT_LLOYD_MAX, _UNIFORM or _NF             */
 } tact_params;
 
 /* Fills *p with the method's defaults for the given geometry and budget
- * (dtype bf16, all axes, water-filling, cap 8, Hadamard rotation). */
+ * (dtype bf16, all axes, water-filling, cap 8, Hadamard rotation,
+ * Lloyd-Max quantizer). */
 void tact_params_init(tact_params* p, int32_t S, int32_t H, int32_t W,
                       int32_t kv_heads, int32_t head_dim, int32_t budget_bits);
 
@@ -184,6 +196,10 @@ const char* tact_last_error(void);
  * 2^bits levels and 2^bits - 1 thresholds, ascending.  Either pointer may be
  * NULL.  Returns the number of levels, or 0 for an invalid bit width. */
 int32_t tact_codebook(int32_t bits, float* levels, float* thresholds);
+
+/* The same for any quantizer (tact_params.quantizer); 0 for an invalid
+ * quantizer or bit width. */
+int32_t tact_quantizer_table(int32_t quantizer, int32_t bits, float* levels, float* thresholds);
 
 #ifdef __cplusplus
 }

@@ -30,12 +30,13 @@ TACT_BF16, TACT_F32 = 0, 1
 AXIS_S, AXIS_H, AXIS_W, AXES_ALL = 1, 2, 4, 7
 ALLOC_WATERFILL, ALLOC_UNIFORM = 0, 1
 ROTATION_NONE, ROTATION_HADAMARD = 0, 1
+QUANT_LLOYD_MAX, QUANT_UNIFORM, QUANT_NF = 0, 1, 2
 
 
 class TactParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("S", "H", "W", "kv_heads", "head_dim", "budget_bits", "max_bits",
-                 "dtype", "axes", "alloc_mode", "rotation")]
+                 "dtype", "axes", "alloc_mode", "rotation", "quantizer")]
 
 
 def _load():
@@ -55,6 +56,7 @@ def _load():
         "tact_status_string": (ctypes.c_char_p, [i32]),
         "tact_last_error": (ctypes.c_char_p, []),
         "tact_codebook": (i32, [i32, vp, vp]),
+        "tact_quantizer_table": (i32, [i32, i32, vp, vp]),
         "tact_attend_workspace_bytes": (sz, [P, i64, i32]),
         "tact_attend": (i32, [P, i64, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]),
         "tact_dbg_workspace_bytes": (sz, [P, i64]),
@@ -75,7 +77,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("tact_params_init", "tact_record_bytes", "tact_workspace_bytes",
             "tact_compress", "tact_decompress", "tact_roundtrip",
-            "tact_status_string", "tact_last_error", "tact_codebook",
+            "tact_status_string", "tact_last_error", "tact_codebook", "tact_quantizer_table",
             "tact_attend_workspace_bytes", "tact_attend",
             "tact_dbg_workspace_bytes", "tact_dbg_dct3", "tact_dbg_bin_variance",
             "tact_dbg_allocate", "tact_dbg_quantize", "tact_dbg_unpack",
@@ -113,6 +115,7 @@ class Geometry:
     axes: int = AXES_ALL
     alloc_mode: int = ALLOC_WATERFILL
     rotation: int = ROTATION_HADAMARD
+    quantizer: int = QUANT_LLOYD_MAX
 
     def params(self) -> TactParams:
         if self.dtype not in (torch.bfloat16, torch.float32):
@@ -120,7 +123,7 @@ class Geometry:
         return TactParams(self.S, self.H, self.W, self.kv_heads, self.head_dim,
                           self.budget_bits, self.max_bits,
                           TACT_BF16 if self.dtype == torch.bfloat16 else TACT_F32,
-                          self.axes, self.alloc_mode, self.rotation)
+                          self.axes, self.alloc_mode, self.rotation, self.quantizer)
 
     @property
     def unit_shape(self):
@@ -185,10 +188,11 @@ def workspace(geom: Geometry, n_units: int, device=None) -> torch.Tensor:
 def compress(kv: torch.Tensor, budget_bits: int, max_bits: int = 8, *,
              records: torch.Tensor | None = None, ws: torch.Tensor | None = None,
              axes: int = AXES_ALL, alloc_mode: int = ALLOC_WATERFILL,
-             rotation: int = ROTATION_HADAMARD) -> torch.Tensor:
+             rotation: int = ROTATION_HADAMARD,
+             quantizer: int = QUANT_LLOYD_MAX) -> torch.Tensor:
     """kv (U, S, H, W, Hkv, d) bf16/fp32 on the GPU -> records uint8 (U, record_bytes)."""
     g = Geometry.of(kv, budget_bits, max_bits=max_bits, axes=axes, alloc_mode=alloc_mode,
-                    rotation=rotation)
+                    rotation=rotation, quantizer=quantizer)
     U = kv.shape[0]
     if records is None:
         records = torch.empty((U, g.record_bytes()), dtype=torch.uint8, device=kv.device)
@@ -220,10 +224,10 @@ def roundtrip(kv: torch.Tensor, budget_bits: int, max_bits: int = 8, *,
               out: torch.Tensor | None = None, records: torch.Tensor | None = None,
               ws: torch.Tensor | None = None, keep_records: bool = True,
               axes: int = AXES_ALL, alloc_mode: int = ALLOC_WATERFILL,
-              rotation: int = ROTATION_HADAMARD):
+              rotation: int = ROTATION_HADAMARD, quantizer: int = QUANT_LLOYD_MAX):
     """Compress then decompress; returns (kv_hat, records or None)."""
     g = Geometry.of(kv, budget_bits, max_bits=max_bits, axes=axes, alloc_mode=alloc_mode,
-                    rotation=rotation)
+                    rotation=rotation, quantizer=quantizer)
     U = kv.shape[0]
     if out is None:
         out = torch.empty_like(kv)
@@ -273,6 +277,16 @@ def attend(k_records: torch.Tensor, v_records: torch.Tensor, geom: Geometry,
                             float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream()),
            "tact_attend")
     return out, lse
+
+
+def quantizer_table(quantizer: int, bits: int):
+    """The library's fp32 table of any quantizer (levels, thresholds), CPU tensors."""
+    n = 1 << bits
+    lv = torch.empty(n, dtype=torch.float32)
+    th = torch.empty(n - 1, dtype=torch.float32)
+    if _lib.tact_quantizer_table(quantizer, bits, lv.data_ptr(), th.data_ptr()) != n:
+        raise ValueError(f"invalid quantizer {quantizer} or bit width {bits}")
+    return lv, th
 
 
 def codebook(bits: int):

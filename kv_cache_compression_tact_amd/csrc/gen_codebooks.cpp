@@ -13,6 +13,8 @@
 //     with phi the density and Q the upper tail of N(0, 1);
 //   * solved by fixed-point (Lloyd) sweeps followed by Newton's method on
 //     F(y) = centroid(y) - y, whose Jacobian is tridiagonal (Thomas solve).
+// It also writes the two other quantizers of the page's comparison (a
+// symmetric uniform grid and NormalFloat, both of [-1, 1]).
 // Output: a C include with the tables as exact hexadecimal float literals
 // (rounded to fp32), ascending, code c = c-th level from the most negative.
 #include <cfloat>
@@ -99,8 +101,34 @@ std::vector<double> solve_positive_levels(int bits) {
 
 }  // namespace
 
+// Standard normal quantile by bisection on the lower tail 0.5 erfc(-x/sqrt2)
+double normal_quantile(double p) {
+  double lo = -40.0, hi = 40.0;
+  for (int it = 0; it < 200; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (0.5 * std::erfc(-mid / std::sqrt(2.0)) < p) lo = mid; else hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+void emit(const char* name, const std::vector<float>& v) {
+  std::printf("#define %s \\\n", name);
+  for (size_t i = 0; i < v.size(); ++i)
+    std::printf("  %a%s", (double)v[i], i + 1 < v.size() ? ",\\\n" : "\n");
+}
+
+// Midpoint thresholds of an ascending level table, rounded to fp32.
+void midpoints(const std::vector<double>& lv, std::vector<float>& thr) {
+  for (size_t j = 0; j + 1 < lv.size(); ++j) thr.push_back((float)(0.5 * (lv[j] + lv[j + 1])));
+}
+
 int main() {
   std::vector<float> levels, thresholds;
+  // the comparison backends of the page's "Main Findings": a symmetric
+  // uniform quantizer (2^b equal cells of [-1, 1], levels at the cell
+  // centres) and NormalFloat (normal quantiles at (k + 1/2) / 2^b, outermost
+  // levels at +-1); both scale by the bin's absolute maximum
+  std::vector<float> ulevels, uthresholds, nlevels, nthresholds;
   for (int b = 1; b <= 8; ++b) {
     const std::vector<double> y = solve_positive_levels(b);
     const int m = (int)y.size();
@@ -109,17 +137,34 @@ int main() {
     for (int j = m - 2; j >= 0; --j) thresholds.push_back((float)(-0.5 * (y[j] + y[j + 1])));
     thresholds.push_back(0.0f);
     for (int j = 0; j + 1 < m; ++j) thresholds.push_back((float)(0.5 * (y[j] + y[j + 1])));
+    const int n = 1 << b;
+    std::vector<double> ul(n), nl(n);
+    const double zmax = normal_quantile((n - 0.5) / n);
+    for (int k = 0; k < n; ++k) ul[k] = (2.0 * k + 1.0 - n) / n;
+    // the quantiles mirror about 1/2: the upper half, mirrored, keeps the
+    // table exactly symmetric (middle threshold 0)
+    for (int k = n / 2; k < n; ++k) {
+      nl[k] = normal_quantile((k + 0.5) / n) / zmax;
+      nl[n - 1 - k] = -nl[k];
+    }
+    for (int k = 0; k < n; ++k) {
+      ulevels.push_back((float)ul[k]);
+      nlevels.push_back((float)nl[k]);
+    }
+    midpoints(ul, uthresholds);
+    midpoints(nl, nthresholds);
   }
   std::printf("/* Generated by gen_codebooks.cpp: Gaussian Lloyd-Max tables, 1..8 bits,\n"
-              " * fp32, ascending.  Level table of b bits starts at (1<<b) - 2,\n"
-              " * threshold table at (1<<b) - b - 1. */\n");
+              " * fp32, ascending, and the uniform and NormalFloat tables of the same\n"
+              " * sizes.  Level table of b bits starts at (1<<b) - 2, threshold table\n"
+              " * at (1<<b) - b - 1. */\n");
   std::printf("#define TACT_CODEBOOK_LEVELS %zu\n#define TACT_CODEBOOK_THRESHOLDS %zu\n",
               levels.size(), thresholds.size());
-  std::printf("#define TACT_CODEBOOK_LEVEL_VALUES \\\n");
-  for (size_t i = 0; i < levels.size(); ++i)
-    std::printf("  %a%s", (double)levels[i], i + 1 < levels.size() ? ",\\\n" : "\n");
-  std::printf("#define TACT_CODEBOOK_THRESHOLD_VALUES \\\n");
-  for (size_t i = 0; i < thresholds.size(); ++i)
-    std::printf("  %a%s", (double)thresholds[i], i + 1 < thresholds.size() ? ",\\\n" : "\n");
+  emit("TACT_CODEBOOK_LEVEL_VALUES", levels);
+  emit("TACT_CODEBOOK_THRESHOLD_VALUES", thresholds);
+  emit("TACT_UNIFORM_LEVEL_VALUES", ulevels);
+  emit("TACT_UNIFORM_THRESHOLD_VALUES", uthresholds);
+  emit("TACT_NF_LEVEL_VALUES", nlevels);
+  emit("TACT_NF_THRESHOLD_VALUES", nthresholds);
   return 0;
 }

@@ -62,6 +62,8 @@ tact_status make_geometry(const tact_params* p, Geometry* g) {
     return fail(TACT_ERR_INVALID_ARGUMENT, "alloc_mode=%d: must be 0 or 1", p->alloc_mode);
   if (p->rotation != TACT_ROTATION_NONE && p->rotation != TACT_ROTATION_HADAMARD)
     return fail(TACT_ERR_INVALID_ARGUMENT, "rotation=%d: must be 0 or 1", p->rotation);
+  if (p->quantizer < TACT_QUANT_LLOYD_MAX || p->quantizer > TACT_QUANT_NF)
+    return fail(TACT_ERR_INVALID_ARGUMENT, "quantizer=%d: must be 0, 1 or 2", p->quantizer);
   Geometry& G = *g;
   G.S = p->S;
   G.H = p->H;
@@ -73,6 +75,7 @@ tact_status make_geometry(const tact_params* p, Geometry* g) {
   G.axes = p->axes;
   G.alloc_mode = p->alloc_mode;
   G.rotation = p->rotation;
+  G.quantizer = p->quantizer;
   G.dtype = p->dtype;
   G.n_bins = int64_t(p->S) * p->H * p->W * p->kv_heads;
   G.n_entries = G.n_bins * p->head_dim;
@@ -219,7 +222,7 @@ void compress_chunk(const Geometry& g, int64_t cn, const void* kv, int64_t kv_st
   const int in_pro = g.dtype == TACT_BF16 ? AX_PRO_BF16 : AX_PRO_F32;
   const int64_t vs = var_stride(g);
   const float inv_d = 1.0f / static_cast<float>(g.head_dim);
-  if (g.axes == TACT_AXES_ALL && plane_supported(g)) {
+  if (g.axes == TACT_AXES_ALL && plane_supported(g) && g.quantizer == TACT_QUANT_LLOYD_MAX) {
     // S on the matrix cores into the fp32 volume, then H and W fused in LDS
     // (the final coefficients replace the volume), the allocation, and one
     // streaming pass over the coded bins
@@ -264,7 +267,7 @@ void decompress_chunk(const Geometry& g, int64_t cn, const uint8_t* recs, void* 
   const RecordView rv = view(g, const_cast<uint8_t*>(recs));
   const int out_epi = g.dtype == TACT_BF16 ? AX_EPI_BF16 : AX_EPI_F32;
   launch_plane_offsets(g, cn, rv, w.poff, s);
-  if (g.axes == TACT_AXES_ALL && plane_supported(g)) {
+  if (g.axes == TACT_AXES_ALL && plane_supported(g) && g.quantizer == TACT_QUANT_LLOYD_MAX) {
     launch_plane(g, cn, 2, nullptr, w.coef, g.n_entries, w.tab, nullptr, 0, rv, w.poff, s);
     // the inverse S axis also undoes the quantizer's rotation (it acts on
     // the channels, so it commutes with the transform)
@@ -365,6 +368,7 @@ void tact_params_init(tact_params* p, int32_t S, int32_t H, int32_t W, int32_t k
   p->axes = TACT_AXES_ALL;
   p->alloc_mode = TACT_ALLOC_WATERFILL;
   p->rotation = TACT_ROTATION_HADAMARD;
+  p->quantizer = TACT_QUANT_LLOYD_MAX;
 }
 
 size_t tact_record_bytes(const tact_params* p) {
@@ -528,6 +532,16 @@ const char* tact_status_string(tact_status s) {
 
 const char* tact_last_error(void) { return g_last_error.c_str(); }
 
+int32_t tact_quantizer_table(int32_t quantizer, int32_t bits, float* levels, float* thresholds) {
+  if (bits < 1 || bits > 8 || quantizer < TACT_QUANT_LLOYD_MAX || quantizer > TACT_QUANT_NF)
+    return 0;
+  const int n = 1 << bits;
+  if (levels) std::memcpy(levels, kHostLevelsQ[quantizer] + (n - 2), sizeof(float) * n);
+  if (thresholds)
+    std::memcpy(thresholds, kHostThresholdsQ[quantizer] + (n - bits - 1), sizeof(float) * (n - 1));
+  return n;
+}
+
 int32_t tact_codebook(int32_t bits, float* levels, float* thresholds) {
   if (bits < 1 || bits > 8) return 0;
   const int n = 1 << bits;
@@ -612,6 +626,8 @@ tact_status tact_dbg_quantize(const tact_params* p, int64_t n_units, const float
   if (g.rotation != TACT_ROTATION_NONE)
     return fail(TACT_ERR_UNSUPPORTED, "tact_dbg_quantize: the stage entry point quantizes without the "
                 "shared rotation; set rotation = TACT_ROTATION_NONE");
+  if (g.quantizer != TACT_QUANT_LLOYD_MAX)
+    return fail(TACT_ERR_UNSUPPORTED, "tact_dbg_quantize: the stage entry point uses the Lloyd-Max table");
   if ((st = check_units(n_units)) != TACT_OK) return st;
   if (n_units == 0) return ok();
   if ((st = check_buffer(coef, "coef", 16)) != TACT_OK) return st;
@@ -644,6 +660,8 @@ tact_status tact_dbg_dequantize(const tact_params* p, int64_t n_units, const voi
   if (g.rotation != TACT_ROTATION_NONE)
     return fail(TACT_ERR_UNSUPPORTED, "tact_dbg_dequantize: the stage entry point quantizes without the "
                 "shared rotation; set rotation = TACT_ROTATION_NONE");
+  if (g.quantizer != TACT_QUANT_LLOYD_MAX)
+    return fail(TACT_ERR_UNSUPPORTED, "tact_dbg_dequantize: the stage entry point uses the Lloyd-Max table");
   if ((st = check_units(n_units)) != TACT_OK) return st;
   if (n_units == 0) return ok();
   if ((st = check_buffer(records, "records", 256)) != TACT_OK) return st;

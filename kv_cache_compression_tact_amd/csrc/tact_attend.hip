@@ -52,7 +52,7 @@ struct AttArgs {
   const float* tab;               // DCT-II matrices [3][64][64]
   float* tabT;                    // their transposes
   int S, H, W, kv_heads, head_dim, q_heads, rep;
-  int rotate, axes, max_bits;
+  int rotate, axes, max_bits, quant;
   int64_t n_bins, total_bits;
   int shw, n_chunks;
 };
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void k_att_proj(AttArgs a) {
   const int h = blockIdx.y;
   const int64_t pair = blockIdx.z;
   for (int j = threadIdx.x; j <= TACT_CODEBOOK_LEVELS; j += blockDim.x)
-    s_lv[j] = j ? c_levels[j - 1] : 0.f;
+    s_lv[j] = j ? c_levels_q[a.quant][j - 1] : 0.f;
   const float* qr = a.qrot + (pair * a.q_heads + static_cast<int64_t>(h) * a.rep) * D;
   for (int e = threadIdx.x; e < D * kMaxRep; e += blockDim.x) {
     const int c = e / kMaxRep, r = e % kMaxRep;
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kWave) void k_att_out(AttArgs a) {
   __shared__ float s_lv[TACT_CODEBOOK_LEVELS + 1];
   __shared__ uint2 s_w[kWave][8 * WPP];        // [bin][plane * WPP + word] as (lo, hi)
   for (int j = threadIdx.x; j <= TACT_CODEBOOK_LEVELS; j += blockDim.x)
-    s_lv[j] = j ? c_levels[j - 1] : 0.f;
+    s_lv[j] = j ? c_levels_q[a.quant][j - 1] : 0.f;
   __syncthreads();
   const int lane = threadIdx.x;
   const int chunk = blockIdx.x, h = blockIdx.y;
@@ -397,6 +397,7 @@ void launch_attend(const Geometry& g, int64_t n_pairs, int q_heads, RecordView k
   a.q_heads = q_heads;
   a.rep = q_heads / g.kv_heads;
   a.rotate = g.rotation == TACT_ROTATION_HADAMARD;
+  a.quant = g.quantizer;
   a.axes = g.axes;
   a.max_bits = g.max_bits;
   a.n_bins = g.n_bins;

@@ -14,7 +14,7 @@ namespace tact {
 // Geometry of one unit and of its record, derived from validated params.
 struct Geometry {
   int S, H, W, kv_heads, head_dim;
-  int max_bits, budget_bits, axes, alloc_mode, rotation;
+  int max_bits, budget_bits, axes, alloc_mode, rotation, quantizer;
   int dtype;
   int64_t n_bins;        // S*H*W*kv_heads
   int64_t n_entries;     // n_bins * head_dim
@@ -128,9 +128,12 @@ void launch_attend(const Geometry& g, int64_t n_pairs, int q_heads, RecordView k
                    float scale, float* qrot, float* field, float* partial, float* out, float* lse,
                    const float* tab, float* tabT, hipStream_t stream);
 
-// Host copy of the fp32 codebooks.
+// Host copy of the fp32 codebooks (Lloyd-Max), and of every quantizer's,
+// indexed [quantizer][...].
 extern const float kHostLevels[];
 extern const float kHostThresholds[];
+extern const float* const kHostLevelsQ[3];
+extern const float* const kHostThresholdsQ[3];
 
 }  // namespace tact
 

@@ -24,6 +24,12 @@ namespace tact {
 
 const float kHostLevels[TACT_CODEBOOK_LEVELS] = {TACT_CODEBOOK_LEVEL_VALUES};
 const float kHostThresholds[TACT_CODEBOOK_THRESHOLDS] = {TACT_CODEBOOK_THRESHOLD_VALUES};
+static const float kHostUniformLevels[TACT_CODEBOOK_LEVELS] = {TACT_UNIFORM_LEVEL_VALUES};
+static const float kHostUniformThresholds[TACT_CODEBOOK_THRESHOLDS] = {TACT_UNIFORM_THRESHOLD_VALUES};
+static const float kHostNfLevels[TACT_CODEBOOK_LEVELS] = {TACT_NF_LEVEL_VALUES};
+static const float kHostNfThresholds[TACT_CODEBOOK_THRESHOLDS] = {TACT_NF_THRESHOLD_VALUES};
+const float* const kHostLevelsQ[3] = {kHostLevels, kHostUniformLevels, kHostNfLevels};
+const float* const kHostThresholdsQ[3] = {kHostThresholds, kHostUniformThresholds, kHostNfThresholds};
 
 namespace {
 

@@ -263,6 +263,10 @@ struct AxisArgs {
                              // inverse rotation R^T to the input rows
   int rot_out;               // EPI_F32 plain pass: apply the rotation R to the
                              // output rows
+  int quant;                 // EPI_QUANT, PRO_DEQUANT: tact_params.quantizer; for
+                             // the uniform and NormalFloat tables EPI_QUANT
+                             // takes each bin's gain as its largest |value|
+                             // and writes it into the record
 };
 
 template <int NP>
@@ -320,9 +324,9 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
   __shared__ __attribute__((aligned(16))) float s_d[(PRO == PRO_DEQUANT) ? 4 * NP * 68 : 1];
   if constexpr (PRO == PRO_DEQUANT || EPI == EPI_QUANT) {
     if constexpr (PRO == PRO_DEQUANT)
-      for (int j = threadIdx.x; j < TACT_CODEBOOK_LEVELS; j += blockDim.x) s_levels[j] = c_levels[j];
+      for (int j = threadIdx.x; j < TACT_CODEBOOK_LEVELS; j += blockDim.x) s_levels[j] = c_levels_q[a.quant][j];
     if constexpr (EPI == EPI_QUANT)
-      for (int j = threadIdx.x; j < TACT_CODEBOOK_THRESHOLDS; j += blockDim.x) s_thr[j] = c_thresholds[j];
+      for (int j = threadIdx.x; j < TACT_CODEBOOK_THRESHOLDS; j += blockDim.x) s_thr[j] = c_thresholds_q[a.quant][j];
     __syncthreads();
   }
   const int N = a.N;
@@ -678,6 +682,8 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
       uint64_t* words = reinterpret_cast<uint64_t*>(r + a.rec.off_codes);
       const uint32_t* poff = a.plane_off + u * a.n_bins;
       const float* invg = a.inv_gain + u * a.var_stride;
+      float* gains = reinterpret_cast<float*>(r + a.rec.off_gains);
+      const bool absmax = a.quant != 0;
       constexpr int HALVES = TPW / 4;                  // 64-channel words per plane
       float* zt = s_z + (threadIdx.x / kWave) * ZROWS * ZROW;
       if (rot) {
@@ -728,9 +734,19 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
         }
         for (int k = s0; k < kend; ++k) {
           const int b = __builtin_amdgcn_readlane(bj, k - s0);
+          float inv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ij), k - s0));
+          if (absmax) {
+            // gain of every bin = largest |value| of its (rotated) vector
+            float mx = 0.f;
+#pragma unroll
+            for (int h = 0; h < HALVES; ++h) mx = fmaxf(mx, fabsf(zt[(k - s0) * ZROW + 64 * h + lane]));
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+            if (lane == 0) gains[bin0 + k * bins_per_k] = mx;
+            inv = mx > 0.f ? 1.0f / mx : 0.f;
+          }
           if (b == 0) continue;
           const int64_t p0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(pjlo, k - s0));
-          const float inv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ij), k - s0));
 #pragma unroll
           for (int h = 0; h < HALVES; ++h) {
             const int code = cell_index_lds(s_thr, zt[(k - s0) * ZROW + 64 * h + lane] * inv, b);
@@ -1782,6 +1798,7 @@ void launch_axis(const Geometry& g, int64_t n_units, int axis, int inverse, int 
   a.rec = rec;
   a.plane_off = plane_off;
   a.rotate = g.rotation == TACT_ROTATION_HADAMARD;
+  a.quant = g.quantizer;
   a.rot_in = rot_in && a.rotate && pro == PRO_F32 && (epi == EPI_F32 || epi == EPI_BF16);
   a.rot_out = rot_out && a.rotate && pro != PRO_DEQUANT && epi == EPI_F32;
   const int tpw = (epi == EPI_STATS || epi == EPI_QUANT) ? g.head_dim / 16 : 4;

@@ -130,6 +130,29 @@ def test_status_strings():
         assert len(lib().tact_status_string(s)) > 0
 
 
+def test_library_quantizer_tables_equal_oracle_tables():
+    from oracle import QUANTIZERS, codebook_f32
+    for q, name in enumerate(QUANTIZERS):
+        for b in range(1, 9):
+            lv, th = tact.quantizer_table(q, b)
+            olv, oth = codebook_f32(b, name)
+            assert torch.equal(lv, torch.from_numpy(olv)) and torch.equal(th, torch.from_numpy(oth))
+    assert lib().tact_quantizer_table(3, 2, None, None) == 0
+    assert lib().tact_quantizer_table(1, 0, None, None) == 0
+
+
+def test_quantizer_parameter():
+    p = _params()
+    assert p.quantizer == 0
+    for bad in (-1, 3):
+        assert lib().tact_record_bytes(ctypes.byref(_params(quantizer=bad))) == 0
+    fake = ctypes.c_void_p(1 << 20)
+    L = lib()
+    q1 = _params(quantizer=1, rotation=0)
+    assert L.tact_dbg_quantize(ctypes.byref(q1), 1, fake, fake, fake, fake, None) == 2
+    assert L.tact_dbg_dequantize(ctypes.byref(q1), 1, fake, fake, None) == 2
+
+
 def test_library_codebook_equals_oracle_table():
     from oracle import codebook_f32
     for b in range(1, 9):

@@ -96,6 +96,28 @@ def test_attend_matches_oracle(geo):
            out=out.cpu().numpy().astype(np.float64), lse=lse.cpu().numpy().astype(np.float64))
 
 
+@pytest.mark.parametrize("quant", [1, 2])
+def test_attend_quantizer_backends(quant):
+    # records coded with the uniform or NormalFloat table (absmax gains)
+    S, H, W, hk, d = 4, 6, 5, 2, 128
+    name = O.QUANTIZERS[quant]
+    p = O.Params(S, H, W, hk, d, 2, 8)
+    g = tact.Geometry(S, H, W, hk, d, 2, quantizer=quant)
+    krec = O.compress(_field(p.shape, 21), p, quantizer=name)[None]
+    vrec = O.compress(_field(p.shape, 22), p, quantizer=name)[None]
+    q = np.random.default_rng(23).standard_normal((1, 8, d)).astype(np.float32)
+    out, lse = tact.attend(torch.from_numpy(krec).cuda(), torch.from_numpy(vrec).cuda(), g,
+                           torch.from_numpy(q).cuda(), 0.1)
+    worst = 0.0
+    o_ref, l_ref = O.attend(krec[0], vrec[0], p, q[0].astype(np.float64), 0.1, quantizer=name)
+    V = O.decompress(vrec[0], p, None, quantizer=name)
+    o, l = out.cpu().numpy()[0], lse.cpu().numpy()[0]
+    for r in range(8):
+        vrms = math.sqrt(np.mean(V[:, :, :, r // 4, :] ** 2))
+        assert abs(l[r] - l_ref[r]) <= 1e-4 * (1 + abs(l_ref[r]))
+        assert np.max(np.abs(o[r] - o_ref[r])) <= 1e-4 * vrms * (1 + abs(l_ref[r]))
+
+
 def test_attend_axis_subset():
     # records coded with two of the three axes: the field transforms follow
     S, H, W, hk, d = 6, 5, 7, 2, 64

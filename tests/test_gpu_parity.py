@@ -48,6 +48,10 @@ def _orot(g):
     return "hadamard" if g.rotation == tact.ROTATION_HADAMARD else "none"
 
 
+def _oquant(g):
+    return O.QUANTIZERS[g.quantizer]
+
+
 def _units(g, n, seed=0, scale_spike=True):
     """n random correlated units of geometry g (AR(1) field + spikes), on GPU."""
     gen = torch.Generator(device="cpu").manual_seed(seed)
@@ -71,8 +75,7 @@ GEOMS = [
     (2, 5, 3, 2, 256, 4, 8, torch.bfloat16),
     (33, 3, 2, 1, 128, 3, 5, torch.bfloat16),       # S beyond 32
     (64, 2, 3, 1, 64, 1, 8, torch.float32),
-    # wider planes: each H / W contraction size and both decoding kernels
-    # (32-channel half planes up to ~600 positions, 64-channel planes above)
+    # wider planes: every H / W contraction size of the plane kernels
     (3, 17, 23, 2, 128, 2, 8, torch.bfloat16),
     (2, 10, 21, 1, 64, 1, 8, torch.float32),
     (2, 20, 12, 2, 64, 3, 8, torch.bfloat16),
@@ -257,7 +260,7 @@ def test_decompress_from_oracle_records(geo, rot):
             assert _rel(out[u], ref) <= 1e-5
 
 
-def _compare_records(rec_gpu, rec_ref, op, coef_ref, rotation="hadamard"):
+def _compare_records(rec_gpu, rec_ref, op, coef_ref, rotation="hadamard", quantizer="lloyd_max"):
     """End-to-end record comparison; returns stats."""
     c1, g1, b1 = O.unpack_record(rec_gpu, op)
     c2, g2, b2 = O.unpack_record(rec_ref, op)
@@ -287,7 +290,7 @@ def _compare_records(rec_gpu, rec_ref, op, coef_ref, rotation="hadamard"):
         u = u_all[~eq]
         bb = b1[same][:, None].repeat(op.head_dim, 1)[~eq]
         for ui, bi in zip(u, bb):
-            _, thr = O.codebook_f32(int(bi))
+            _, thr = O.codebook_f32(int(bi), quantizer)
             t = thr[np.argmin(np.abs(thr - ui))]
             # distance to the boundary in units of the bin gain
             assert abs(ui - t) <= 1e-5 * max(abs(float(t)), 1.0), (ui, t)
@@ -313,7 +316,8 @@ def _roundtrip_check(x_gpu, g, units=None):
     axes = tuple(a for a in range(3) if g.axes & (1 << a))
     alloc = "uniform" if g.alloc_mode == tact.ALLOC_UNIFORM else "waterfill"
     out, rec = tact.roundtrip(x_gpu, g.budget_bits, g.max_bits, axes=g.axes,
-                              alloc_mode=g.alloc_mode, rotation=g.rotation)
+                              alloc_mode=g.alloc_mode, rotation=g.rotation,
+                              quantizer=g.quantizer)
     units = range(x_gpu.shape[0]) if units is None else units
     for u in units:
         xs = x_gpu[u].float().cpu().numpy().astype(np.float64)
@@ -322,12 +326,13 @@ def _roundtrip_check(x_gpu, g, units=None):
         say(f"  unit {u}: forward rel err {e:.3e}")
         assert e <= 1e-5
         od = "bf16" if g.dtype == torch.bfloat16 else "f32"
-        ref_out, ref_rec = O.roundtrip(xs, op, od, axes, alloc, _orot(g))
+        ref_out, ref_rec = O.roundtrip(xs, op, od, axes, alloc, _orot(g), _oquant(g))
         m_gpu = O.mse(out[u].float().cpu().numpy(), xs)
         m_ref = O.mse(ref_out, xs)
         say(f"  unit {u}: mse gpu {m_gpu:.6e} oracle {m_ref:.6e}")
         assert abs(m_gpu / m_ref - 1) <= 1e-3
-        _compare_records(rec[u].cpu().numpy(), ref_rec, op, O.dct3_forward(xs, axes), _orot(g))
+        _compare_records(rec[u].cpu().numpy(), ref_rec, op, O.dct3_forward(xs, axes), _orot(g),
+                         _oquant(g))
 
 
 @pytest.mark.parametrize("geo", GEOMS + GEOMS_AXIS_PATH)
@@ -343,6 +348,31 @@ def test_roundtrip_without_rotation(geo):
     g = _geom(*geo, rotation=0)
     say("roundtrip no rotation", geo)
     _roundtrip_check(_units(g, 2, seed=13), g)
+
+
+@pytest.mark.parametrize("quant", [1, 2])
+@pytest.mark.parametrize("rot", [1, 0])
+@pytest.mark.parametrize("geo", [GEOMS[1], GEOMS[3], GEOMS[6], GEOMS_AXIS_PATH[0]])
+def test_roundtrip_quantizer_backends(geo, rot, quant):
+    # the page's quantizer comparison: symmetric uniform and NormalFloat
+    # tables with absmax gains (records, gains and round-trip MSE)
+    g = _geom(*geo, rotation=rot, quantizer=quant)
+    say("roundtrip quantizer", quant, geo, "rotation", rot)
+    _roundtrip_check(_units(g, 2, seed=15), g)
+
+
+@pytest.mark.parametrize("quant", [1, 2])
+def test_decompress_quantizer_backends_from_oracle_records(quant):
+    g = _geom(3, 17, 23, 2, 128, 2, 8, torch.float32, quantizer=quant)
+    op = _oparams(g)
+    xs = _units(g, 2, seed=16).cpu().numpy().astype(np.float64)
+    recs = np.stack([O.compress(xs[u], op, quantizer=_oquant(g)) for u in range(2)])
+    out = tact.decompress(torch.from_numpy(recs).cuda(), g).cpu().numpy()
+    for u in range(2):
+        ref = O.decompress(recs[u], op, None, quantizer=_oquant(g))
+        e = _rel(out[u], ref)
+        say(f"  quantizer {quant} unit {u}: rel err {e:.2e}")
+        assert e <= 1e-5
 
 
 def test_rotation_spreads_a_spike_channel():
