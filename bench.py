@@ -44,6 +44,11 @@ def _parse():
     ap.add_argument("--attend", action="store_true",
                     help="time decoding fused into attention (tact_attend) over every "
                          "layer and sequence of the workload instead of the codec")
+    ap.add_argument("--ablations", action="store_true",
+                    help="reconstruction error of the page's ablations (axes, allocation, "
+                         "rotation, quantizer backends) on the GPU, and Theorem 1's closure")
+    ap.add_argument("--ablation-units", type=int, default=8,
+                    help="units of the workload used by --ablations")
     ap.add_argument("--q-per-kv", type=int, default=4,
                     help="query heads per kv head for --attend")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -122,6 +127,62 @@ def measured_traffic(workload: str):
     if h.hexdigest() != rec.get("source_sha256"):
         return None
     return rec
+
+
+def bench_ablations(args, tact, wl, budget, g, x):
+    """Relative reconstruction error ||x_hat - x||^2 / ||x||^2 of the codec
+    and of the page's ablations ("Main Findings": fewer transform axes,
+    uniform allocation, the quantizer backends; and the rotation), all run on
+    the GPU over the first units of the workload; and Theorem 1's closure:
+    the measured distortion ratio of uniform to water-filling allocation
+    beside 1/gamma, gamma the spectral flatness (geometric over arithmetic
+    mean) of each unit's bin variances."""
+    n = min(args.ablation_units, x.shape[0])
+    xs = x[:n].contiguous()
+    ref = xs.float()
+    energy = float((ref * ref).sum())
+
+    def err(**kw):
+        out, _ = tact.roundtrip(xs, budget, wl.max_bits, keep_records=False, **kw)
+        return float(((out.float() - ref) ** 2).sum()) / energy
+
+    variants = {
+        "method (3-axis DCT, water-filling, rotation, Lloyd-Max)": {},
+        "2-axis DCT (H, W)": {"axes": tact.AXIS_H | tact.AXIS_W},
+        "2-axis DCT (S, W)": {"axes": tact.AXIS_S | tact.AXIS_W},
+        "1-axis DCT (S)": {"axes": tact.AXIS_S},
+        "uniform allocation": {"alloc_mode": tact.ALLOC_UNIFORM},
+        "no rotation": {"rotation": tact.ROTATION_NONE},
+        "symmetric uniform quantizer": {"quantizer": tact.QUANT_UNIFORM},
+        "NormalFloat quantizer": {"quantizer": tact.QUANT_NF},
+        "symmetric uniform quantizer, no rotation": {"quantizer": tact.QUANT_UNIFORM,
+                                                     "rotation": tact.ROTATION_NONE},
+        "NormalFloat quantizer, no rotation": {"quantizer": tact.QUANT_NF,
+                                               "rotation": tact.ROTATION_NONE},
+    }
+    res = {name: round(err(**kw), 6) for name, kw in variants.items()}
+    # Theorem 1: D_uniform / D_waterfill against 1 / gamma, per unit
+    coef = tact.dbg_dct3(xs, g)
+    var = tact.dbg_bin_variance(coef, g).double().reshape(n, -1).clamp_min(1e-300)
+    gamma = torch.exp(torch.log(var).mean(1)) / var.mean(1)
+    out_w, _ = tact.roundtrip(xs, budget, wl.max_bits, keep_records=False)
+    out_u, _ = tact.roundtrip(xs, budget, wl.max_bits, keep_records=False,
+                              alloc_mode=tact.ALLOC_UNIFORM)
+    dims = tuple(range(1, xs.dim()))
+    d_w = ((out_w.float() - ref) ** 2).sum(dims).double()
+    d_u = ((out_u.float() - ref) ** 2).sum(dims).double()
+    closure = [{"unit": u, "inv_gamma": round(float(1 / gamma[u]), 3),
+                "measured_ratio": round(float(d_u[u] / d_w[u]), 3)} for u in range(n)]
+    line = {
+        "metric": "relative reconstruction error of the codec and its ablations (GPU)",
+        "value": res["method (3-axis DCT, water-filling, rotation, Lloyd-Max)"],
+        "unit": "||x_hat - x||^2 / ||x||^2", "higher_is_better": False, "n_gpus": 1,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "units": n, "unit_shape": list(wl.unit_shape),
+                   "budget_bits": budget},
+        "ablations": res, "theorem1_closure": closure,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def bench_attend(args, tact, wl, budget, g, x):
@@ -211,6 +272,9 @@ def main():
     U = wl.n_units
     if args.attend:
         bench_attend(args, tact, wl, budget, g, x)
+        return
+    if args.ablations:
+        bench_ablations(args, tact, wl, budget, g, x)
         return
     rec = torch.empty((U, g.record_bytes()), dtype=torch.uint8, device=dev)
     out = torch.empty_like(x)
