@@ -77,6 +77,34 @@ __device__ __forceinline__ void split2(float x, _Float16& hi, _Float16& lo) {
   lo = static_cast<_Float16>(x - static_cast<float>(hi));
 }
 
+// The same split for two products a0 * b0 and a1 * b1, packed two halves
+// per register: v_fma_mix rounds each product to fp16 (hi), then reads that
+// hi back as an fp16 operand and rounds the exactly formed remainder
+// a * b - hi to fp16 (lo).  When b is a power of two the product is exact
+// and the result equals split2 of the scaled value; otherwise hi + lo
+// carries the product to about 22 bits.  Products must stay below 2^15.
+// A matrix instruction may read a VGPR only two wait states after a VALU
+// write; the compiler's hazard check counts an asm block as one, so each
+// block ends with those two itself.
+__device__ __forceinline__ uint32_t split_hi_pair(float a0, float b0, float a1, float b1) {
+  uint32_t hi;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0\n\t"
+      "v_fma_mixhi_f16 %0, %3, %4, 0\n\t"
+      "s_nop 1"
+      : "=&v"(hi)
+      : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
+  return hi;
+}
+__device__ __forceinline__ uint32_t split_lo_pair(float a0, float b0, float a1, float b1, uint32_t hi) {
+  uint32_t lo;
+  asm("v_fma_mixlo_f16 %0, %1, %2, -%5 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %3, %4, -%5 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "s_nop 1"
+      : "=&v"(lo)
+      : "v"(a0), "v"(b0), "v"(a1), "v"(b1), "v"(hi));
+  return lo;
+}
+
 // max over the 4 lane groups that hold the K ranges of one column: the
 // permlane swaps exchange lanes l and l ^ 32 (then l ^ 16) between two
 // copies of v, so the max of the two results is the pairwise max
@@ -278,6 +306,18 @@ struct Frag {
   static constexpr int MT = NP / 16;
   typedef typename std::conditional<NP == 16, f16x4, f16x8>::type vec;
 };
+
+// KV fp16 values from KV / 2 packed pairs
+template <int NP>
+__device__ __forceinline__ typename Frag<NP>::vec pairs_to_vec(const uint32_t (&w)[Frag<NP>::KV / 2]) {
+  if constexpr (Frag<NP>::KV == 8) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(typename Frag<NP>::vec, u4{w[0], w[1], w[2], w[3]});
+  } else {
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(typename Frag<NP>::vec, u2{w[0], w[1]});
+  }
+}
 
 template <int NP>
 __device__ __forceinline__ f32x4 mfma(typename Frag<NP>::vec a, typename Frag<NP>::vec b, f32x4 c) {
@@ -585,21 +625,24 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
       const float unscale = ldexpf(1.0f, e - 26) * rpost[i];
 #pragma unroll
       for (int ks = 0; ks < F::KSTEPS; ++ks) {
-        vec bhi, blo;
+        uint32_t hw[F::KV / 2], lw[F::KV / 2];
 #pragma unroll
-        for (int v = 0; v < F::KV; ++v) {
-          _Float16 h, l;
-          split2(xi[ks][v] * sc, h, l);
-          bhi[v] = h;
-          blo[v] = l;
+        for (int v = 0; v < F::KV; v += 2) {
+          hw[v / 2] = split_hi_pair(xi[ks][v], sc, xi[ks][v + 1], sc);
+          // a scaled bf16 input is exact in fp16 down to 2^-14, 2^27 below
+          // the column maximum: its x_lo term is negligible and skipped
+          if constexpr (PRO != PRO_BF16) lw[v / 2] = split_lo_pair(xi[ks][v], sc, xi[ks][v + 1], sc, hw[v / 2]);
         }
+        const vec bhi = pairs_to_vec<NP>(hw);
 #pragma unroll
         for (int m = 0; m < F::MT; ++m) {
           acc[i][m] = mfma<NP>(ahi[m][ks], bhi, acc[i][m]);
           acc[i][m] = mfma<NP>(alo[m][ks], bhi, acc[i][m]);
-          // a scaled bf16 input is exact in fp16 down to 2^-14, 2^27 below
-          // the column maximum: its x_lo term is negligible and skipped
-          if constexpr (PRO != PRO_BF16) acc[i][m] = mfma<NP>(ahi[m][ks], blo, acc[i][m]);
+        }
+        if constexpr (PRO != PRO_BF16) {
+          const vec blo = pairs_to_vec<NP>(lw);
+#pragma unroll
+          for (int m = 0; m < F::MT; ++m) acc[i][m] = mfma<NP>(ahi[m][ks], blo, acc[i][m]);
         }
       }
 #pragma unroll
@@ -850,14 +893,13 @@ __device__ __forceinline__ void contract4(const typename Frag<NP>::vec (&ahi)[Fr
     const float unscale = ldexpf(1.0f, e - 26) * post[i];
 #pragma unroll
     for (int ks = 0; ks < F::KSTEPS; ++ks) {
-      vec bhi, blo;
+      uint32_t hw[F::KV / 2], lw[F::KV / 2];
 #pragma unroll
-      for (int v = 0; v < F::KV; ++v) {
-        _Float16 h, l;
-        split2(xv[i][ks][v] * sc, h, l);
-        bhi[v] = h;
-        blo[v] = l;
+      for (int v = 0; v < F::KV; v += 2) {
+        hw[v / 2] = split_hi_pair(xv[i][ks][v], sc, xv[i][ks][v + 1], sc);
+        lw[v / 2] = split_lo_pair(xv[i][ks][v], sc, xv[i][ks][v + 1], sc, hw[v / 2]);
       }
+      const vec bhi = pairs_to_vec<NP>(hw), blo = pairs_to_vec<NP>(lw);
 #pragma unroll
       for (int m = 0; m < F::MT; ++m) {
         acc[i][m] = mfma<NP>(ahi[m][ks], bhi, acc[i][m]);
@@ -981,7 +1023,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
   extern __shared__ float4 plane_v4[];
   float* plane = reinterpret_cast<float*>(plane_v4);
   const int lane = threadIdx.x % kWave;
-  const int wv = threadIdx.x / kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
   const int t = lane % 16, g = lane / 16;
   const int H = a.H, W = a.W;
   constexpr int kGroups = MODE == MODE_DEQUANT ? kXcds : 1;
@@ -1199,9 +1241,10 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
       const bool more = pn >= 0;
       // ---- inverse W: decode into the B fragments, contract; a wave owns one
       // kh row.  The row's LDS area first holds its bins' side info and code
-      // words, 80 bytes per bin: {bits, gain, 0, 0}, the low 32-bit halves of
-      // the 8 plane words, then their high halves (planes at or above the
-      // bin's bit width are 0).  Lane (t, g) then rebuilds the codes of its
+      // words, 80 bytes per bin: {bits, gain, first level-table entry, 0},
+      // the low 32-bit halves of the 8 plane words, then their high halves
+      // (planes at or above the bin's bit width are 0; bins without bits
+      // have gain 0).  Lane (t, g) then rebuilds the codes of its
       // channels 4t..4t+3 for its K rows kw: it reads the 8 halves that hold
       // its channels at once, and each plane gives a nibble, spread into one
       // byte per channel.
@@ -1216,7 +1259,10 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
         if (kh >= H) break;
         uint4* st = reinterpret_cast<uint4*>(plane + static_cast<int64_t>(kh) * W * 64);
         if (lane < W) {
-          st[lane * 5] = uint4{static_cast<uint32_t>(bj[q]), __float_as_uint(gjv[q]), 0u, 0u};
+          // {bits, gain (0 without bits), first level-table entry, 0}
+          const int b = bj[q];
+          st[lane * 5] = uint4{static_cast<uint32_t>(b), b > 0 ? __float_as_uint(gjv[q]) : 0u,
+                               b > 0 ? (1u << b) - 1u : 0u, 0u};
           st[lane * 5 + 1] = uint4{wd[q][0].x, wd[q][1].x, wd[q][2].x, wd[q][3].x};
           st[lane * 5 + 2] = uint4{wd[q][4].x, wd[q][5].x, wd[q][6].x, wd[q][7].x};
           st[lane * 5 + 3] = uint4{wd[q][0].y, wd[q][1].y, wd[q][2].y, wd[q][3].y};
@@ -1244,25 +1290,35 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
         for (int ks = 0; ks < FW::KSTEPS; ++ks)
 #pragma unroll
           for (int v = 0; v < FW::KV; ++v) {
+            // K rows kw >= W read the staging of bin W - 1 and take gain 0:
+            // their A' column is 0, so the (finite) levels they pick add
+            // nothing.  Every table index stays below 2^(b + 1) - 1 for the
+            // b of the staged bin (its planes at or above b are 0).
             const int kw = ks * FW::KPER + FW::KV * g + v;
-            uint4 sb = uint4{0u, 0u, 0u, 0u}, w03 = sb, w47 = sb;
-            if (kw < W) {
-              sb = st[kw * 5];
-              w03 = st[kw * 5 + half];
-              w47 = st[kw * 5 + half + 1];
-            }
-            const uint32_t wk[8] = {w03.x, w03.y, w03.z, w03.w, w47.x, w47.y, w47.z, w47.w};
-            const int b = static_cast<int>(sb.x);
-            // byte i of `codes` collects the bits of channel 4t + i
+            const bool in = kw < W;
+            const int kc = in ? kw : W - 1;
+            const uint4 sb = st[kc * 5];
+            const uint4 w03 = st[kc * 5 + half];
+            const uint4 w47 = st[kc * 5 + half + 1];
+            uint32_t wk[8] = {w03.x, w03.y, w03.z, w03.w, w47.x, w47.y, w47.z, w47.w};
+            // (all three reads issue here, not one word per plane below)
+            asm("" : "+v"(wk[0]), "+v"(wk[1]), "+v"(wk[2]), "+v"(wk[3]), "+v"(wk[4]), "+v"(wk[5]),
+                "+v"(wk[6]), "+v"(wk[7]));
+            int b = in ? static_cast<int>(sb.x) : 0;
+            asm("" : "+v"(b));
+            // byte i of `codes` collects the bits of channel 4t + i (the
+            // spread is kept apart from the shift so that it stays a 24-bit
+            // multiply)
             uint32_t codes = 0;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
               if (__ballot(k < b) == 0) break;
-              const uint32_t nib = __builtin_amdgcn_ubfe(wk[k], nib_sh, 4);
-              codes |= ((nib * 0x204081u) & 0x01010101u) << k;
+              uint32_t sp = __builtin_amdgcn_ubfe(wk[k], nib_sh, 4) * 0x204081u;
+              asm("" : "+v"(sp));
+              codes |= (sp & 0x01010101u) << k;
             }
-            gv[ks][v] = b > 0 ? __uint_as_float(sb.y) : 0.f;
-            const int base = b > 0 ? (1 << b) - 1 : 0;        // s_lp[0] = 0
+            gv[ks][v] = in ? __uint_as_float(sb.y) : 0.f;
+            const int base = static_cast<int>(sb.z);           // s_lp[0] = 0
 #pragma unroll
             for (int i = 0; i < 4; ++i) bp[i][ks][v] = s_lp[base + static_cast<int>((codes >> (8 * i)) & 0xFFu)];
           }
@@ -1286,22 +1342,23 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
         typename FW::vec ahi_w[FW::MT][FW::KSTEPS], alo_w[FW::MT][FW::KSTEPS];
         const int la = opaque(lane);
 #pragma unroll
+        for (int ks = 0; ks < FW::KSTEPS; ++ks)
+#pragma unroll
+          for (int v = 0; v < FW::KV; ++v) gv[ks][v] *= gsc;
+#pragma unroll
         for (int m = 0; m < FW::MT; ++m)
 #pragma unroll
-          for (int ks = 0; ks < FW::KSTEPS; ++ks)
+          for (int ks = 0; ks < FW::KSTEPS; ++ks) {
+            uint32_t hw[FW::KV / 2], lw[FW::KV / 2];
 #pragma unroll
-            for (int v = 0; v < FW::KV; ++v) {
-              // the product is rounded to fp32 and hidden from the optimizer
-              // before the split: otherwise hi is formed once from the exact
-              // product (fused) and once from the rounded one, and lo pairs
-              // with a hi that differs from the operand hi
-              float ap = s_aw[((m * FW::KSTEPS + ks) * FW::KV + v) * kWave + la] * (gv[ks][v] * gsc);
-              asm volatile("" : "+v"(ap));
-              _Float16 h, l;
-              split2(ap, h, l);
-              ahi_w[m][ks][v] = h;
-              alo_w[m][ks][v] = l;
+            for (int v = 0; v < FW::KV; v += 2) {
+              const float* c = s_aw + ((m * FW::KSTEPS + ks) * FW::KV + v) * kWave + la;
+              hw[v / 2] = split_hi_pair(c[0], gv[ks][v], c[kWave], gv[ks][v + 1]);
+              lw[v / 2] = split_lo_pair(c[0], gv[ks][v], c[kWave], gv[ks][v + 1], hw[v / 2]);
             }
+            ahi_w[m][ks] = pairs_to_vec<NPW>(hw);
+            alo_w[m][ks] = pairs_to_vec<NPW>(lw);
+          }
         f32x4 acc[4][FW::MT];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
