@@ -1036,6 +1036,10 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
   // byte strides of a slice: one w step, one h row; this lane's columns
   const int cbytes = static_cast<int>(a.C) * 4;
   const int row_bytes = W * cbytes;
+  // LDS row stride in 64-float positions: the decode pass stages the side
+  // info of NPW bins (80 bytes each) in a row's area, so short rows are
+  // padded
+  const int RW = MODE == MODE_DEQUANT ? max(W, (NPW * 80 + 255) / 256) : W;
   // bin of (s, kh, kw) of a plane's head
   auto bin_of3 = [&](const PlaneId& id, int kh, int kw) -> int64_t {
     return ((static_cast<int64_t>(id.s) * H + kh) * W + kw) * a.kv_heads + id.head;
@@ -1257,8 +1261,9 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
       for (int q = 0; q < SLH; ++q) {
         const int kh = wv + kPlaneWaves * q;
         if (kh >= H) break;
-        uint4* st = reinterpret_cast<uint4*>(plane + static_cast<int64_t>(kh) * W * 64);
-        if (lane < W) {
+        uint4* st = reinterpret_cast<uint4*>(plane + static_cast<int64_t>(kh) * RW * 64);
+        // lanes W..NPW-1 read nothing and stage an empty bin
+        if (lane < NPW) {
           // {bits, gain (0 without bits), first level-table entry, 0}
           const int b = bj[q];
           st[lane * 5] = uint4{static_cast<uint32_t>(b), b > 0 ? __float_as_uint(gjv[q]) : 0u,
@@ -1279,7 +1284,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
       for (int q = 0; q < SLH; ++q) {
         const int kh = wv + kPlaneWaves * q;
         if (kh >= H) break;
-        float* row = plane + static_cast<int64_t>(kh) * W * 64;
+        float* row = plane + static_cast<int64_t>(kh) * RW * 64;
         const uint4* st = reinterpret_cast<const uint4*>(row);
         const int nib_sh = (4 * t) & 31;
         const int half = t >= 8 ? 3 : 1;     // the halves holding channels 4t..4t+3
@@ -1290,21 +1295,16 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
         for (int ks = 0; ks < FW::KSTEPS; ++ks)
 #pragma unroll
           for (int v = 0; v < FW::KV; ++v) {
-            // K rows kw >= W read the staging of bin W - 1 and take gain 0:
-            // their A' column is 0, so the (finite) levels they pick add
-            // nothing.  Every table index stays below 2^(b + 1) - 1 for the
-            // b of the staged bin (its planes at or above b are 0).
+            // (K rows kw >= W are staged as empty bins)
             const int kw = ks * FW::KPER + FW::KV * g + v;
-            const bool in = kw < W;
-            const int kc = in ? kw : W - 1;
-            const uint4 sb = st[kc * 5];
-            const uint4 w03 = st[kc * 5 + half];
-            const uint4 w47 = st[kc * 5 + half + 1];
+            const uint4 sb = st[kw * 5];
+            const uint4 w03 = st[kw * 5 + half];
+            const uint4 w47 = st[kw * 5 + half + 1];
             uint32_t wk[8] = {w03.x, w03.y, w03.z, w03.w, w47.x, w47.y, w47.z, w47.w};
             // (all three reads issue here, not one word per plane below)
             asm("" : "+v"(wk[0]), "+v"(wk[1]), "+v"(wk[2]), "+v"(wk[3]), "+v"(wk[4]), "+v"(wk[5]),
                 "+v"(wk[6]), "+v"(wk[7]));
-            int b = in ? static_cast<int>(sb.x) : 0;
+            int b = static_cast<int>(sb.x);
             asm("" : "+v"(b));
             // byte i of `codes` collects the bits of channel 4t + i (the
             // spread is kept apart from the shift so that it stays a 24-bit
@@ -1317,7 +1317,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
               asm("" : "+v"(sp));
               codes |= (sp & 0x01010101u) << k;
             }
-            gv[ks][v] = in ? __uint_as_float(sb.y) : 0.f;
+            gv[ks][v] = __uint_as_float(sb.y);
             const int base = static_cast<int>(sb.z);           // s_lp[0] = 0
 #pragma unroll
             for (int i = 0; i < 4; ++i) bp[i][ks][v] = s_lp[base + static_cast<int>((codes >> (8 * i)) & 0xFFu)];
@@ -1410,7 +1410,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
           for (int v = 0; v < FH::KV; ++v) {
             const int kh = ks * FH::KPER + FH::KV * g + v;
             float4 qv = float4{0.f, 0.f, 0.f, 0.f};
-            if (kh < H) qv = lds_ld4(plane + (kh * W + w) * 64 + 4 * t);
+            if (kh < H) qv = lds_ld4(plane + (kh * RW + w) * 64 + 4 * t);
             xv[0][ks][v] = qv.x; xv[1][ks][v] = qv.y; xv[2][ks][v] = qv.z; xv[3][ks][v] = qv.w;
           }
         f32x4 acc[4][FH::MT];
@@ -1916,8 +1916,15 @@ void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in,
   a.n_units = n_units;
   const int64_t n_planes = n_units * g.S * (a.C / 64);
   const dim3 block(64 * kPlaneWaves);
-  const size_t lds = static_cast<size_t>(g.H) * g.W * 64 * sizeof(float);
   const bool h16 = g.H <= 16, w16 = g.W <= 16;
+  // the decode pass pads rows shorter than its staging (80 bytes per bin of
+  // the 16 or 32 K rows)
+  int rw = g.W;
+  if (mode == MODE_DEQUANT) {
+    const int need = ((w16 ? 16 : 32) * 80 + 255) / 256;
+    if (rw < need) rw = need;
+  }
+  const size_t lds = static_cast<size_t>(g.H) * rw * 64 * sizeof(float);
   // the plane needs more dynamic LDS than the default limit
   // persistent grid: as many blocks as the device holds at once
 #define TACT_PLANE_ONE(NH, NW, M, SL)                                                           \
