@@ -970,6 +970,9 @@ static_assert(levels_below(8.0f), "decode scaling assumes |level| < 8");
 // the H columns of its w; inverse: the record words and side info of its kh
 // rows), so memory and compute overlap.
 constexpr int kPlaneWaves = 8;
+// the decode pass runs 12 waves (3 per SIMD) on planes of 17..24 rows and
+// columns: two rows and two columns per wave, 146 VGPRs
+constexpr int kDecodeWaves = 12;
 
 // The decoding walk is XCD-aware.  Workgroups are dispatched to the 8 XCDs
 // round robin (block b runs on XCD b % 8) and every XCD has its own L2.  The
@@ -1062,14 +1065,15 @@ __device__ __forceinline__ PlaneId plane_id(const PlaneArgs& a, int64_t p64) {
   return id;
 }
 
-template <int NPH, int NPW, int MODE, int SL>
-__global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
+template <int NPH, int NPW, int MODE, int SL, int WV>
+__global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
+  constexpr int kWaves = WV;
   using FH = Frag<NPH>;
   using FW = Frag<NPW>;
   // w columns (H passes) and kh rows (W passes) per wave: SL covers
   // ceil(max(H, W) / 8)
-  constexpr int SLW = (SL < NPW / kPlaneWaves) ? SL : NPW / kPlaneWaves;
-  constexpr int SLH = (SL < NPH / kPlaneWaves) ? SL : NPH / kPlaneWaves;
+  constexpr int SLW = (SL < (NPW + kWaves - 1) / kWaves) ? SL : (NPW + kWaves - 1) / kWaves;
+  constexpr int SLH = (SL < (NPH + kWaves - 1) / kWaves) ? SL : (NPH + kWaves - 1) / kWaves;
   // [H][W][64] fp32; 16-byte aligned so that float4 accesses are single
   // 128-bit LDS operations (a 16-lane group then covers all 64 banks once)
   extern __shared__ float4 plane_v4[];
@@ -1151,7 +1155,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
     float xs[SLW][4][FH::KSTEPS][FH::KV];
     auto fetch_cols = [&](int64_t p, int j) {
       const PlaneId id = plane_id(a, p);
-      const int w = wv + kPlaneWaves * j;
+      const int w = wv + kWaves * j;
       // the slice as a buffer: rows h >= H read as 0
       const __amdgpu_buffer_rsrc_t rin = make_rsrc(a.in + id.vol, static_cast<int64_t>(row_bytes) * H);
       const int voff = (FH::KV * g * W + w) * cbytes + static_cast<int>(id.c0 + 4 * t) * 4;
@@ -1167,7 +1171,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
     if (p >= 0) {
 #pragma unroll
       for (int j = 0; j < SLW; ++j)
-        if (wv + kPlaneWaves * j < W) fetch_cols(p, j);
+        if (wv + kWaves * j < W) fetch_cols(p, j);
     }
     for (uint32_t k = k0; p >= 0; k += walk.per_group) {
       const PlaneId id = plane_id(a, p);
@@ -1178,7 +1182,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
       // ---- H axis: registers -> LDS; then fetch the next plane's columns
 #pragma unroll
       for (int j = 0; j < SLW; ++j) {
-        const int w = wv + kPlaneWaves * j;
+        const int w = wv + kWaves * j;
         if (w >= W) break;
         f32x4 acc[4][FH::MT];
         typename FH::vec ahi[FH::MT][FH::KSTEPS], alo[FH::MT][FH::KSTEPS];
@@ -1199,7 +1203,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
       // ---- W axis: LDS -> epilogue; a wave owns the columns of one kh ----
 #pragma unroll
       for (int r = 0; r < SLH; ++r) {
-        const int kh = wv + kPlaneWaves * r;
+        const int kh = wv + kWaves * r;
         if (kh >= H) break;
         float xv[4][FW::KSTEPS][FW::KV];
 #pragma unroll
@@ -1259,7 +1263,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
       const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.plane_off + id.u * a.n_bins, 4 * a.n_bins);
 #pragma unroll
       for (int q = 0; q < SLH; ++q) {
-        const int kh = wv + kPlaneWaves * q;
+        const int kh = wv + kWaves * q;
         const bool ok = kh < H && lane < W;
         const int bin = static_cast<int>(bin_of3(id, kh, lane));
         const int vb = ok ? bin : kPastBuffer, vw = ok ? 4 * bin : kPastBuffer;
@@ -1288,7 +1292,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
     };
     // Largest gain of a coded bin of the plane, per wave, for the scaling of
     // both stages; written one plane ahead, slot = plane count parity
-    __shared__ float s_gmax[2][kPlaneWaves];
+    __shared__ float s_gmax[2][kWaves];
     auto gain_max = [&]() {
       float m = 0.f;
 #pragma unroll
@@ -1316,7 +1320,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
       // The H-stage outputs are then 2^12 2^-17 2^(25 - e) y = 2^(20 - e) y.
       float gmax = 0.f;
 #pragma unroll
-      for (int w8 = 0; w8 < kPlaneWaves; ++w8) gmax = fmaxf(gmax, s_gmax[it & 1][w8]);
+      for (int w8 = 0; w8 < kWaves; ++w8) gmax = fmaxf(gmax, s_gmax[it & 1][w8]);
       int e = 0;
       if (gmax > 0.f) frexpf(gmax, &e);
       e = e < -100 ? -100 : e;
@@ -1338,7 +1342,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
       // drain during the next W stage.
 #pragma unroll
       for (int q = 0; q < SLH; ++q) {
-        const int kh = wv + kPlaneWaves * q;
+        const int kh = wv + kWaves * q;
         if (kh >= H) break;
         uint4* st = reinterpret_cast<uint4*>(plane + static_cast<int64_t>(kh) * RW * 64);
         // lanes W..NPW-1 read nothing and stage an empty bin
@@ -1361,7 +1365,7 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
       for (int q = 0; q < SLH; ++q) {
-        const int kh = wv + kPlaneWaves * q;
+        const int kh = wv + kWaves * q;
         if (kh >= H) break;
         float* row = plane + static_cast<int64_t>(kh) * RW * 64;
         const uint4* st = reinterpret_cast<const uint4*>(row);
@@ -1468,8 +1472,8 @@ __global__ __launch_bounds__(64 * kPlaneWaves) void k_plane(PlaneArgs a) {
       // column W - 1 and stored through an empty buffer (dropped).
 #pragma unroll
       for (int j = 0; j < SLW; ++j) {
-        const bool wok = wv + kPlaneWaves * j < W;
-        const int w = wok ? wv + kPlaneWaves * j : W - 1;
+        const bool wok = wv + kWaves * j < W;
+        const int w = wok ? wv + kWaves * j : W - 1;
         const __amdgpu_buffer_rsrc_t rout =
             make_rsrc(a.out + id.vol, wok ? static_cast<int64_t>(row_bytes) * H : 0);
         float xv[4][FH::KSTEPS][FH::KV];
@@ -1984,7 +1988,9 @@ void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in,
   a.plane_off = plane_off;
   a.n_units = n_units;
   const int64_t n_planes = n_units * g.S * (a.C / 64);
-  const dim3 block(64 * kPlaneWaves);
+  const int span = g.H > g.W ? g.H : g.W;
+  const int waves = (mode == MODE_DEQUANT && span > 16 && span <= 24) ? kDecodeWaves : kPlaneWaves;
+  const dim3 block(64 * waves);
   const bool h16 = g.H <= 16, w16 = g.W <= 16;
   // the decode pass pads rows shorter than its staging (80 bytes per bin of
   // the 16 or 32 K rows)
@@ -1996,18 +2002,18 @@ void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in,
   const size_t lds = static_cast<size_t>(g.H) * rw * 64 * sizeof(float);
   // the plane needs more dynamic LDS than the default limit
   // persistent grid: as many blocks as the device holds at once
-#define TACT_PLANE_ONE(NH, NW, M, SL)                                                           \
+#define TACT_PLANE_ONE(NH, NW, M, SL, WV)                                                       \
   do {                                                                                          \
-    const void* fn = reinterpret_cast<const void*>(&k_plane<NH, NW, M, SL>);                    \
+    const void* fn = reinterpret_cast<const void*>(&k_plane<NH, NW, M, SL, WV>);                \
     (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,                   \
                               static_cast<int>(lds));                                           \
-    const dim3 grid(static_cast<unsigned>(xcd_grid(persistent_blocks(fn, 64 * kPlaneWaves, lds, n_planes)))); \
-    hipLaunchKernelGGL((k_plane<NH, NW, M, SL>), grid, block, lds, s, a);                       \
+    const dim3 grid(static_cast<unsigned>(xcd_grid(persistent_blocks(fn, 64 * waves, lds, n_planes)))); \
+    hipLaunchKernelGGL((k_plane<NH, NW, M, SL, WV>), grid, block, lds, s, a);                   \
   } while (0)
 #define TACT_PLANE_SL(NH, NW, SL)                                                               \
   do {                                                                                          \
-    if (mode == MODE_STATS) TACT_PLANE_ONE(NH, NW, MODE_STATS, SL);                             \
-    else TACT_PLANE_ONE(NH, NW, MODE_DEQUANT, SL);                                              \
+    if (mode == MODE_STATS) TACT_PLANE_ONE(NH, NW, MODE_STATS, SL, kPlaneWaves);                \
+    else TACT_PLANE_ONE(NH, NW, MODE_DEQUANT, SL, kPlaneWaves);                                 \
   } while (0)
 #define TACT_PLANE(NH, NW)                                                                      \
   do {                                                                                          \
@@ -2015,8 +2021,12 @@ void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in,
     else if (slots == 3) TACT_PLANE_SL(NH, NW, 3);                                              \
     else TACT_PLANE_SL(NH, NW, 4);                                                              \
   } while (0)
-  const int slots = ((g.H > g.W ? g.H : g.W) + kPlaneWaves - 1) / kPlaneWaves;
-  if (h16 && w16) TACT_PLANE_SL(16, 16, 2);
+  const int slots = (span + kPlaneWaves - 1) / kPlaneWaves;
+  if (waves == kDecodeWaves) {             // decode, 17..24 rows or columns
+    if (h16) TACT_PLANE_ONE(16, 32, MODE_DEQUANT, 2, kDecodeWaves);
+    else if (w16) TACT_PLANE_ONE(32, 16, MODE_DEQUANT, 2, kDecodeWaves);
+    else TACT_PLANE_ONE(32, 32, MODE_DEQUANT, 2, kDecodeWaves);
+  } else if (h16 && w16) TACT_PLANE_SL(16, 16, 2);
   else if (h16) TACT_PLANE(16, 32);
   else if (w16) TACT_PLANE(32, 16);
   else TACT_PLANE(32, 32);
