@@ -233,7 +233,7 @@ void compress_chunk(const Geometry& g, int64_t cn, const void* kv, int64_t kv_st
                 nullptr, nullptr, 0, none, nullptr, s, /*rot_in=*/false, /*rot_out=*/true);
     launch_plane(g, cn, 0, w.coef, w.coef, g.n_entries, w.tab, w.var, vs, none, nullptr, s);
     launch_allocate2(g, cn, w.var, vs, static_cast<int>(var_parts(g)), inv_d, nullptr,
-                     view(g, recs), w.poff, w.invg, s);
+                     view(g, recs), w.poff, w.invg, s, /*planes=*/true);
     launch_quant(g, cn, w.coef, g.n_entries, w.invg, vs, view(g, recs), w.poff, s);
     return;
   }

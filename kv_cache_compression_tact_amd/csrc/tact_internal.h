@@ -93,10 +93,13 @@ void launch_axis(const Geometry& g, int64_t n_units, int axis, int inverse, int 
 
 // Allocation by exact radix selection; writes bits_out and/or the record
 // header, and per-bin first planes into plane_off (each may be null).
-// var holds `parts` partial sums per bin (consecutive), scaled by var_scale.
+// var holds `parts` partial sums per bin, scaled by var_scale: consecutive
+// per bin, or (planes) stored plane by plane as the plane pass writes them,
+// [slab][s][kh][kw] per unit.
 void launch_allocate2(const Geometry& g, int64_t n_units, const float* var, int64_t var_stride,
                       int parts, float var_scale, uint8_t* bits_out, RecordView rec,
-                      uint32_t* plane_off, float* inv_gain, hipStream_t stream);
+                      uint32_t* plane_off, float* inv_gain, hipStream_t stream,
+                      bool planes = false);
 
 // Fused H and W axes (see tact_mfma.hip); mode 0 = forward: coefficients
 // to `out` (may equal `in`) and variance partial sums; 2 = decode + inverse.

@@ -839,7 +839,8 @@ struct PlaneArgs {
   int head_dim, kv_heads;
   int64_t n_bins, total_bits;
   int max_bits;
-  float* var_part;           // MODE_STATS: raw sums of squares, [u][bin][part]
+  float* var_part;           // MODE_STATS: raw sums of squares per plane,
+                             // [u][slab][s][kh][kw] (slab = 64-channel word)
   int parts;                 // head_dim / 64
   int64_t var_stride;        // floats per unit in var_part
   RecordView rec;
@@ -1220,9 +1221,10 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
         frag_from_lds<NPW>(s_fw, lane, bhi_w, blo_w);
         contract4<NPW>(bhi_w, blo_w, xv, acc, kOne);
         {
-          // partial sums of bin (s, kh, kw, head): kw steps kv_heads * parts
-          float* vrow = a.var_part + id.u * a.var_stride + bin_of3(id, kh, 0) * a.parts + id.half;
-          const int kw_step = a.kv_heads * a.parts;
+          // partial sums of bin (s, kh, kw, head), plane by plane: a row's
+          // sums are adjacent
+          float* vrow = a.var_part + id.u * a.var_stride +
+                        ((id.c0 / 64 * a.S + id.s) * static_cast<int64_t>(H) + kh) * W;
           // the final coefficients go back over this plane's input
           const int vo = (kh * W + 4 * g) * cbytes + static_cast<int>(id.c0 + 4 * t) * 4;
 #pragma unroll
@@ -1234,7 +1236,7 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
               for (int i = 0; i < 4; ++i) sq = fmaf(acc[i][m][rr], acc[i][m][rr], sq);
               sq = row_sum16(sq);
               const int kw = 16 * m + 4 * g + rr;
-              if (t == 0 && kw < W) vrow[kw * kw_step] = sq;
+              if (t == 0 && kw < W) vrow[kw] = sq;
               if (kw < W)
                 buf_st4(rcoef, vo, (16 * m + rr) * cbytes,
                         float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
@@ -1629,17 +1631,52 @@ __device__ __forceinline__ void var4(const float* v, int64_t nb, int parts, floa
   for (int j = 0; j < 4; ++j) out[j] *= scale;
 }
 
-// Calls f(i, v_i) for the bins of one unit, 4 consecutive bins per thread
-// per step.
+// Partial sums stored plane by plane: [slab][position], slab = head * parts
+// + part, position = bin / kv_heads (the bin is position * kv_heads + head).
+// The variance adds the parts in part order, as var4 does.
+struct VarView {
+  const float* v;
+  int64_t nb, npos;
+  int parts, kv;
+  bool planes, vec;
+  __device__ __forceinline__ float at(int h, int64_t pos, float scale) const {
+    const float* q = v + static_cast<int64_t>(h) * parts * npos + pos;
+    float acc = q[0];
+    for (int p = 1; p < parts; ++p) acc += q[p * npos];
+    return acc * scale;
+  }
+};
+
+// Calls f(v_i) for every bin of one unit, in no particular order: 4
+// consecutive entries per thread per step, in the order of the storage.
 template <typename Fn>
-__device__ __forceinline__ void for_bins4(const float* v, int64_t nb, int parts, float scale,
-                                          Fn f) {
-  const bool vec = (reinterpret_cast<uintptr_t>(v) & 15) == 0;
-  for (int64_t i0 = 4 * static_cast<int64_t>(threadIdx.x); i0 < nb; i0 += 4 * blockDim.x) {
-    float q[4];
-    var4(v, nb, parts, scale, vec, i0, q);
-    for (int j = 0; j < 4; ++j)
-      if (i0 + j < nb) f(i0 + j, q[j]);
+__device__ __forceinline__ void for_bins4(const VarView& vv, float scale, Fn f) {
+  const int64_t nb = vv.nb;
+  if (!vv.planes) {
+    for (int64_t i0 = 4 * static_cast<int64_t>(threadIdx.x); i0 < nb; i0 += 4 * blockDim.x) {
+      float q[4];
+      var4(vv.v, nb, vv.parts, scale, vv.vec, i0, q);
+      for (int j = 0; j < 4; ++j)
+        if (i0 + j < nb) f(q[j]);
+    }
+    return;
+  }
+  // head by head, positions in storage order
+  if (vv.vec && (vv.npos & 3) == 0) {
+    for (int h = 0; h < vv.kv; ++h) {
+      const float* q = vv.v + static_cast<int64_t>(h) * vv.parts * vv.npos;
+      for (int64_t pos = 4 * static_cast<int64_t>(threadIdx.x); pos < vv.npos; pos += 4 * blockDim.x) {
+        float4 acc = *reinterpret_cast<const float4*>(q + pos);
+        for (int p = 1; p < vv.parts; ++p) {
+          const float4 r = *reinterpret_cast<const float4*>(q + p * vv.npos + pos);
+          acc.x += r.x; acc.y += r.y; acc.z += r.z; acc.w += r.w;
+        }
+        f(acc.x * scale); f(acc.y * scale); f(acc.z * scale); f(acc.w * scale);
+      }
+    }
+  } else {
+    for (int h = 0; h < vv.kv; ++h)
+      for (int64_t pos = threadIdx.x; pos < vv.npos; pos += blockDim.x) f(vv.at(h, pos, scale));
   }
 }
 
@@ -1655,12 +1692,22 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
                                                              RecordView rec,
                                                              uint32_t* __restrict__ plane_off,
                                                              float* __restrict__ inv_gain,
-                                                             int parts, float var_scale) {
+                                                             int parts, float var_scale,
+                                                             int planes) {
   __shared__ uint32_t hist[4096];
+  __shared__ float s_var[4 * kAllocThreads];   // one chunk of variances, bin order
   __shared__ int sh[kAllocThreads / kWave];
   __shared__ long long sh64[kAllocThreads / kWave];
   const int64_t u = blockIdx.x;
   const float* v = var + u * var_stride;
+  VarView vv;
+  vv.v = v;
+  vv.nb = g.n_bins;
+  vv.npos = static_cast<int64_t>(g.S) * g.H * g.W;
+  vv.parts = parts;
+  vv.kv = g.kv_heads;
+  vv.planes = planes != 0;
+  vv.vec = (reinterpret_cast<uintptr_t>(v) & 15) == 0;
   const int bmax = g.max_bits;
   const int64_t T = g.total_bits;
   const int64_t nb = g.n_bins;
@@ -1673,7 +1720,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
     // ---- sweep 1: exponent of the T-th largest gain --------------------
     for (int j = threadIdx.x; j < 4096; j += blockDim.x) hist[j] = 0;
     __syncthreads();
-    for_bins4(v, nb, parts, var_scale, [&](int64_t, float x) { atomicAdd(&hist[gain_key(x) >> 52], 1u); });
+    for_bins4(vv, var_scale, [&](float x) { atomicAdd(&hist[gain_key(x) >> 52], 1u); });
     __syncthreads();
     // gains per exponent e: bins with E in {e, e+2, ..., e+2(bmax-1)} (E > 0);
     // all bmax gains of zero bins sit at e = 0
@@ -1699,7 +1746,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
       // ---- sweep 2: top 12 mantissa bits among gains with exponent ebin --
       for (int j = threadIdx.x; j < 4096; j += blockDim.x) hist[j] = 0;
       __syncthreads();
-      for_bins4(v, nb, parts, var_scale, [&](int64_t, float x) {
+      for_bins4(vv, var_scale, [&](float x) {
         const uint64_t key = gain_key(x);
         if (has_gain_at(static_cast<int>(key >> 52), ebin, bmax))
           atomicAdd(&hist[(key >> 40) & 0xFFF], 1u);
@@ -1711,7 +1758,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
       // ---- sweep 3: next 11 mantissa bits ---------------------------------
       for (int j = threadIdx.x; j < 4096; j += blockDim.x) hist[j] = 0;
       __syncthreads();
-      for_bins4(v, nb, parts, var_scale, [&](int64_t, float x) {
+      for_bins4(vv, var_scale, [&](float x) {
         const uint64_t key = gain_key(x);
         if (has_gain_at(static_cast<int>(key >> 52), ebin, bmax) &&
             static_cast<int>((key >> 40) & 0xFFF) == b2)
@@ -1725,7 +1772,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
             (static_cast<uint64_t>(b3) << 29);
     }
     int64_t gt = 0, eq = 0;
-    for_bins4(v, nb, parts, var_scale, [&](int64_t, float x) {
+    for_bins4(vv, var_scale, [&](float x) {
       const uint64_t key = gain_key(x);
       const int a1 = count_ge(key, tau + 1, bmax);
       gt += a1;
@@ -1742,12 +1789,28 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
   uint8_t* bo = bits_out ? bits_out + u * nb : nullptr;
   uint8_t* r = rec.base ? rec.base + u * rec.stride : nullptr;
   uint32_t* po = plane_off ? plane_off + u * nb : nullptr;
-  const bool vec = (reinterpret_cast<uintptr_t>(v) & 15) == 0;
   int64_t tie_carry = 0, plane_carry = 0;
   for (int64_t base = 0; base < nb; base += 4 * blockDim.x) {
     const int64_t i0 = base + 4 * static_cast<int64_t>(threadIdx.x);
     float vi[4];
-    var4(v, nb, parts, var_scale, vec, i0, vi);
+    if (vv.planes) {
+      // the chunk's variances into LDS in bin order, read position by
+      // position (consecutive threads, consecutive positions of one head)
+      const int64_t end = base + 4 * blockDim.x < nb ? base + 4 * blockDim.x : nb;
+      const int64_t pos_lo = base / vv.kv;
+      const uint32_t np = static_cast<uint32_t>((end - 1) / vv.kv - pos_lo + 1);
+      __syncthreads();                       // the previous chunk is read
+      for (uint32_t e = threadIdx.x; e < static_cast<uint32_t>(vv.kv) * np; e += blockDim.x) {
+        const uint32_t h = e / np;
+        const int64_t pos = pos_lo + (e - h * np);
+        const int64_t i = pos * vv.kv + h;
+        if (i >= base && i < end) s_var[i - base] = vv.at(static_cast<int>(h), pos, var_scale);
+      }
+      __syncthreads();
+      for (int j = 0; j < 4; ++j) vi[j] = i0 + j < nb ? s_var[4 * threadIdx.x + j] : 0.f;
+    } else {
+      var4(v, nb, parts, var_scale, vv.vec, i0, vi);
+    }
     int b[4] = {0, 0, 0, 0}, eqv[4] = {0, 0, 0, 0};
     int eq_sum = 0;
     for (int j = 0; j < 4; ++j) {
@@ -2037,9 +2100,10 @@ void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in,
 
 void launch_allocate2(const Geometry& g, int64_t n_units, const float* var, int64_t var_stride,
                       int parts, float var_scale, uint8_t* bits_out, RecordView rec,
-                      uint32_t* plane_off, float* inv_gain, hipStream_t s) {
+                      uint32_t* plane_off, float* inv_gain, hipStream_t s, bool planes) {
   hipLaunchKernelGGL(k_allocate2, dim3(static_cast<unsigned>(n_units)), dim3(kAllocThreads), 0, s,
-                     g, var, var_stride, bits_out, rec, plane_off, inv_gain, parts, var_scale);
+                     g, var, var_stride, bits_out, rec, plane_off, inv_gain, parts, var_scale,
+                     planes ? 1 : 0);
 }
 
 void launch_plane_offsets(const Geometry& g, int64_t n_units, RecordView rec, uint32_t* plane_off,
