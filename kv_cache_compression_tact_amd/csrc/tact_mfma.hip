@@ -1307,6 +1307,14 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
       fetch_words(p);
       const float m = gain_max();
       if (lane == 0) s_gmax[0][wv] = m;
+      // As many stores as the H stage issues, through an empty buffer (all
+      // dropped): the loop is entered with the same number of memory
+      // operations after the code-word loads as its back edge carries, so
+      // the compiler's wait for those loads at the loop top counts the
+      // stores instead of waiting for them.
+      const __amdgpu_buffer_rsrc_t none = make_rsrc(a.out, 0);
+#pragma unroll
+      for (int j = 0; j < SLW * FH::MT * 4; ++j) buf_st4(none, 0, 0, float4{0.f, 0.f, 0.f, 0.f});
     }
     __syncthreads();
     for (uint32_t k = k0, it = 0; p >= 0; k += walk.per_group, ++it) {
