@@ -1671,15 +1671,35 @@ __device__ __forceinline__ void for_bins4(const VarView& vv, float scale, Fn f) 
   }
   // head by head, positions in storage order
   if (vv.vec && (vv.npos & 3) == 0) {
+    // four groups of 4 positions per thread per step, all loads first (the
+    // sweep is otherwise one load latency per group); indices past the end
+    // are clamped and their values unused
+    const int64_t n4 = vv.npos / 4;
     for (int h = 0; h < vv.kv; ++h) {
-      const float* q = vv.v + static_cast<int64_t>(h) * vv.parts * vv.npos;
-      for (int64_t pos = 4 * static_cast<int64_t>(threadIdx.x); pos < vv.npos; pos += 4 * blockDim.x) {
-        float4 acc = *reinterpret_cast<const float4*>(q + pos);
-        for (int p = 1; p < vv.parts; ++p) {
-          const float4 r = *reinterpret_cast<const float4*>(q + p * vv.npos + pos);
-          acc.x += r.x; acc.y += r.y; acc.z += r.z; acc.w += r.w;
+      const float4* q = reinterpret_cast<const float4*>(vv.v + static_cast<int64_t>(h) * vv.parts * vv.npos);
+      for (int64_t g0 = threadIdx.x; g0 < n4; g0 += 4 * static_cast<int64_t>(blockDim.x)) {
+        float4 x0[4], x1[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          int64_t g = g0 + u * static_cast<int64_t>(blockDim.x);
+          g = g < n4 ? g : n4 - 1;
+          x0[u] = q[g];
+          x1[u] = vv.parts > 1 ? q[n4 + g] : float4{0.f, 0.f, 0.f, 0.f};
         }
-        f(acc.x * scale); f(acc.y * scale); f(acc.z * scale); f(acc.w * scale);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t g = g0 + u * static_cast<int64_t>(blockDim.x);
+          if (g >= n4) break;
+          float4 acc = x0[u];
+          if (vv.parts > 1) {
+            acc.x += x1[u].x; acc.y += x1[u].y; acc.z += x1[u].z; acc.w += x1[u].w;
+          }
+          for (int p = 2; p < vv.parts; ++p) {
+            const float4 r = q[p * n4 + g];
+            acc.x += r.x; acc.y += r.y; acc.z += r.z; acc.w += r.w;
+          }
+          f(acc.x * scale); f(acc.y * scale); f(acc.z * scale); f(acc.w * scale);
+        }
       }
     }
   } else {
