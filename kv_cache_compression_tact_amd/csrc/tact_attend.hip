@@ -131,22 +131,33 @@ __global__ __launch_bounds__(256) void k_att_proj(AttArgs a) {
       wl[k] = static_cast<uint32_t>(w);
       wh[k] = static_cast<uint32_t>(w >> 32);
     }
-#pragma unroll 8
-    for (int jj = 0; jj < 64; ++jj) {
-      uint32_t code = 0;
+    // channels in groups of 4: each plane gives a nibble, spread into one
+    // byte per channel (byte i of `codes` collects channel 4 t4 + i; the
+    // spread stays a 24-bit multiply)
+#pragma unroll 4
+    for (int t4 = 0; t4 < 16; ++t4) {
+      uint32_t codes = 0;
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (k < bw) code |= __builtin_amdgcn_ubfe(jj < 32 ? wl[k] : wh[k], jj & 31, 1) << k;
-      const float val = s_lv[base + static_cast<int>(code)];
-      const float4* qc = reinterpret_cast<const float4*>(s_qt + (64 * hw + jj) * kMaxRep);
+        if (k < bw) {
+          uint32_t sp = __builtin_amdgcn_ubfe(t4 < 8 ? wl[k] : wh[k], (4 * t4) & 31, 4) * 0x204081u;
+          asm("" : "+v"(sp));
+          codes |= (sp & 0x01010101u) << k;
+        }
 #pragma unroll
-      for (int r4 = 0; r4 < kMaxRep / 4; ++r4) {
-        if (r4 >= n4) break;
-        const float4 qv = qc[r4];
-        acc[4 * r4 + 0] = fmaf(val, qv.x, acc[4 * r4 + 0]);
-        acc[4 * r4 + 1] = fmaf(val, qv.y, acc[4 * r4 + 1]);
-        acc[4 * r4 + 2] = fmaf(val, qv.z, acc[4 * r4 + 2]);
-        acc[4 * r4 + 3] = fmaf(val, qv.w, acc[4 * r4 + 3]);
+      for (int i = 0; i < 4; ++i) {
+        const int jj = 4 * t4 + i;
+        const float val = s_lv[base + static_cast<int>((codes >> (8 * i)) & 0xFFu)];
+        const float4* qc = reinterpret_cast<const float4*>(s_qt + (64 * hw + jj) * kMaxRep);
+#pragma unroll
+        for (int r4 = 0; r4 < kMaxRep / 4; ++r4) {
+          if (r4 >= n4) break;
+          const float4 qv = qc[r4];
+          acc[4 * r4 + 0] = fmaf(val, qv.x, acc[4 * r4 + 0]);
+          acc[4 * r4 + 1] = fmaf(val, qv.y, acc[4 * r4 + 1]);
+          acc[4 * r4 + 2] = fmaf(val, qv.z, acc[4 * r4 + 2]);
+          acc[4 * r4 + 3] = fmaf(val, qv.w, acc[4 * r4 + 3]);
+        }
       }
     }
   }
