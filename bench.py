@@ -151,6 +151,7 @@ def bench_ablations(args, tact, wl, budget, g, x):
         "2-axis DCT (H, W)": {"axes": tact.AXIS_H | tact.AXIS_W},
         "2-axis DCT (S, W)": {"axes": tact.AXIS_S | tact.AXIS_W},
         "1-axis DCT (S)": {"axes": tact.AXIS_S},
+        "no transform": {"axes": tact.AXES_NONE},
         "uniform allocation": {"alloc_mode": tact.ALLOC_UNIFORM},
         "no rotation": {"rotation": tact.ROTATION_NONE},
         "symmetric uniform quantizer": {"quantizer": tact.QUANT_UNIFORM},

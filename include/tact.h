@@ -74,8 +74,9 @@ typedef enum {
 typedef enum { TACT_BF16 = 0, TACT_F32 = 1 } tact_dtype;
 
 /* Transform axes (bit mask); the method transforms all three.  Subsets are
- * the transform ablation of the page's "Main Findings". */
-enum { TACT_AXIS_S = 1, TACT_AXIS_H = 2, TACT_AXIS_W = 4, TACT_AXES_ALL = 7 };
+ * the transform ablation of the page's "Main Findings"; 0 (TACT_AXES_NONE)
+ * codes the tokens without a transform (each bin is one token of one head). */
+enum { TACT_AXES_NONE = 0, TACT_AXIS_S = 1, TACT_AXIS_H = 2, TACT_AXIS_W = 4, TACT_AXES_ALL = 7 };
 
 /* Allocation mode: 0 = reverse water-filling (the method); 1 = uniform, every
  * bin budget_bits planes (the page's "uniform allocation" ablation). */
@@ -112,7 +113,7 @@ typedef struct {
   int32_t budget_bits;  /* average code bits per entry, 0..max_bits          */
   int32_t max_bits;     /* per-bin cap, 1..8 (the page caps at 8)            */
   int32_t dtype;        /* tact_dtype of the cache tensors (in == out)       */
-  int32_t axes;         /* TACT_AXES_ALL, or a non-empty subset              */
+  int32_t axes;         /* TACT_AXES_ALL, a subset, or TACT_AXES_NONE        */
   int32_t alloc_mode;   /* TACT_ALLOC_WATERFILL or TACT_ALLOC_UNIFORM        */
   int32_t rotation;     /* TACT_ROTATION_HADAMARD or TACT_ROTATION_NONE      */
   int32_t quantizer;    /* TACT_QUANT_LLOYD_MAX, _UNIFORM or _NF             */

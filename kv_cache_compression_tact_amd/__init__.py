@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libtact.so")
 TACT_OK, TACT_ERR_INVALID_ARGUMENT, TACT_ERR_UNSUPPORTED, TACT_ERR_WORKSPACE, \
     TACT_ERR_HIP = range(5)
 TACT_BF16, TACT_F32 = 0, 1
-AXIS_S, AXIS_H, AXIS_W, AXES_ALL = 1, 2, 4, 7
+AXES_NONE, AXIS_S, AXIS_H, AXIS_W, AXES_ALL = 0, 1, 2, 4, 7
 ALLOC_WATERFILL, ALLOC_UNIFORM = 0, 1
 ROTATION_NONE, ROTATION_HADAMARD = 0, 1
 QUANT_LLOYD_MAX, QUANT_UNIFORM, QUANT_NF = 0, 1, 2

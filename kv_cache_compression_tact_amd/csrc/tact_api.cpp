@@ -55,9 +55,8 @@ tact_status make_geometry(const tact_params* p, Geometry* g) {
                 p->budget_bits, p->max_bits);
   if (p->dtype != TACT_BF16 && p->dtype != TACT_F32)
     return fail(TACT_ERR_INVALID_ARGUMENT, "dtype=%d: must be TACT_BF16 or TACT_F32", p->dtype);
-  if (!in(p->axes, 1, 7))
-    return fail(TACT_ERR_INVALID_ARGUMENT, "axes=%d: must be a non-empty subset of S|H|W",
-                p->axes);
+  if (!in(p->axes, 0, 7))
+    return fail(TACT_ERR_INVALID_ARGUMENT, "axes=%d: must be a subset of S|H|W", p->axes);
   if (p->alloc_mode != TACT_ALLOC_WATERFILL && p->alloc_mode != TACT_ALLOC_UNIFORM)
     return fail(TACT_ERR_INVALID_ARGUMENT, "alloc_mode=%d: must be 0 or 1", p->alloc_mode);
   if (p->rotation != TACT_ROTATION_NONE && p->rotation != TACT_ROTATION_HADAMARD)
@@ -205,11 +204,14 @@ RecordView view(const Geometry& g, void* base) {
   return r;
 }
 
-// Transform axes in forward order (S, H, W) restricted to the mask.
+// Transform axes in forward order (S, H, W) restricted to the mask.  With no
+// axis the S pass runs with the identity matrix in place of the DCT (the
+// tables kernel writes it for axes == 0), so coding needs no separate path.
 int forward_axes(const Geometry& g, int* ax) {
   int m = 0;
   for (int a = 0; a < 3; ++a)
     if (g.axes & (1 << a)) ax[m++] = a;
+  if (m == 0) ax[m++] = 0;
   return m;
 }
 

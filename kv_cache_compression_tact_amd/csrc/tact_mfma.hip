@@ -50,16 +50,21 @@ constexpr float kLevelScale = 2048.0f;
 // ---------------------------------------------------------------------------
 // DCT-II matrices of the three axes, fp32, zero padded to 64 x 64:
 // tab[a][k][n] = a_k cos(pi (2n+1) k / 2N_a), a_0 = sqrt(1/N), a_k = sqrt(2/N).
+// With identity0 the S table is the identity instead (no-transform coding).
 // ---------------------------------------------------------------------------
-__global__ void k_dct_tables(float* __restrict__ tab, int n0, int n1, int n2) {
+__global__ void k_dct_tables(float* __restrict__ tab, int n0, int n1, int n2, int identity0) {
   const int a = blockIdx.x;
   const int N = a == 0 ? n0 : (a == 1 ? n1 : n2);
   for (int e = threadIdx.x; e < 64 * 64; e += blockDim.x) {
     const int k = e / 64, n = e % 64;
     float v = 0.f;
     if (k < N && n < N) {
-      const double al = (k == 0) ? sqrt(1.0 / N) : sqrt(2.0 / N);
-      v = static_cast<float>(al * cospi((2.0 * n + 1.0) * k / (2.0 * N)));
+      if (a == 0 && identity0) {
+        v = k == n ? 1.f : 0.f;
+      } else {
+        const double al = (k == 0) ? sqrt(1.0 / N) : sqrt(2.0 / N);
+        v = static_cast<float>(al * cospi((2.0 * n + 1.0) * k / (2.0 * N)));
+      }
     }
     tab[a * 4096 + e] = v;
   }
@@ -1978,7 +1983,7 @@ void launch_axis_np(const AxisArgs& a, int pro, int epi, int tpw, hipStream_t s)
 // host-facing launchers (declared in tact_internal.h)
 // ---------------------------------------------------------------------------
 void launch_dct_tables(const Geometry& g, float* tab, hipStream_t s) {
-  hipLaunchKernelGGL(k_dct_tables, dim3(3), dim3(256), 0, s, tab, g.S, g.H, g.W);
+  hipLaunchKernelGGL(k_dct_tables, dim3(3), dim3(256), 0, s, tab, g.S, g.H, g.W, g.axes == 0 ? 1 : 0);
 }
 
 // axis: 0 = S, 1 = H, 2 = W

@@ -58,7 +58,7 @@ def test_record_bytes_matches_layout():
 @pytest.mark.parametrize("field,value,status", [
     ("S", 0, 2), ("H", 65, 2), ("W", -1, 2), ("kv_heads", 0, 2), ("head_dim", 96, 2),
     ("max_bits", 0, 1), ("max_bits", 9, 1), ("budget_bits", 9, 1), ("budget_bits", -1, 1),
-    ("dtype", 5, 1), ("axes", 0, 1), ("axes", 8, 1), ("alloc_mode", 2, 1),
+    ("dtype", 5, 1), ("axes", -1, 1), ("axes", 8, 1), ("alloc_mode", 2, 1),
     ("rotation", 2, 1), ("rotation", -1, 1),
 ])
 def test_invalid_params_rejected(field, value, status):
@@ -69,6 +69,13 @@ def test_invalid_params_rejected(field, value, status):
     st = lib().tact_compress(ctypes.byref(p), 1, fake, 32768, fake, fake, 1 << 30, None)
     assert st == status
     assert len(lib().tact_last_error()) > 0
+
+
+def test_no_transform_axes_accepted():
+    # axes = 0: the no-transform ablation (tokens coded as they are)
+    p = _params(axes=0)
+    assert lib().tact_record_bytes(ctypes.byref(p)) == lib().tact_record_bytes(ctypes.byref(_params()))
+    assert lib().tact_workspace_bytes(ctypes.byref(p), 4) > 0
 
 
 def test_unit_size_cap():

@@ -118,12 +118,13 @@ def test_attend_quantizer_backends(quant):
         assert np.max(np.abs(o[r] - o_ref[r])) <= 1e-4 * vrms * (1 + abs(l_ref[r]))
 
 
-def test_attend_axis_subset():
-    # records coded with two of the three axes: the field transforms follow
+@pytest.mark.parametrize("axes", [(0, 2), ()])
+def test_attend_axis_subset(axes):
+    # records coded with two of the three axes, or with none: the field
+    # transforms follow
     S, H, W, hk, d = 6, 5, 7, 2, 64
     p = O.Params(S, H, W, hk, d, 2, 8)
-    g = tact.Geometry(S, H, W, hk, d, 2, axes=tact.AXIS_S | tact.AXIS_W)
-    axes = (0, 2)
+    g = tact.Geometry(S, H, W, hk, d, 2, axes=sum(1 << a for a in axes))
     krec = O.compress(_field(p.shape, 3), p, axes=axes)[None]
     vrec = O.compress(_field(p.shape, 4), p, axes=axes)[None]
     q = np.random.default_rng(8).standard_normal((1, 4, d)).astype(np.float32)

@@ -116,7 +116,7 @@ GEOMS_AXIS_PATH = [
 ]
 
 
-@pytest.mark.parametrize("axes", [1, 2, 4, 3, 6, 5])
+@pytest.mark.parametrize("axes", [1, 2, 4, 3, 6, 5, 0])
 def test_dct_axis_subsets(axes):
     g = _geom(5, 6, 7, 2, 64, 1, axes=axes)
     say("dct axes", axes)
@@ -389,9 +389,10 @@ def test_rotation_spreads_a_spike_channel():
     assert e[1] < 0.1 * e[0]
 
 
-@pytest.mark.parametrize("axes", [1, 2, 4, 3, 5, 6])
+@pytest.mark.parametrize("axes", [1, 2, 4, 3, 5, 6, 0])
 def test_roundtrip_axis_subsets(axes):
-    # the page's transform ablation: 1- and 2-axis DCTs through the codec
+    # the page's transform ablation: 1- and 2-axis DCTs, and no transform
+    # (axes 0), through the codec
     g = _geom(5, 7, 9, 2, 64, 2, axes=axes)
     say("roundtrip axes", axes)
     _roundtrip_check(_units(g, 2, seed=11), g)
