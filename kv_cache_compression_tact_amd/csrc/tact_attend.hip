@@ -34,6 +34,12 @@ namespace tact {
 namespace {
 
 constexpr int kWave = 64;
+// raw buffer descriptor (gfx9 word 3): loads past its byte range return 0
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kPastBuffer = 0x7FFFFFF0;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t att_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufWord3);
+}
 constexpr int kMaxRep = 16;       // query heads per kv head
 constexpr int kChunk = 256;       // bins per wave in k_att_out
 constexpr int kFieldThreads = 512;
@@ -286,27 +292,49 @@ __global__ __launch_bounds__(kWave) void k_att_out(AttArgs a) {
     for (int hw = 0; hw < WPP; ++hw) acc[r][hw] = 0.f;
   const int f_end = min(a.shw, (chunk + 1) * kChunk);
   for (int f0 = chunk * kChunk; f0 < f_end; f0 += kWave) {
-    // side info, probabilities and plane words of bins f0 + lane
+    // side info, probabilities and plane words of bins f0 + lane, all
+    // through buffer loads that every lane issues (lanes with nothing to
+    // read take an offset past the buffer and read 0), so one wait covers
+    // each batch
     const int f = f0 + lane;
-    int bj = 0;
-    int64_t pj = 0;
-    float gj = 0.f;
+    const bool ok = f < f_end;
+    const int bin = ok ? f * a.kv_heads + h : 0;
+    const uint8_t* rv = a.vrec.base + pair * a.vrec.stride;
+    int bj = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b8(
+        att_rsrc(rv + a.vrec.off_bits, a.n_bins), ok ? bin : kPastBuffer, 0, 0));
+    const int64_t pj = __builtin_amdgcn_raw_buffer_load_b32(
+        att_rsrc(a.vpoff + pair * a.n_bins, 4 * a.n_bins), ok ? 4 * bin : kPastBuffer, 0, 0);
+    const float gj = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        att_rsrc(rv + a.vrec.off_gains, 4 * a.n_bins), ok ? 4 * bin : kPastBuffer, 0, 0));
     float pr[kMaxRep];
+    const __amdgpu_buffer_rsrc_t rp = att_rsrc(P, 4 * static_cast<int64_t>(a.rep) * a.shw);
 #pragma unroll
-    for (int r = 0; r < kMaxRep; ++r) pr[r] = 0.f;
-    if (f < f_end) {
-      bin_side(a.vrec, a.vpoff, pair, static_cast<int64_t>(f) * a.kv_heads + h, a, bj, pj, gj);
+    for (int r = 0; r < kMaxRep; ++r)
+      pr[r] = r < a.rep ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                              rp, ok ? 4 * (r * a.shw + f) : kPastBuffer, 0, 0))
+                        : 0.f;
+    if (bj > a.max_bits || pj + bj > a.total_bits) bj = 0;
+    // plane k of the bin: WPP consecutive 64-bit words
+    const __amdgpu_buffer_rsrc_t rw = att_rsrc(words, a.total_bits * WPP * 8);
+    uint2 wk[8][WPP];
 #pragma unroll
-      for (int r = 0; r < kMaxRep; ++r)
-        if (r < a.rep) pr[r] = P[static_cast<int64_t>(r) * a.shw + f];
+    for (int k = 0; k < 8; ++k) {
+      const int off = k < bj ? static_cast<int>((pj + k) * WPP * 8) : kPastBuffer;
+      if constexpr (WPP == 1) {
+        wk[k][0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rw, off, 0, 0));
+      } else {
+#pragma unroll
+        for (int q = 0; q < WPP / 2; ++q) {
+          const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 16 * q, 0));
+          wk[k][2 * q] = uint2{v.x, v.y};
+          wk[k][2 * q + 1] = uint2{v.z, v.w};
+        }
+      }
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k)
 #pragma unroll
-      for (int hw = 0; hw < WPP; ++hw) {
-        const uint64_t w = k < bj ? words[(pj + k) * WPP + hw] : 0ull;
-        s_w[lane][k * WPP + hw] = uint2{static_cast<uint32_t>(w), static_cast<uint32_t>(w >> 32)};
-      }
+      for (int hw = 0; hw < WPP; ++hw) s_w[lane][k * WPP + hw] = wk[k][hw];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
