@@ -79,17 +79,6 @@ __global__ void k_att_qrot(AttArgs a) {
   }
 }
 
-// Bin side info of a record, validated: bits 0 for a bin whose planes would
-// fall outside the record.
-__device__ __forceinline__ void bin_side(const RecordView& rv, const uint32_t* poff, int64_t pair,
-                                         int64_t bin, const AttArgs& a, int& b, int64_t& p0, float& g) {
-  const uint8_t* r = rv.base + pair * rv.stride;
-  b = r[rv.off_bits + bin];
-  p0 = poff[pair * a.n_bins + bin];
-  g = reinterpret_cast<const float*>(r + rv.off_gains)[bin];
-  if (b > a.max_bits || p0 + b > a.total_bits) b = 0;
-}
-
 // ---- projections: lane = bin f of kv head h --------------------------------
 // The rotated, scaled queries of the kv head are staged in LDS transposed
 // (channel-major, the query heads of a channel adjacent), so one broadcast
@@ -111,12 +100,17 @@ __global__ __launch_bounds__(256) void k_att_proj(AttArgs a) {
   __syncthreads();
   const int f = blockIdx.x * blockDim.x + threadIdx.x;
   const bool live = f < a.shw;
-  int b = 0;
-  int64_t p0 = 0;
-  float g = 0.f;
-  if (live) bin_side(a.krec, a.kpoff, pair, static_cast<int64_t>(f) * a.kv_heads + h, a, b, p0, g);
-  const uint64_t* words = reinterpret_cast<const uint64_t*>(
-      a.krec.base + pair * a.krec.stride + a.krec.off_codes);
+  // side info through buffer loads every lane issues (past the buffer: 0)
+  const int bin = live ? f * a.kv_heads + h : 0;
+  const uint8_t* rk = a.krec.base + pair * a.krec.stride;
+  int b = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b8(
+      att_rsrc(rk + a.krec.off_bits, a.n_bins), live ? bin : kPastBuffer, 0, 0));
+  const int64_t p0 = __builtin_amdgcn_raw_buffer_load_b32(
+      att_rsrc(a.kpoff + pair * a.n_bins, 4 * a.n_bins), live ? 4 * bin : kPastBuffer, 0, 0);
+  const float g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+      att_rsrc(rk + a.krec.off_gains, 4 * a.n_bins), live ? 4 * bin : kPastBuffer, 0, 0));
+  if (b > a.max_bits || p0 + b > a.total_bits) b = 0;
+  const __amdgpu_buffer_rsrc_t rw = att_rsrc(rk + a.krec.off_codes, a.total_bits * WPP * 8);
   const int base = b > 0 ? (1 << b) - 1 : 0;
   // the largest bit width in the wave bounds the planes read per channel
   int bw = 0;
@@ -133,9 +127,10 @@ __global__ __launch_bounds__(256) void k_att_proj(AttArgs a) {
     uint32_t wl[8], wh[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const uint64_t w = k < b ? words[(p0 + k) * WPP + hw] : 0ull;
-      wl[k] = static_cast<uint32_t>(w);
-      wh[k] = static_cast<uint32_t>(w >> 32);
+      const uint2 w = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+          rw, k < b ? static_cast<int>(((p0 + k) * WPP + hw) * 8) : kPastBuffer, 0, 0));
+      wl[k] = w.x;
+      wh[k] = w.y;
     }
     // channels in groups of 4: each plane gives a nibble, spread into one
     // byte per channel (byte i of `codes` collects channel 4 t4 + i; the
