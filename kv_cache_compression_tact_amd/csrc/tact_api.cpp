@@ -302,7 +302,7 @@ constexpr int64_t kMaxAttendField = 40000;   // S*H*W fp32 held in LDS (160 KB)
 
 struct AttendWs {
   float* tab;
-  float* tabT;
+  uint32_t* frags;
   uint32_t* kpoff;
   uint32_t* vpoff;
   float* qrot;
@@ -323,7 +323,7 @@ int64_t attend_ws_bytes(const Geometry& g, int64_t n_pairs, int q_heads, AttendW
   const int rep = q_heads / g.kv_heads;
   AttendWs x;
   x.tab = reinterpret_cast<float*>(take(4 * kDctTableFloats));
-  x.tabT = reinterpret_cast<float*>(take(4 * kDctTableFloats));
+  x.frags = reinterpret_cast<uint32_t*>(take(kAttendFragBytes));
   x.kpoff = reinterpret_cast<uint32_t*>(take(4 * n_pairs * g.n_bins));
   x.vpoff = reinterpret_cast<uint32_t*>(take(4 * n_pairs * g.n_bins));
   x.qrot = reinterpret_cast<float*>(take(4 * n_pairs * q_heads * g.head_dim));
@@ -517,7 +517,7 @@ tact_status tact_attend(const tact_params* p, int64_t n_pairs, int32_t q_heads,
   launch_plane_offsets(g, n_pairs, kv, w.kpoff, stream);
   launch_plane_offsets(g, n_pairs, vv, w.vpoff, stream);
   launch_attend(g, n_pairs, q_heads, kv, vv, w.kpoff, w.vpoff, q, scale, w.qrot, w.field,
-                w.partial, out, lse, w.tab, w.tabT, stream);
+                w.partial, out, lse, w.tab, w.frags, stream);
   return after_launch("tact_attend");
 }
 

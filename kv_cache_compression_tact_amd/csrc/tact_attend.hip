@@ -15,7 +15,9 @@
 //   k_att_qrot   q' = scale * R q;
 //   k_att_proj   s_f = g_f * sum_j level_j * q'_j over the K record's bins
 //                (lane = bin, the codes read straight from the bit planes);
-//   k_att_field  scores = IDCT3(s) in LDS, the softmax, lse, P = DCT3(p);
+//   k_att_frags  the DCT tables as split fp16 MFMA fragments (once a call);
+//   k_att_field  scores = IDCT3(s) in LDS on the matrix cores, the softmax,
+//                lse, P = DCT3(p);
 //   k_att_out    partial sums of P_f * level * g over the V record's bins
 //                (lane = channel), per chunk of bins;
 //   k_att_final  the sum over chunks and R^T, into the output.
@@ -23,6 +25,8 @@
 // capped (the host checks it).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "tact_internal.h"
 
@@ -34,6 +38,8 @@ namespace tact {
 namespace {
 
 constexpr int kWave = 64;
+
+#include "tact_mfma_ops.h"
 // raw buffer descriptor (gfx9 word 3): loads past its byte range return 0
 constexpr int kBufWord3 = 0x00020000;
 constexpr int kPastBuffer = 0x7FFFFFF0;
@@ -56,7 +62,7 @@ struct AttArgs {
   float* out;                     // [pair][q_heads][head_dim]
   float* lse;                     // [pair][q_heads]
   const float* tab;               // DCT-II matrices [3][64][64]
-  float* tabT;                    // their transposes
+  uint4* frags;                   // their split fp16 MFMA fragments
   int S, H, W, kv_heads, head_dim, q_heads, rep;
   int rotate, axes, max_bits, quant;
   int64_t n_bins, total_bits;
@@ -170,48 +176,135 @@ __global__ __launch_bounds__(256) void k_att_proj(AttArgs a) {
 }
 
 // ---- the field of one query head: IDCT3, softmax, DCT3 ---------------------
-// One axis of the field in LDS: each thread transforms whole lines, the line
-// in registers (NP >= N, zero padded), y[n] = sum_k M[n][k] x[k] with M the
-// DCT-II matrix (forward) or its transpose (inverse), rows of 64 floats,
-// zero padded; the rows are uniform operands.
+// One axis of the field in LDS on the matrix cores: the field's lines along
+// the axis are the columns of B (16 lines per tile, lane t = line, K rows
+// 8g..8g+7 per lane group g), the DCT matrix (or its transpose, inverse) is
+// A, split into fp16 hi / lo like the codec's contractions.  Every input x
+// of the pass satisfies |x| <= bound < 2^e, so x 2^(14 - e) fits fp16 with
+// its lo part; outputs are scaled back.  A wave reads a whole tile before
+// writing it, and tiles hold disjoint lines, so the pass runs in place.
+// fragment slot of (axis, direction, row tile m, K step, hi / lo, lane)
+__device__ __forceinline__ int frag_slot(int axis, int inverse, int m, int ks, int hl, int lane) {
+  return ((((axis * 2 + inverse) * 4 + m) * 2 + ks) * 2 + hl) * kWave + lane;
+}
+
 template <int NP>
-__device__ void line_pass(float* fld, int n_lines, int N, int inner, const float* __restrict__ M) {
-  for (int l = threadIdx.x; l < n_lines; l += blockDim.x) {
-    // lines are (outer, inner) pairs with elements `inner` apart; the
-    // innermost axis (inner == 1) has contiguous lines
-    const int o = l / inner, in = l % inner;
-    float* p = fld + static_cast<int64_t>(o) * inner * N + in;
-    float x[NP];
+__device__ void mfma_axis_pass(float* fld, int n_lines, int N, int inner, const uint4* frags, int axis,
+                               int inverse, int e) {
+  using F = Frag<NP>;
+  using vec = typename F::vec;
+  const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+  const int t = lane % 16, g = lane / 16;
+  vec ahi[F::MT][F::KSTEPS], alo[F::MT][F::KSTEPS];
 #pragma unroll
-    for (int k = 0; k < NP; ++k) x[k] = k < N ? p[k * inner] : 0.f;
-    for (int n = 0; n < N; ++n) {
-      const float* m = M + n * 64;
-      float v = 0.f;
+  for (int m = 0; m < F::MT; ++m)
 #pragma unroll
-      for (int k = 0; k < NP; ++k) v = fmaf(m[k], x[k], v);
-      p[n * inner] = v;
+    for (int ks = 0; ks < F::KSTEPS; ++ks) {
+      const uint4 h = frags[frag_slot(axis, inverse, m, ks, 0, lane)];
+      const uint4 l = frags[frag_slot(axis, inverse, m, ks, 1, lane)];
+      if constexpr (F::KV == 8) {
+        ahi[m][ks] = __builtin_bit_cast(vec, h);
+        alo[m][ks] = __builtin_bit_cast(vec, l);
+      } else {
+        ahi[m][ks] = __builtin_bit_cast(vec, uint2{h.x, h.y});
+        alo[m][ks] = __builtin_bit_cast(vec, uint2{l.x, l.y});
+      }
     }
+  const float sc = ldexpf(1.0f, 14 - e);
+  const float post = ldexpf(1.0f, e - 26);         // 2^-12 (matrix) / sc
+  const int n_tiles = (n_lines + 15) / 16;
+  const int nw = static_cast<int>(blockDim.x / kWave);
+  for (int ti = wv; ti < n_tiles; ti += nw) {
+    const int l = 16 * ti + t;
+    const bool ok = l < n_lines;
+    const int lc = ok ? l : n_lines - 1;
+    float* p = fld + (lc / inner) * inner * N + (lc % inner);
+    f32x4 acc[F::MT];
+#pragma unroll
+    for (int m = 0; m < F::MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < F::KSTEPS; ++ks) {
+      float x[F::KV];
+#pragma unroll
+      for (int v = 0; v < F::KV; ++v) {
+        const int k = ks * F::KPER + F::KV * g + v;
+        x[v] = k < N ? p[k * inner] : 0.f;
+      }
+      uint32_t hw[F::KV / 2], lw[F::KV / 2];
+#pragma unroll
+      for (int v = 0; v < F::KV; v += 2) {
+        hw[v / 2] = split_hi_pair(x[v], sc, x[v + 1], sc);
+        lw[v / 2] = split_lo_pair(x[v], sc, x[v + 1], sc, hw[v / 2]);
+      }
+      const vec bhi = pairs_to_vec<NP>(hw), blo = pairs_to_vec<NP>(lw);
+#pragma unroll
+      for (int m = 0; m < F::MT; ++m) {
+        acc[m] = mfma<NP>(ahi[m][ks], bhi, acc[m]);
+        acc[m] = mfma<NP>(alo[m][ks], bhi, acc[m]);
+        acc[m] = mfma<NP>(ahi[m][ks], blo, acc[m]);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < F::MT; ++m)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int n = 16 * m + 4 * g + rr;
+        if (ok && n < N) p[n * inner] = acc[m][rr] * post;
+      }
   }
 }
 
-__device__ void axis_pass(float* fld, const AttArgs& a, int axis, const float* M) {
+__device__ void axis_pass(float* fld, const AttArgs& a, int axis, int inverse, int e) {
   // field [S][H][W]; axis 0: lines over (h, w), elements H*W apart; axis 1:
   // lines over (s, w), W apart; axis 2: lines over (s, h), contiguous
   const int N = axis == 0 ? a.S : (axis == 1 ? a.H : a.W);
   const int n_lines = a.shw / N;
   const int inner = axis == 0 ? a.H * a.W : (axis == 1 ? a.W : 1);
-  M += axis * 4096;
-  if (N <= 16) line_pass<16>(fld, n_lines, N, inner, M);
-  else if (N <= 32) line_pass<32>(fld, n_lines, N, inner, M);
-  else line_pass<64>(fld, n_lines, N, inner, M);
+  if (N <= 16) mfma_axis_pass<16>(fld, n_lines, N, inner, a.frags, axis, inverse, e);
+  else if (N <= 32) mfma_axis_pass<32>(fld, n_lines, N, inner, a.frags, axis, inverse, e);
+  else mfma_axis_pass<64>(fld, n_lines, N, inner, a.frags, axis, inverse, e);
 }
 
-// the transposed DCT matrices, tabT[a][n][k] = tab[a][k][n]
-__global__ void k_att_transpose(AttArgs a) {
-  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < 3 * 4096; e += gridDim.x * blockDim.x) {
-    const int ax = e / 4096, k = (e / 64) % 64, n = e % 64;
-    a.tabT[ax * 4096 + n * 64 + k] = a.tab[e];
-  }
+// The DCT tables as split fp16 A fragments of the field passes, one block
+// per (axis, direction): the axis's matrix (forward) or its transpose
+// (inverse), in the lane layout of Frag<NP> for the axis's padded length.
+__device__ __forceinline__ uint32_t pack_f16(_Float16 a, _Float16 b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+template <int NP>
+__device__ void frags_of(const float* tab, int inverse, uint4* out, int axis) {
+  using F = Frag<NP>;
+  const int lane = threadIdx.x % kWave;
+  if (threadIdx.x >= kWave) return;
+  typename F::vec hi[F::MT][F::KSTEPS], lo[F::MT][F::KSTEPS];
+  load_afrag<NP>(tab, inverse, lane % 16, lane / 16, hi, lo);
+#pragma unroll
+  for (int m = 0; m < F::MT; ++m)
+#pragma unroll
+    for (int ks = 0; ks < F::KSTEPS; ++ks) {
+      uint4 h = uint4{0u, 0u, 0u, 0u}, l = h;
+      h.x = pack_f16(hi[m][ks][0], hi[m][ks][1]);
+      h.y = pack_f16(hi[m][ks][2], hi[m][ks][3]);
+      l.x = pack_f16(lo[m][ks][0], lo[m][ks][1]);
+      l.y = pack_f16(lo[m][ks][2], lo[m][ks][3]);
+      if constexpr (F::KV == 8) {
+        h.z = pack_f16(hi[m][ks][4], hi[m][ks][5]);
+        h.w = pack_f16(hi[m][ks][6], hi[m][ks][7]);
+        l.z = pack_f16(lo[m][ks][4], lo[m][ks][5]);
+        l.w = pack_f16(lo[m][ks][6], lo[m][ks][7]);
+      }
+      out[frag_slot(axis, inverse, m, ks, 0, lane)] = h;
+      out[frag_slot(axis, inverse, m, ks, 1, lane)] = l;
+    }
+}
+__global__ void k_att_frags(AttArgs a) {
+  const int axis = blockIdx.x / 2, inverse = blockIdx.x % 2;
+  const int N = axis == 0 ? a.S : (axis == 1 ? a.H : a.W);
+  const float* tab = a.tab + axis * 4096;
+  if (N <= 16) frags_of<16>(tab, inverse, a.frags, axis);
+  else if (N <= 32) frags_of<32>(tab, inverse, a.frags, axis);
+  else frags_of<64>(tab, inverse, a.frags, axis);
 }
 
 __device__ float block_reduce(float v, bool is_max, float* red) {
@@ -236,11 +329,20 @@ __global__ __launch_bounds__(kFieldThreads) void k_att_field(AttArgs a) {
   __shared__ float red[kFieldThreads / kWave];
   const int64_t row = static_cast<int64_t>(blockIdx.y) * a.q_heads + blockIdx.x;
   float* gf = a.field + row * a.shw;
-  for (int e = threadIdx.x; e < a.shw; e += blockDim.x) fld[e] = gf[e];
-  __syncthreads();
+  float ss = 0.f;
+  for (int e = threadIdx.x; e < a.shw; e += blockDim.x) {
+    const float x = gf[e];
+    fld[e] = x;
+    ss = fmaf(x, x, ss);
+  }
+  // The transforms are orthonormal, so every value of every intermediate
+  // field is at most the field's L2 norm: one scale serves all passes.
+  ss = block_reduce(ss, false, red);
+  int e_in = 0;
+  if (ss > 0.f) frexpf(sqrtf(ss) * 1.0001f, &e_in);
   for (int axis = 2; axis >= 0; --axis)
     if (a.axes & (1 << axis)) {
-      axis_pass(fld, a, axis, a.tabT);
+      axis_pass(fld, a, axis, 1, e_in);
       __syncthreads();
     }
   float m = -INFINITY;
@@ -252,9 +354,10 @@ __global__ __launch_bounds__(kFieldThreads) void k_att_field(AttArgs a) {
   const float lse = m + logf(l);
   for (int e = threadIdx.x; e < a.shw; e += blockDim.x) fld[e] = expf(fld[e] - lse);
   __syncthreads();
+  // probabilities: L2 norm at most 1
   for (int axis = 0; axis < 3; ++axis)
     if (a.axes & (1 << axis)) {
-      axis_pass(fld, a, axis, a.tab);
+      axis_pass(fld, a, axis, 0, 1);
       __syncthreads();
     }
   for (int e = threadIdx.x; e < a.shw; e += blockDim.x) gf[e] = fld[e];
@@ -408,7 +511,7 @@ int attend_chunks(const Geometry& g) {
 void launch_attend(const Geometry& g, int64_t n_pairs, int q_heads, RecordView krec,
                    RecordView vrec, const uint32_t* kpoff, const uint32_t* vpoff, const float* q,
                    float scale, float* qrot, float* field, float* partial, float* out, float* lse,
-                   const float* tab, float* tabT, hipStream_t s) {
+                   const float* tab, uint32_t* frags, hipStream_t s) {
   AttArgs a;
   a.krec = krec;
   a.vrec = vrec;
@@ -422,7 +525,7 @@ void launch_attend(const Geometry& g, int64_t n_pairs, int q_heads, RecordView k
   a.out = out;
   a.lse = lse;
   a.tab = tab;
-  a.tabT = tabT;
+  a.frags = reinterpret_cast<uint4*>(frags);
   a.S = g.S;
   a.H = g.H;
   a.W = g.W;
@@ -439,7 +542,7 @@ void launch_attend(const Geometry& g, int64_t n_pairs, int q_heads, RecordView k
   a.shw = g.S * g.H * g.W;
   a.n_chunks = attend_chunks(g);
   const unsigned np = static_cast<unsigned>(n_pairs);
-  hipLaunchKernelGGL(k_att_transpose, dim3(12), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_att_frags, dim3(6), dim3(kWave), 0, s, a);
   hipLaunchKernelGGL(k_att_qrot, dim3(q_heads, np), dim3(g.head_dim), 0, s, a);
   const dim3 gp((a.shw + 255) / 256, g.kv_heads, np), go(a.n_chunks, g.kv_heads, np);
   if (g.head_dim == 64) {

@@ -122,14 +122,17 @@ void launch_plane_offsets(const Geometry& g, int64_t n_units, RecordView rec,
 // Decoding fused into attention (tact_attend.hip): per unit pair the
 // projections, the field transforms and softmax, the output partial sums per
 // chunk of bins, and the final sum and inverse rotation.  Workspace: tab
-// (DCT tables, filled by launch_dct_tables), tabT (3 x 64 x 64 fp32), the
-// per-bin first planes of both record arrays, qrot [pairs][q_heads][d],
+// (DCT tables, filled by launch_dct_tables), frags (the tables as split fp16
+// MFMA fragments, kAttendFragBytes), the per-bin first planes of both record
+// arrays, qrot [pairs][q_heads][d],
 // field [pairs][q_heads][S*H*W], partial [pairs][kv_heads][chunks][rep][d].
 int attend_chunks(const Geometry& g);
+// 3 axes x 2 directions x 4 row tiles x 2 K steps x (hi, lo) x 64 lanes x 16 B
+constexpr int64_t kAttendFragBytes = 3 * 2 * 4 * 2 * 2 * 64 * 16;
 void launch_attend(const Geometry& g, int64_t n_pairs, int q_heads, RecordView krec,
                    RecordView vrec, const uint32_t* kpoff, const uint32_t* vpoff, const float* q,
                    float scale, float* qrot, float* field, float* partial, float* out, float* lse,
-                   const float* tab, float* tabT, hipStream_t stream);
+                   const float* tab, uint32_t* frags, hipStream_t stream);
 
 // Host copy of the fp32 codebooks (Lloyd-Max), and of every quantizer's,
 // indexed [quantizer][...].
