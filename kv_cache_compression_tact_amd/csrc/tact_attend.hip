@@ -329,11 +329,37 @@ __global__ __launch_bounds__(kFieldThreads) void k_att_field(AttArgs a) {
   __shared__ float red[kFieldThreads / kWave];
   const int64_t row = static_cast<int64_t>(blockIdx.y) * a.q_heads + blockIdx.x;
   float* gf = a.field + row * a.shw;
+  // the field into LDS, eight 16-byte loads in flight per thread (a field
+  // row starts 16-byte aligned when S*H*W is a multiple of 4)
   float ss = 0.f;
-  for (int e = threadIdx.x; e < a.shw; e += blockDim.x) {
-    const float x = gf[e];
-    fld[e] = x;
-    ss = fmaf(x, x, ss);
+  if ((a.shw & 3) == 0) {
+    const int n4 = a.shw / 4;
+    const float4* g4 = reinterpret_cast<const float4*>(gf);
+    for (int e0 = threadIdx.x; e0 < n4; e0 += 8 * blockDim.x) {
+      float4 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * blockDim.x;
+        x[u] = g4[e < n4 ? e : n4 - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * blockDim.x;
+        if (e < n4) {
+          fld_v4[e] = x[u];
+          ss = fmaf(x[u].x, x[u].x, ss);
+          ss = fmaf(x[u].y, x[u].y, ss);
+          ss = fmaf(x[u].z, x[u].z, ss);
+          ss = fmaf(x[u].w, x[u].w, ss);
+        }
+      }
+    }
+  } else {
+    for (int e = threadIdx.x; e < a.shw; e += blockDim.x) {
+      const float x = gf[e];
+      fld[e] = x;
+      ss = fmaf(x, x, ss);
+    }
   }
   // The transforms are orthonormal, so every value of every intermediate
   // field is at most the field's L2 norm: one scale serves all passes.
