@@ -469,21 +469,50 @@ __global__ __launch_bounds__(kWave) void k_att_out(AttArgs a) {
       const int b = __builtin_amdgcn_readlane(bj, j);
       const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gj), j));
       const int base = (1 << b) - 1;
+      if constexpr (WPP == 4) {
+        // plane by plane, the four words of a plane read together (faster
+        // for head_dim 256; for 64 and 128 the per-word order below is)
+        uint32_t code[WPP];
 #pragma unroll
-      for (int hw = 0; hw < WPP; ++hw) {
-        uint32_t code = 0;
+        for (int hw = 0; hw < WPP; ++hw) code[hw] = 0;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           if (k >= b) break;
-          const uint2 w = s_w[j][k * WPP + hw];
-          code |= __builtin_amdgcn_ubfe(hi ? w.y : w.x, sh, 1) << k;
+#pragma unroll
+          for (int hw = 0; hw < WPP; ++hw) {
+            const uint2 w = s_w[j][k * WPP + hw];
+            code[hw] |= __builtin_amdgcn_ubfe(hi ? w.y : w.x, sh, 1) << k;
+          }
         }
-        const float val = g * s_lv[base + static_cast<int>(code)];
+        float pj[kMaxRep];
 #pragma unroll
         for (int r = 0; r < kMaxRep; ++r)
-          if (r < a.rep)
-            acc[r][hw] = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[r]), j)),
-                              val, acc[r][hw]);
+          pj[r] = r < a.rep ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[r]), j))
+                            : 0.f;
+#pragma unroll
+        for (int hw = 0; hw < WPP; ++hw) {
+          const float val = g * s_lv[base + static_cast<int>(code[hw])];
+#pragma unroll
+          for (int r = 0; r < kMaxRep; ++r)
+            if (r < a.rep) acc[r][hw] = fmaf(pj[r], val, acc[r][hw]);
+        }
+      } else {
+#pragma unroll
+        for (int hw = 0; hw < WPP; ++hw) {
+          uint32_t code = 0;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            if (k >= b) break;
+            const uint2 w = s_w[j][k * WPP + hw];
+            code |= __builtin_amdgcn_ubfe(hi ? w.y : w.x, sh, 1) << k;
+          }
+          const float val = g * s_lv[base + static_cast<int>(code)];
+#pragma unroll
+          for (int r = 0; r < kMaxRep; ++r)
+            if (r < a.rep)
+              acc[r][hw] = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[r]), j)),
+                                val, acc[r][hw]);
+        }
       }
     }
     // every lane has read the words before the next group overwrites them
