@@ -463,15 +463,14 @@ __global__ __launch_bounds__(kWave) void k_att_out(AttArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     uint64_t todo = __ballot(bj > 0);
-    while (todo) {
-      const int j = __builtin_ctzll(todo);
-      todo &= todo - 1;
-      const int b = __builtin_amdgcn_readlane(bj, j);
-      const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gj), j));
-      const int base = (1 << b) - 1;
-      if constexpr (WPP == 4) {
-        // plane by plane, the four words of a plane read together (faster
-        // for head_dim 256; for 64 and 128 the per-word order below is)
+    if constexpr (WPP == 4) {
+      while (todo) {
+        const int j = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        const int b = __builtin_amdgcn_readlane(bj, j);
+        const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gj), j));
+        const int base = (1 << b) - 1;
+        // plane by plane, the four words of a plane read together
         uint32_t code[WPP];
 #pragma unroll
         for (int hw = 0; hw < WPP; ++hw) code[hw] = 0;
@@ -496,22 +495,44 @@ __global__ __launch_bounds__(kWave) void k_att_out(AttArgs a) {
           for (int r = 0; r < kMaxRep; ++r)
             if (r < a.rep) acc[r][hw] = fmaf(pj[r], val, acc[r][hw]);
         }
-      } else {
+      }
+    } else {
+      // two bins per step (independent decode chains); the second may be
+      // absent (b1 = 0 contributes nothing)
+      while (todo) {
+        const int j0 = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        const int j1 = todo ? __builtin_ctzll(todo) : j0;
+        const int b1 = todo ? __builtin_amdgcn_readlane(bj, j1) : 0;
+        todo &= todo ? todo - 1 : 0;
+        const int b0 = __builtin_amdgcn_readlane(bj, j0);
+        const float g0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gj), j0));
+        const float g1 = b1 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gj), j1))
+                            : 0.f;
 #pragma unroll
         for (int hw = 0; hw < WPP; ++hw) {
-          uint32_t code = 0;
+          uint32_t c0 = 0, c1 = 0;
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            if (k >= b) break;
-            const uint2 w = s_w[j][k * WPP + hw];
-            code |= __builtin_amdgcn_ubfe(hi ? w.y : w.x, sh, 1) << k;
+            if (k >= b0 && k >= b1) break;
+            if (k < b0) {
+              const uint2 w = s_w[j0][k * WPP + hw];
+              c0 |= __builtin_amdgcn_ubfe(hi ? w.y : w.x, sh, 1) << k;
+            }
+            if (k < b1) {
+              const uint2 w = s_w[j1][k * WPP + hw];
+              c1 |= __builtin_amdgcn_ubfe(hi ? w.y : w.x, sh, 1) << k;
+            }
           }
-          const float val = g * s_lv[base + static_cast<int>(code)];
+          const float v0 = g0 * s_lv[(1 << b0) - 1 + static_cast<int>(c0)];
+          const float v1 = b1 ? g1 * s_lv[(1 << b1) - 1 + static_cast<int>(c1)] : 0.f;
 #pragma unroll
           for (int r = 0; r < kMaxRep; ++r)
-            if (r < a.rep)
-              acc[r][hw] = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[r]), j)),
-                                val, acc[r][hw]);
+            if (r < a.rep) {
+              const float p0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[r]), j0));
+              const float p1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[r]), j1));
+              acc[r][hw] = fmaf(p1, v1, fmaf(p0, v0, acc[r][hw]));
+            }
         }
       }
     }
