@@ -366,6 +366,7 @@ __global__ __launch_bounds__(kFieldThreads) void k_att_field(AttArgs a) {
   ss = block_reduce(ss, false, red);
   int e_in = 0;
   if (ss > 0.f) frexpf(sqrtf(ss) * 1.0001f, &e_in);
+  if (!(ss < INFINITY)) e_in = 128;         // the sum overflowed: the largest scale
   for (int axis = 2; axis >= 0; --axis)
     if (a.axes & (1 << axis)) {
       axis_pass(fld, a, axis, 1, e_in);
