@@ -179,9 +179,12 @@ __device__ __forceinline__ void store_gap() {
   asm volatile("s_nop 0");
   __builtin_amdgcn_sched_barrier(0);
 }
+// AUX: cache policy bits of the store (2 = nt, streaming: data not reused
+// soon)
+template <int AUX = 0>
 __device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, int voff, int soff, float4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint32_t __attribute__((ext_vector_type(4))), v),
-                                         r, voff, soff, 0);
+                                         r, voff, soff, AUX);
   store_gap();
 }
 
@@ -1152,7 +1155,7 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
               const int kw = 16 * m + 4 * g + rr;
               if (t == 0 && kw < W) vrow[kw] = sq;
               if (kw < W)
-                buf_st4(rcoef, vo, (16 * m + rr) * cbytes,
+                buf_st4<2>(rcoef, vo, (16 * m + rr) * cbytes,
                         float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
             }
         }
