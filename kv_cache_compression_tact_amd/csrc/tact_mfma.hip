@@ -1030,6 +1030,8 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
                                  ? kAwFloats + TACT_CODEBOOK_LEVELS + 1
                                  : static_cast<int>(sizeof(FragLds<NPW>) / 4);
   __shared__ __attribute__((aligned(16))) uint32_t s_wbuf[kWBufWords];
+  // decode: where the W stage writes its output columns past W (dropped)
+  __shared__ __attribute__((aligned(16))) float s_sink[MODE == MODE_DEQUANT ? 4 * kWave : 4];
   FragLds<NPW>& s_fw = *reinterpret_cast<FragLds<NPW>*>(s_wbuf);
   float* s_aw = reinterpret_cast<float*>(s_wbuf);
   uint32_t* s_lp = s_wbuf + kAwFloats;
@@ -1378,14 +1380,14 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
             }
           }
         }
+        // output columns w >= W go to a per-lane sink (no predicate)
 #pragma unroll
         for (int m = 0; m < FW::MT; ++m)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const int w = 16 * m + 4 * g + rr;
-            if (w < W)
-              lds_st4(row + w * 64 + 4 * t,
-                      float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
+            lds_st4(w < W ? row + w * 64 + 4 * t : s_sink + 4 * lane,
+                    float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
           }
       }
       fetch_words(pf);
