@@ -1130,9 +1130,10 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
         for (int ks = 0; ks < FW::KSTEPS; ++ks)
 #pragma unroll
           for (int v = 0; v < FW::KV; ++v) {
+            // K rows w >= W read row W - 1: the zero-padded matrix column
+            // takes them out of the product (no predicate)
             const int w = ks * FW::KPER + FW::KV * g + v;
-            float4 q = float4{0.f, 0.f, 0.f, 0.f};
-            if (w < W) q = lds_ld4(plane + (kh * W + w) * 64 + 4 * t);
+            const float4 q = lds_ld4(plane + (kh * W + (w < W ? w : W - 1)) * 64 + 4 * t);
             xv[0][ks][v] = q.x; xv[1][ks][v] = q.y; xv[2][ks][v] = q.z; xv[3][ks][v] = q.w;
           }
         f32x4 acc[4][FW::MT];
@@ -1410,9 +1411,10 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
         for (int ks = 0; ks < FH::KSTEPS; ++ks)
 #pragma unroll
           for (int v = 0; v < FH::KV; ++v) {
+            // K rows kh >= H read row H - 1: the zero-padded matrix column
+            // takes them out of the product (no predicate)
             const int kh = ks * FH::KPER + FH::KV * g + v;
-            float4 qv = float4{0.f, 0.f, 0.f, 0.f};
-            if (kh < H) qv = lds_ld4(plane + (kh * RW + w) * 64 + 4 * t);
+            const float4 qv = lds_ld4(plane + ((kh < H ? kh : H - 1) * RW + w) * 64 + 4 * t);
             xv[0][ks][v] = qv.x; xv[1][ks][v] = qv.y; xv[2][ks][v] = qv.z; xv[3][ks][v] = qv.w;
           }
         f32x4 acc[4][FH::MT];
