@@ -1030,8 +1030,8 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
                                  ? kAwFloats + TACT_CODEBOOK_LEVELS + 1
                                  : static_cast<int>(sizeof(FragLds<NPW>) / 4);
   __shared__ __attribute__((aligned(16))) uint32_t s_wbuf[kWBufWords];
-  // decode: where the W stage writes its output columns past W (dropped)
-  __shared__ __attribute__((aligned(16))) float s_sink[MODE == MODE_DEQUANT ? 4 * kWave : 4];
+  // where a stage writes its output rows or columns past H or W (dropped)
+  __shared__ __attribute__((aligned(16))) float s_sink[4 * kWave];
   FragLds<NPW>& s_fw = *reinterpret_cast<FragLds<NPW>*>(s_wbuf);
   float* s_aw = reinterpret_cast<float*>(s_wbuf);
   uint32_t* s_lp = s_wbuf + kAwFloats;
@@ -1113,9 +1113,8 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const int kh = 16 * m + 4 * g + rr;
-            if (kh < H)
-              lds_st4(plane + (kh * W + w) * 64 + 4 * t,
-                      float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
+            lds_st4(kh < H ? plane + (kh * W + w) * 64 + 4 * t : s_sink + 4 * lane,
+                    float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
           }
         if (more) fetch_cols(pn, j);
       }
@@ -1157,9 +1156,9 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
               sq = row_sum16(sq);
               const int kw = 16 * m + 4 * g + rr;
               if (t == 0 && kw < W) vrow[kw] = sq;
-              if (kw < W)
-                buf_st4<2>(rcoef, vo, (16 * m + rr) * cbytes,
-                        float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
+              // columns past W take an offset past the buffer (dropped)
+              buf_st4<2>(rcoef, kw < W ? vo : kPastBuffer, (16 * m + rr) * cbytes,
+                         float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
             }
         }
       }
