@@ -96,6 +96,27 @@ def test_attend_matches_oracle(geo):
            out=out.cpu().numpy().astype(np.float64), lse=lse.cpu().numpy().astype(np.float64))
 
 
+def _random_att_geometries(n, seed):
+    # seeded shapes: every field axis from 1 to 64 / 32 / 40, 1..3 kv heads,
+    # every head_dim, 1..8 query heads per kv head, both rotations
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        S, H, W = int(rng.integers(1, 65)), int(rng.integers(1, 33)), int(rng.integers(1, 41))
+        hk, d = int(rng.integers(1, 4)), int(rng.choice([64, 128, 256]))
+        if S * H * W * hk * d > 60000:
+            continue
+        bmax = int(rng.integers(1, 9))
+        out.append((S, H, W, hk, d, int(rng.integers(1, bmax + 1)), bmax,
+                    hk * int(rng.integers(1, 9)), "hadamard" if rng.random() < 0.8 else "none"))
+    return out
+
+
+@pytest.mark.parametrize("geo", _random_att_geometries(6, 4242))
+def test_attend_random_geometries(geo):
+    test_attend_matches_oracle(geo)
+
+
 @pytest.mark.parametrize("quant", [1, 2])
 def test_attend_quantizer_backends(quant):
     # records coded with the uniform or NormalFloat table (absmax gains)
