@@ -1820,26 +1820,41 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
   }
 }
 
-// Per-bin first plane from a record's bits (decoding side): one block per
-// unit, block scan over the bins.
-__global__ __launch_bounds__(1024) void k_plane_offsets(Geometry g, RecordView rec,
-                                                        uint32_t* __restrict__ plane_off) {
-  __shared__ int sh[1024 / kWave];
-  const int64_t u = blockIdx.x;
-  const uint8_t* bits = rec.base + u * rec.stride + rec.off_bits;
-  uint32_t* po = plane_off + u * g.n_bins;
-  int64_t carry = 0;
-  for (int64_t base = 0; base < g.n_bins; base += 4 * blockDim.x) {
-    const int64_t i0 = base + 4 * static_cast<int64_t>(threadIdx.x);
-    int b[4];
-    for (int j = 0; j < 4; ++j) b[j] = (i0 + j < g.n_bins) ? bits[i0 + j] : 0;
-    int tot;
-    int64_t p = carry + block_exscan(b[0] + b[1] + b[2] + b[3], sh, &tot);
-    for (int j = 0; j < 4; ++j) {
-      if (i0 + j < g.n_bins) po[i0 + j] = static_cast<uint32_t>(p);
-      p += b[j];
-    }
-    carry += tot;
+// Per-bin first plane from a record (decoding side): the record's group
+// index holds the first plane of every 64th bin; a thread takes four bins
+// (one 4-byte load of their bit counts), so 16 lanes cover a group and scan
+// it from that base.  The bit-count region is padded to 256 bytes and 4-byte
+// aligned in every record, so the load past n_bins stays in the record.
+__global__ __launch_bounds__(256) void k_plane_offsets(Geometry g, RecordView rec,
+                                                       uint32_t* __restrict__ plane_off) {
+  const int64_t n = g.n_bins, per_unit = (n + 1023) / 1024;
+  const int64_t u = blockIdx.x / per_unit;
+  const int64_t bin = 4 * ((blockIdx.x - u * per_unit) * 256 + threadIdx.x);
+  const bool live = bin < n;
+  const uint8_t* r = rec.base + u * rec.stride;
+  const uint32_t w = live ? *reinterpret_cast<const uint32_t*>(r + rec.off_bits + bin) : 0u;
+  const int b0 = w & 255, b1 = bin + 1 < n ? (w >> 8) & 255 : 0,
+            b2 = bin + 2 < n ? (w >> 16) & 255 : 0, b3 = bin + 3 < n ? w >> 24 : 0;
+  const int sum = b0 + b1 + b2 + b3;
+  const int seg = threadIdx.x % 16;
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+    const int o = __shfl_up(incl, off, 16);
+    if (seg >= off) incl += o;
+  }
+  if (!live) return;
+  const uint32_t p0 =
+      reinterpret_cast<const uint32_t*>(r + rec.off_groups)[bin >> 6] + static_cast<uint32_t>(incl - sum);
+  const uint32_t p1 = p0 + b0, p2 = p1 + b1, p3 = p2 + b2;
+  uint32_t* po = plane_off + u * n + bin;
+  if ((n & 3) == 0) {
+    *reinterpret_cast<uint4*>(po) = make_uint4(p0, p1, p2, p3);
+  } else {
+    po[0] = p0;
+    if (bin + 1 < n) po[1] = p1;
+    if (bin + 2 < n) po[2] = p2;
+    if (bin + 3 < n) po[3] = p3;
   }
 }
 
@@ -2056,8 +2071,9 @@ void launch_allocate2(const Geometry& g, int64_t n_units, const float* var, int6
 
 void launch_plane_offsets(const Geometry& g, int64_t n_units, RecordView rec, uint32_t* plane_off,
                           hipStream_t s) {
-  hipLaunchKernelGGL(k_plane_offsets, dim3(static_cast<unsigned>(n_units)), dim3(1024), 0, s, g,
-                     rec, plane_off);
+  hipLaunchKernelGGL(k_plane_offsets,
+                     dim3(static_cast<unsigned>((g.n_bins + 1023) / 1024 * n_units)),
+                     dim3(256), 0, s, g, rec, plane_off);
 }
 
 }  // namespace tact
