@@ -392,27 +392,110 @@ __global__ __launch_bounds__(kFieldThreads) void k_att_field(AttArgs a) {
 }
 
 // ---- output partial sums: lane = channel, one wave per chunk of bins ------
-// Bins are taken 64 at a time: lane j loads bin j's side info, its query
-// heads' probabilities and its plane words (into LDS, 8 planes x WPP words
-// per bin), then the wave walks the coded bins with every operand on chip.
-template <int WPP>
+// Bins are taken 64 at a time.  Lane j loads bin j's side info, its query
+// heads' probabilities (folded with the bin's gain) and its plane words, and
+// turns the planes into one byte of code per channel (each plane's nibble
+// spread into four bytes, as in the projections), written to LDS.  The wave
+// then walks the coded bins: a lane reads its channel's code byte, looks up
+// the level and accumulates.  Planes at or past a bin's width were loaded as
+// zeros, so the batch is decoded over NB planes (its largest width rounded up
+// to 1, 2, 4 or 8) with no branch per bin.  RC is a power of two at least
+// the number of query heads per kv head; the unused heads carry probability 0.
+template <int WPP, int RC>
+struct OutStage {
+  uint32_t code[kWave * WPP * 16];   // [bin][word][t4]: byte i = channel 4 t4 + i
+  float lv[TACT_CODEBOOK_LEVELS + 1];
+};
+
+template <int WPP, int RC, int NB>
+__device__ __forceinline__ void out_group(OutStage<WPP, RC>& st, const uint32_t (&wk)[8][2 * WPP],
+                                          uint64_t todo, int bj, const float (&pg)[RC],
+                                          float (&acc)[RC][WPP], int lane) {
+  // codes of bin `lane`, one byte per channel
+#pragma unroll
+  for (int hw = 0; hw < WPP; ++hw)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t c4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t4 = 4 * q + i;
+        uint32_t codes = 0;
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+          uint32_t sp = __builtin_amdgcn_ubfe(wk[k][2 * hw + (t4 >= 8)], (4 * t4) & 31, 4) * 0x204081u;
+          asm("" : "+v"(sp));
+          codes |= (sp & 0x01010101u) << k;
+        }
+        c4[i] = codes;
+      }
+      *reinterpret_cast<uint4*>(st.code + (lane * WPP + hw) * 16 + 4 * q) =
+          make_uint4(c4[0], c4[1], c4[2], c4[3]);
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int BS = WPP == 4 ? 1 : 2;   // bins per step (independent chains)
+  const uint8_t* cb = reinterpret_cast<const uint8_t*>(st.code) + lane;
+  while (todo) {
+    // the second bin of a step may be absent: it repeats the first with
+    // probability 0
+    int jb[BS];
+    float keep[BS];
+    jb[0] = __builtin_ctzll(todo);
+    keep[0] = 1.f;
+    todo &= todo - 1;
+#pragma unroll
+    for (int i = 1; i < BS; ++i) {
+      keep[i] = todo ? 1.f : 0.f;
+      jb[i] = todo ? __builtin_ctzll(todo) : jb[0];
+      todo &= todo ? todo - 1 : 0;
+    }
+    float v[BS][WPP];
+#pragma unroll
+    for (int i = 0; i < BS; ++i) {
+      const int b = __builtin_amdgcn_readlane(bj, jb[i]);
+      const float* lvb = st.lv + ((1 << b) - 1);
+#pragma unroll
+      for (int hw = 0; hw < WPP; ++hw) v[i][hw] = lvb[cb[(jb[i] * WPP + hw) * 64]];
+    }
+#pragma unroll
+    for (int r = 0; r < RC; ++r) {
+      float p[BS];
+#pragma unroll
+      for (int i = 0; i < BS; ++i)
+        p[i] = keep[i] * __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                       __builtin_bit_cast(int, pg[r]), jb[i]));
+#pragma unroll
+      for (int hw = 0; hw < WPP; ++hw)
+#pragma unroll
+        for (int i = 0; i < BS; ++i) acc[r][hw] = fmaf(p[i], v[i][hw], acc[r][hw]);
+    }
+  }
+}
+
+template <int WPP, int RC>
 __global__ __launch_bounds__(kWave) void k_att_out(AttArgs a) {
-  __shared__ float s_lv[TACT_CODEBOOK_LEVELS + 1];
-  __shared__ uint2 s_w[kWave][8 * WPP];        // [bin][plane * WPP + word] as (lo, hi)
+  __shared__ OutStage<WPP, RC> st;
   for (int j = threadIdx.x; j <= TACT_CODEBOOK_LEVELS; j += blockDim.x)
-    s_lv[j] = j ? c_levels_q[a.quant][j - 1] : 0.f;
+    st.lv[j] = j ? c_levels_q[a.quant][j - 1] : 0.f;
   __syncthreads();
   const int lane = threadIdx.x;
   const int chunk = blockIdx.x, h = blockIdx.y;
   const int64_t pair = blockIdx.z;
-  const uint64_t* words = reinterpret_cast<const uint64_t*>(
-      a.vrec.base + pair * a.vrec.stride + a.vrec.off_codes);
-  const float* P = a.field + (pair * a.q_heads + static_cast<int64_t>(h) * a.rep) * a.shw;
-  const int sh = lane & 31;
-  const bool hi = lane >= 32;
-  float acc[kMaxRep][WPP];
+  const uint8_t* rv = a.vrec.base + pair * a.vrec.stride;
+  const __amdgpu_buffer_rsrc_t rw = att_rsrc(rv + a.vrec.off_codes, a.total_bits * WPP * 8);
+  const __amdgpu_buffer_rsrc_t rb = att_rsrc(rv + a.vrec.off_bits, a.n_bins);
+  const __amdgpu_buffer_rsrc_t rg = att_rsrc(rv + a.vrec.off_gains, 4 * a.n_bins);
+  const __amdgpu_buffer_rsrc_t ro = att_rsrc(a.vpoff + pair * a.n_bins, 4 * a.n_bins);
+  // the probabilities of this kv head's query heads; heads past a.rep fall
+  // past the descriptor's range and read 0
+  const __amdgpu_buffer_rsrc_t rp = att_rsrc(
+      a.field + (pair * a.q_heads + static_cast<int64_t>(h) * a.rep) * a.shw,
+      4 * static_cast<int64_t>(a.rep) * a.shw);
+  float acc[RC][WPP];
 #pragma unroll
-  for (int r = 0; r < kMaxRep; ++r)
+  for (int r = 0; r < RC; ++r)
 #pragma unroll
     for (int hw = 0; hw < WPP; ++hw) acc[r][hw] = 0.f;
   const int f_end = min(a.shw, (chunk + 1) * kChunk);
@@ -424,127 +507,60 @@ __global__ __launch_bounds__(kWave) void k_att_out(AttArgs a) {
     const int f = f0 + lane;
     const bool ok = f < f_end;
     const int bin = ok ? f * a.kv_heads + h : 0;
-    const uint8_t* rv = a.vrec.base + pair * a.vrec.stride;
-    int bj = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b8(
-        att_rsrc(rv + a.vrec.off_bits, a.n_bins), ok ? bin : kPastBuffer, 0, 0));
-    const int64_t pj = __builtin_amdgcn_raw_buffer_load_b32(
-        att_rsrc(a.vpoff + pair * a.n_bins, 4 * a.n_bins), ok ? 4 * bin : kPastBuffer, 0, 0);
-    const float gj = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-        att_rsrc(rv + a.vrec.off_gains, 4 * a.n_bins), ok ? 4 * bin : kPastBuffer, 0, 0));
-    float pr[kMaxRep];
-    const __amdgpu_buffer_rsrc_t rp = att_rsrc(P, 4 * static_cast<int64_t>(a.rep) * a.shw);
+    int bj = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b8(rb, ok ? bin : kPastBuffer, 0, 0));
+    const int64_t pj = __builtin_amdgcn_raw_buffer_load_b32(ro, ok ? 4 * bin : kPastBuffer, 0, 0);
+    const float gj = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rg, ok ? 4 * bin : kPastBuffer, 0, 0));
+    float pg[RC];
 #pragma unroll
-    for (int r = 0; r < kMaxRep; ++r)
-      pr[r] = r < a.rep ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                              rp, ok ? 4 * (r * a.shw + f) : kPastBuffer, 0, 0))
-                        : 0.f;
+    for (int r = 0; r < RC; ++r)
+      pg[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rp, ok && r < a.rep ? 4 * (r * a.shw + f) : kPastBuffer, 0, 0));
     if (bj > a.max_bits || pj + bj > a.total_bits) bj = 0;
+#pragma unroll
+    for (int r = 0; r < RC; ++r) pg[r] = bj > 0 ? pg[r] * gj : 0.f;
     // plane k of the bin: WPP consecutive 64-bit words
-    const __amdgpu_buffer_rsrc_t rw = att_rsrc(words, a.total_bits * WPP * 8);
-    uint2 wk[8][WPP];
+    uint32_t wk[8][2 * WPP];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int off = k < bj ? static_cast<int>((pj + k) * WPP * 8) : kPastBuffer;
       if constexpr (WPP == 1) {
-        wk[k][0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rw, off, 0, 0));
+        const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rw, off, 0, 0));
+        wk[k][0] = v.x;
+        wk[k][1] = v.y;
       } else {
 #pragma unroll
         for (int q = 0; q < WPP / 2; ++q) {
           const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 16 * q, 0));
-          wk[k][2 * q] = uint2{v.x, v.y};
-          wk[k][2 * q + 1] = uint2{v.z, v.w};
+          wk[k][4 * q + 0] = v.x;
+          wk[k][4 * q + 1] = v.y;
+          wk[k][4 * q + 2] = v.z;
+          wk[k][4 * q + 3] = v.w;
         }
       }
     }
+    int bw = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-#pragma unroll
-      for (int hw = 0; hw < WPP; ++hw) s_w[lane][k * WPP + hw] = wk[k][hw];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    uint64_t todo = __ballot(bj > 0);
-    if constexpr (WPP == 4) {
-      while (todo) {
-        const int j = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        const int b = __builtin_amdgcn_readlane(bj, j);
-        const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gj), j));
-        const int base = (1 << b) - 1;
-        // plane by plane, the four words of a plane read together
-        uint32_t code[WPP];
-#pragma unroll
-        for (int hw = 0; hw < WPP; ++hw) code[hw] = 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          if (k >= b) break;
-#pragma unroll
-          for (int hw = 0; hw < WPP; ++hw) {
-            const uint2 w = s_w[j][k * WPP + hw];
-            code[hw] |= __builtin_amdgcn_ubfe(hi ? w.y : w.x, sh, 1) << k;
-          }
-        }
-        float pj[kMaxRep];
-#pragma unroll
-        for (int r = 0; r < kMaxRep; ++r)
-          pj[r] = r < a.rep ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[r]), j))
-                            : 0.f;
-#pragma unroll
-        for (int hw = 0; hw < WPP; ++hw) {
-          const float val = g * s_lv[base + static_cast<int>(code[hw])];
-#pragma unroll
-          for (int r = 0; r < kMaxRep; ++r)
-            if (r < a.rep) acc[r][hw] = fmaf(pj[r], val, acc[r][hw]);
-        }
-      }
+      if (__ballot(k < bj)) bw = k + 1;
+    const uint64_t todo = __ballot(bj > 0);
+    if (bw <= 1) {
+      out_group<WPP, RC, 1>(st, wk, todo, bj, pg, acc, lane);
+    } else if (bw <= 2) {
+      out_group<WPP, RC, 2>(st, wk, todo, bj, pg, acc, lane);
+    } else if (bw <= 4) {
+      out_group<WPP, RC, 4>(st, wk, todo, bj, pg, acc, lane);
     } else {
-      // two bins per step (independent decode chains); the second may be
-      // absent (b1 = 0 contributes nothing)
-      while (todo) {
-        const int j0 = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        const int j1 = todo ? __builtin_ctzll(todo) : j0;
-        const int b1 = todo ? __builtin_amdgcn_readlane(bj, j1) : 0;
-        todo &= todo ? todo - 1 : 0;
-        const int b0 = __builtin_amdgcn_readlane(bj, j0);
-        const float g0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gj), j0));
-        const float g1 = b1 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gj), j1))
-                            : 0.f;
-#pragma unroll
-        for (int hw = 0; hw < WPP; ++hw) {
-          uint32_t c0 = 0, c1 = 0;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            if (k >= b0 && k >= b1) break;
-            if (k < b0) {
-              const uint2 w = s_w[j0][k * WPP + hw];
-              c0 |= __builtin_amdgcn_ubfe(hi ? w.y : w.x, sh, 1) << k;
-            }
-            if (k < b1) {
-              const uint2 w = s_w[j1][k * WPP + hw];
-              c1 |= __builtin_amdgcn_ubfe(hi ? w.y : w.x, sh, 1) << k;
-            }
-          }
-          const float v0 = g0 * s_lv[(1 << b0) - 1 + static_cast<int>(c0)];
-          const float v1 = b1 ? g1 * s_lv[(1 << b1) - 1 + static_cast<int>(c1)] : 0.f;
-#pragma unroll
-          for (int r = 0; r < kMaxRep; ++r)
-            if (r < a.rep) {
-              const float p0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[r]), j0));
-              const float p1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[r]), j1));
-              acc[r][hw] = fmaf(p1, v1, fmaf(p0, v0, acc[r][hw]));
-            }
-        }
-      }
+      out_group<WPP, RC, 8>(st, wk, todo, bj, pg, acc, lane);
     }
-    // every lane has read the words before the next group overwrites them
+    // every lane has read the codes before the next group overwrites them
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   float* dst = a.partial + ((pair * a.kv_heads + h) * a.n_chunks + chunk) * a.rep * (64 * WPP);
 #pragma unroll
-  for (int r = 0; r < kMaxRep; ++r)
+  for (int r = 0; r < RC; ++r)
     if (r < a.rep)
 #pragma unroll
       for (int hw = 0; hw < WPP; ++hw) dst[r * 64 * WPP + 64 * hw + lane] = acc[r][hw];
@@ -583,6 +599,22 @@ __global__ void k_att_final(AttArgs a) {
 int attend_chunks(const Geometry& g) {
   const int shw = g.S * g.H * g.W;
   return (shw + kChunk - 1) / kChunk;
+}
+
+// the output kernel for the smallest power-of-two head capacity >= a.rep
+template <int WPP>
+void launch_out(dim3 grid, const AttArgs& a, hipStream_t s) {
+  if (a.rep <= 1) {
+    hipLaunchKernelGGL((k_att_out<WPP, 1>), grid, dim3(kWave), 0, s, a);
+  } else if (a.rep <= 2) {
+    hipLaunchKernelGGL((k_att_out<WPP, 2>), grid, dim3(kWave), 0, s, a);
+  } else if (a.rep <= 4) {
+    hipLaunchKernelGGL((k_att_out<WPP, 4>), grid, dim3(kWave), 0, s, a);
+  } else if (a.rep <= 8) {
+    hipLaunchKernelGGL((k_att_out<WPP, 8>), grid, dim3(kWave), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_att_out<WPP, 16>), grid, dim3(kWave), 0, s, a);
+  }
 }
 
 void launch_attend(const Geometry& g, int64_t n_pairs, int q_heads, RecordView krec,
@@ -634,11 +666,11 @@ void launch_attend(const Geometry& g, int64_t n_pairs, int q_heads, RecordView k
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   hipLaunchKernelGGL(k_att_field, dim3(q_heads, np), dim3(kFieldThreads), lds, s, a);
   if (g.head_dim == 64) {
-    hipLaunchKernelGGL(k_att_out<1>, go, dim3(kWave), 0, s, a);
+    launch_out<1>(go, a, s);
   } else if (g.head_dim == 128) {
-    hipLaunchKernelGGL(k_att_out<2>, go, dim3(kWave), 0, s, a);
+    launch_out<2>(go, a, s);
   } else {
-    hipLaunchKernelGGL(k_att_out<4>, go, dim3(kWave), 0, s, a);
+    launch_out<4>(go, a, s);
   }
   hipLaunchKernelGGL(k_att_final, dim3(q_heads, np), dim3(g.head_dim),
                      g.head_dim * sizeof(float), s, a);
