@@ -403,7 +403,11 @@ __global__ __launch_bounds__(kFieldThreads) void k_att_field(AttArgs a) {
 // the number of query heads per kv head; the unused heads carry probability 0.
 template <int WPP, int RC>
 struct OutStage {
-  uint32_t code[kWave * WPP * 16];   // [bin][word][t4]: byte i = channel 4 t4 + i
+  // [bin][word][t4]: byte i = channel 4 t4 + i.  A bin's row is padded by
+  // four dwords, so the 16-byte writes of consecutive lanes (bins) fall in
+  // distinct banks.
+  static constexpr int kRow = WPP * 16 + 4;
+  uint32_t code[kWave * kRow];
   float lv[TACT_CODEBOOK_LEVELS + 1];
 };
 
@@ -429,47 +433,57 @@ __device__ __forceinline__ void out_group(OutStage<WPP, RC>& st, const uint32_t 
         }
         c4[i] = codes;
       }
-      *reinterpret_cast<uint4*>(st.code + (lane * WPP + hw) * 16 + 4 * q) =
+      *reinterpret_cast<uint4*>(st.code + lane * st.kRow + hw * 16 + 4 * q) =
           make_uint4(c4[0], c4[1], c4[2], c4[3]);
     }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  constexpr int BS = WPP == 4 ? 1 : 2;   // bins per step (independent chains)
   const uint8_t* cb = reinterpret_cast<const uint8_t*>(st.code) + lane;
-  while (todo) {
-    // the second bin of a step may be absent: it repeats the first with
-    // probability 0
-    int jb[BS];
-    float keep[BS];
-    jb[0] = __builtin_ctzll(todo);
-    keep[0] = 1.f;
-    todo &= todo - 1;
+  // level values of bin j at this lane's channels, and the accumulation
+  auto levels = [&](int j, float (&v)[WPP]) {
+    const int b = __builtin_amdgcn_readlane(bj, j);
+    const float* lvb = st.lv + ((1 << b) - 1);
 #pragma unroll
-    for (int i = 1; i < BS; ++i) {
-      keep[i] = todo ? 1.f : 0.f;
-      jb[i] = todo ? __builtin_ctzll(todo) : jb[0];
-      todo &= todo ? todo - 1 : 0;
+    for (int hw = 0; hw < WPP; ++hw) v[hw] = lvb[cb[(j * st.kRow + hw * 16) * 4]];
+  };
+  auto prob = [&](int r, int j) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pg[r]), j));
+  };
+  int n = __builtin_popcountll(todo);
+  // ST bins per step (independent chains, so the LDS round trips overlap)
+  constexpr int ST = (WPP == 4 || RC == 16) ? 2 : 4;
+  for (; n >= ST; n -= ST) {
+    int j[ST];
+    float v[ST][WPP];
+#pragma unroll
+    for (int i = 0; i < ST; ++i) {
+      j[i] = __builtin_ctzll(todo);
+      todo &= todo - 1;
     }
-    float v[BS][WPP];
 #pragma unroll
-    for (int i = 0; i < BS; ++i) {
-      const int b = __builtin_amdgcn_readlane(bj, jb[i]);
-      const float* lvb = st.lv + ((1 << b) - 1);
-#pragma unroll
-      for (int hw = 0; hw < WPP; ++hw) v[i][hw] = lvb[cb[(jb[i] * WPP + hw) * 64]];
-    }
+    for (int i = 0; i < ST; ++i) levels(j[i], v[i]);
 #pragma unroll
     for (int r = 0; r < RC; ++r) {
-      float p[BS];
+      float p[ST];
 #pragma unroll
-      for (int i = 0; i < BS; ++i)
-        p[i] = keep[i] * __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                       __builtin_bit_cast(int, pg[r]), jb[i]));
+      for (int i = 0; i < ST; ++i) p[i] = prob(r, j[i]);
 #pragma unroll
       for (int hw = 0; hw < WPP; ++hw)
 #pragma unroll
-        for (int i = 0; i < BS; ++i) acc[r][hw] = fmaf(p[i], v[i][hw], acc[r][hw]);
+        for (int i = 0; i < ST; ++i) acc[r][hw] = fmaf(p[i], v[i][hw], acc[r][hw]);
+    }
+  }
+  for (; n > 0; --n) {
+    const int j = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    float v[WPP];
+    levels(j, v);
+#pragma unroll
+    for (int r = 0; r < RC; ++r) {
+      const float p = prob(r, j);
+#pragma unroll
+      for (int hw = 0; hw < WPP; ++hw) acc[r][hw] = fmaf(p, v[hw], acc[r][hw]);
     }
   }
 }
