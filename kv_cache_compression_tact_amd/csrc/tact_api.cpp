@@ -297,7 +297,6 @@ void decompress_chunk(const Geometry& g, int64_t cn, const uint8_t* recs, void* 
 namespace tact {
 namespace {
 
-constexpr int kMaxAttendRep = 16;
 constexpr int64_t kMaxAttendField = 40000;   // S*H*W fp32 held in LDS (160 KB)
 
 struct AttendWs {

@@ -46,7 +46,6 @@ constexpr int kPastBuffer = 0x7FFFFFF0;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t att_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufWord3);
 }
-constexpr int kMaxRep = 16;       // query heads per kv head
 constexpr int kChunk = 256;       // bins per wave in k_att_out
 constexpr int kFieldThreads = 512;
 
@@ -88,34 +87,65 @@ __global__ void k_att_qrot(AttArgs a) {
 // ---- projections: lane = bin f of kv head h --------------------------------
 // The rotated, scaled queries of the kv head are staged in LDS transposed
 // (channel-major, the query heads of a channel adjacent), so one broadcast
-// read serves every lane.
-template <int WPP>
+// read serves every lane.  RQ (a multiple of 4) is at least the number of
+// query heads per kv head; the unused heads have zero queries.
+template <int WPP, int RQ>
 __global__ __launch_bounds__(256) void k_att_proj(AttArgs a) {
   constexpr int D = 64 * WPP;
   __shared__ float s_lv[TACT_CODEBOOK_LEVELS + 1];   // s_lv[0] = 0; b bits at (1 << b) - 1
-  __shared__ __attribute__((aligned(16))) float s_qt[D * kMaxRep];   // [channel][r]
+  __shared__ __attribute__((aligned(16))) float s_qt[D * RQ];   // [channel][r]
   const int h = blockIdx.y;
   const int64_t pair = blockIdx.z;
   for (int j = threadIdx.x; j <= TACT_CODEBOOK_LEVELS; j += blockDim.x)
     s_lv[j] = j ? c_levels_q[a.quant][j - 1] : 0.f;
   const float* qr = a.qrot + (pair * a.q_heads + static_cast<int64_t>(h) * a.rep) * D;
-  for (int e = threadIdx.x; e < D * kMaxRep; e += blockDim.x) {
-    const int c = e / kMaxRep, r = e % kMaxRep;
+  for (int e = threadIdx.x; e < D * RQ; e += blockDim.x) {
+    const int c = e / RQ, r = e % RQ;
     s_qt[e] = r < a.rep ? qr[r * D + c] : 0.f;
   }
   __syncthreads();
-  const int f = blockIdx.x * blockDim.x + threadIdx.x;
+  int f = blockIdx.x * blockDim.x + threadIdx.x;
   const bool live = f < a.shw;
   // side info through buffer loads every lane issues (past the buffer: 0)
   const int bin = live ? f * a.kv_heads + h : 0;
   const uint8_t* rk = a.krec.base + pair * a.krec.stride;
   int b = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b8(
       att_rsrc(rk + a.krec.off_bits, a.n_bins), live ? bin : kPastBuffer, 0, 0));
-  const int64_t p0 = __builtin_amdgcn_raw_buffer_load_b32(
+  int64_t p0 = __builtin_amdgcn_raw_buffer_load_b32(
       att_rsrc(a.kpoff + pair * a.n_bins, 4 * a.n_bins), live ? 4 * bin : kPastBuffer, 0, 0);
-  const float g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+  float g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
       att_rsrc(rk + a.krec.off_gains, 4 * a.n_bins), live ? 4 * bin : kPastBuffer, 0, 0));
   if (b > a.max_bits || p0 + b > a.total_bits) b = 0;
+  float* fld = a.field + (pair * a.q_heads + static_cast<int64_t>(h) * a.rep) * a.shw;
+  // A bin without bits projects to 0.  The coded bins of the block are then
+  // packed into its first threads (in bin order), so that lanes do not idle
+  // on uncoded bins and waves left without a coded bin exit.
+  if (live && b == 0)
+    for (int r = 0; r < a.rep; ++r) fld[static_cast<int64_t>(r) * a.shw + f] = 0.f;
+  __shared__ int s_cnt[256 / kWave];
+  __shared__ int4 s_side[256];
+  const uint64_t cm = __ballot(b > 0);
+  const int wv = threadIdx.x / kWave;
+  if (threadIdx.x % kWave == 0) s_cnt[wv] = static_cast<int>(__popcll(cm));
+  __syncthreads();
+  int pos = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+      static_cast<uint32_t>(cm >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(cm), 0u)));
+  int n = 0;
+#pragma unroll
+  for (int w = 0; w < 256 / kWave; ++w) {
+    if (w < wv) pos += s_cnt[w];
+    n += s_cnt[w];
+  }
+  if (b > 0) s_side[pos] = int4{f, b, static_cast<int>(p0), __float_as_int(g)};
+  __syncthreads();
+  if (static_cast<int>(threadIdx.x) >= n) return;
+  {
+    const int4 sd = s_side[threadIdx.x];
+    f = sd.x;
+    b = sd.y;
+    p0 = static_cast<uint32_t>(sd.z);
+    g = __int_as_float(sd.w);
+  }
   const __amdgpu_buffer_rsrc_t rw = att_rsrc(rk + a.krec.off_codes, a.total_bits * WPP * 8);
   const int base = b > 0 ? (1 << b) - 1 : 0;
   // the largest bit width in the wave bounds the planes read per channel
@@ -124,10 +154,9 @@ __global__ __launch_bounds__(256) void k_att_proj(AttArgs a) {
   for (int k = 0; k < 8; ++k)
     if (__ballot(k < b)) bw = k + 1;
   // query heads in groups of 4 (one 128-bit LDS read per channel and group)
-  const int n4 = (a.rep + 3) / 4;
-  float acc[kMaxRep];
+  float acc[RQ];
 #pragma unroll
-  for (int r = 0; r < kMaxRep; ++r) acc[r] = 0.f;
+  for (int r = 0; r < RQ; ++r) acc[r] = 0.f;
 #pragma unroll
   for (int hw = 0; hw < WPP; ++hw) {
     uint32_t wl[8], wh[8];
@@ -155,10 +184,9 @@ __global__ __launch_bounds__(256) void k_att_proj(AttArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int jj = 4 * t4 + i;
         const float val = s_lv[base + static_cast<int>((codes >> (8 * i)) & 0xFFu)];
-        const float4* qc = reinterpret_cast<const float4*>(s_qt + (64 * hw + jj) * kMaxRep);
+        const float4* qc = reinterpret_cast<const float4*>(s_qt + (64 * hw + jj) * RQ);
 #pragma unroll
-        for (int r4 = 0; r4 < kMaxRep / 4; ++r4) {
-          if (r4 >= n4) break;
+        for (int r4 = 0; r4 < RQ / 4; ++r4) {
           const float4 qv = qc[r4];
           acc[4 * r4 + 0] = fmaf(val, qv.x, acc[4 * r4 + 0]);
           acc[4 * r4 + 1] = fmaf(val, qv.y, acc[4 * r4 + 1]);
@@ -168,11 +196,9 @@ __global__ __launch_bounds__(256) void k_att_proj(AttArgs a) {
       }
     }
   }
-  if (!live) return;
 #pragma unroll
-  for (int r = 0; r < kMaxRep; ++r)
-    if (r < a.rep)
-      a.field[(pair * a.q_heads + static_cast<int64_t>(h) * a.rep + r) * a.shw + f] = g * acc[r];
+  for (int r = 0; r < RQ; ++r)
+    if (r < a.rep) fld[static_cast<int64_t>(r) * a.shw + f] = g * acc[r];
 }
 
 // ---- the field of one query head: IDCT3, softmax, DCT3 ---------------------
@@ -615,6 +641,20 @@ int attend_chunks(const Geometry& g) {
   return (shw + kChunk - 1) / kChunk;
 }
 
+static_assert(kMaxAttendRep == 16, "head capacities below cover 1..16 query heads per kv head");
+
+// the projection kernel for the smallest of 4, 8, 16 that is >= a.rep
+template <int WPP>
+void launch_proj(dim3 grid, const AttArgs& a, hipStream_t s) {
+  if (a.rep <= 4) {
+    hipLaunchKernelGGL((k_att_proj<WPP, 4>), grid, dim3(256), 0, s, a);
+  } else if (a.rep <= 8) {
+    hipLaunchKernelGGL((k_att_proj<WPP, 8>), grid, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_att_proj<WPP, 16>), grid, dim3(256), 0, s, a);
+  }
+}
+
 // the output kernel for the smallest power-of-two head capacity >= a.rep
 template <int WPP>
 void launch_out(dim3 grid, const AttArgs& a, hipStream_t s) {
@@ -669,11 +709,11 @@ void launch_attend(const Geometry& g, int64_t n_pairs, int q_heads, RecordView k
   hipLaunchKernelGGL(k_att_qrot, dim3(q_heads, np), dim3(g.head_dim), 0, s, a);
   const dim3 gp((a.shw + 255) / 256, g.kv_heads, np), go(a.n_chunks, g.kv_heads, np);
   if (g.head_dim == 64) {
-    hipLaunchKernelGGL(k_att_proj<1>, gp, dim3(256), 0, s, a);
+    launch_proj<1>(gp, a, s);
   } else if (g.head_dim == 128) {
-    hipLaunchKernelGGL(k_att_proj<2>, gp, dim3(256), 0, s, a);
+    launch_proj<2>(gp, a, s);
   } else {
-    hipLaunchKernelGGL(k_att_proj<4>, gp, dim3(256), 0, s, a);
+    launch_proj<4>(gp, a, s);
   }
   const size_t lds = static_cast<size_t>(a.shw) * sizeof(float);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_att_field),

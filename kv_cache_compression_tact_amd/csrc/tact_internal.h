@@ -128,6 +128,9 @@ void launch_plane_offsets(const Geometry& g, int64_t n_units, RecordView rec,
 // field [pairs][q_heads][S*H*W], partial [pairs][kv_heads][chunks][rep][d].
 int attend_chunks(const Geometry& g);
 // 3 axes x 2 directions x 4 row tiles x 2 K steps x (hi, lo) x 64 lanes x 16 B
+// query heads per kv head that tact_attend accepts (its kernels are
+// specialised for capacities up to this)
+constexpr int kMaxAttendRep = 16;
 constexpr int64_t kAttendFragBytes = 3 * 2 * 4 * 2 * 2 * 64 * 16;
 void launch_attend(const Geometry& g, int64_t n_pairs, int q_heads, RecordView krec,
                    RecordView vrec, const uint32_t* kpoff, const uint32_t* vpoff, const float* q,
