@@ -429,10 +429,11 @@ __global__ __launch_bounds__(kFieldThreads) void k_att_field(AttArgs a) {
 // the number of query heads per kv head; the unused heads carry probability 0.
 template <int WPP, int RC>
 struct OutStage {
-  // [bin][word][t4]: byte i = channel 4 t4 + i.  A bin's row is padded by
-  // four dwords, so the 16-byte writes of consecutive lanes (bins) fall in
-  // distinct banks.
-  static constexpr int kRow = WPP * 16 + 4;
+  // A bin's row: its codes, [word][t4] with byte i = channel 4 t4 + i, then
+  // its RC probabilities (at least four dwords, so that the 16-byte writes of
+  // consecutive lanes (bins) fall in distinct banks for RC <= 4).
+  static constexpr int kCodes = WPP * 16;
+  static constexpr int kRow = kCodes + (RC < 4 ? 4 : RC);
   uint32_t code[kWave * kRow];
   float lv[TACT_CODEBOOK_LEVELS + 1];
 };
@@ -462,19 +463,46 @@ __device__ __forceinline__ void out_group(OutStage<WPP, RC>& st, const uint32_t 
       *reinterpret_cast<uint4*>(st.code + lane * st.kRow + hw * 16 + 4 * q) =
           make_uint4(c4[0], c4[1], c4[2], c4[3]);
     }
+  float* prow = reinterpret_cast<float*>(st.code + lane * st.kRow + st.kCodes);
+  if constexpr (RC >= 4) {
+#pragma unroll
+    for (int r = 0; r < RC; r += 4)
+      *reinterpret_cast<float4*>(prow + r) = make_float4(pg[r], pg[r + 1], pg[r + 2], pg[r + 3]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < RC; ++r) prow[r] = pg[r];
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const uint8_t* cb = reinterpret_cast<const uint8_t*>(st.code) + lane;
-  // level values of bin j at this lane's channels, and the accumulation
+  // level values of bin j at this lane's channels: the lane reads the dword
+  // that holds its channel's code byte (four lanes share it: one broadcast,
+  // where byte reads of one dword by several lanes conflict) and extracts it
+  const uint32_t* cw = st.code + lane / 4;
+  const int byte_sh = 8 * (lane % 4);
   auto levels = [&](int j, float (&v)[WPP]) {
     const int b = __builtin_amdgcn_readlane(bj, j);
     const float* lvb = st.lv + ((1 << b) - 1);
 #pragma unroll
-    for (int hw = 0; hw < WPP; ++hw) v[hw] = lvb[cb[(j * st.kRow + hw * 16) * 4]];
+    for (int hw = 0; hw < WPP; ++hw)
+      v[hw] = lvb[__builtin_amdgcn_ubfe(cw[j * st.kRow + hw * 16], byte_sh, 8)];
   };
-  auto prob = [&](int r, int j) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pg[r]), j));
+  // the probabilities of bin j (one broadcast read)
+  auto probs = [&](int j, float (&pv)[RC]) {
+    const float* pr = reinterpret_cast<const float*>(st.code + j * st.kRow + st.kCodes);
+    if constexpr (RC >= 4) {
+#pragma unroll
+      for (int r = 0; r < RC; r += 4) {
+        const float4 v4 = *reinterpret_cast<const float4*>(pr + r);
+        pv[r] = v4.x;
+        pv[r + 1] = v4.y;
+        pv[r + 2] = v4.z;
+        pv[r + 3] = v4.w;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < RC; ++r) pv[r] = pr[r];
+    }
   };
   int n = __builtin_popcountll(todo);
   // ST bins per step (independent chains, so the LDS round trips overlap)
@@ -487,30 +515,29 @@ __device__ __forceinline__ void out_group(OutStage<WPP, RC>& st, const uint32_t 
       j[i] = __builtin_ctzll(todo);
       todo &= todo - 1;
     }
+    float p[ST][RC];
 #pragma unroll
-    for (int i = 0; i < ST; ++i) levels(j[i], v[i]);
+    for (int i = 0; i < ST; ++i) {
+      levels(j[i], v[i]);
+      probs(j[i], p[i]);
+    }
 #pragma unroll
-    for (int r = 0; r < RC; ++r) {
-      float p[ST];
-#pragma unroll
-      for (int i = 0; i < ST; ++i) p[i] = prob(r, j[i]);
+    for (int r = 0; r < RC; ++r)
 #pragma unroll
       for (int hw = 0; hw < WPP; ++hw)
 #pragma unroll
-        for (int i = 0; i < ST; ++i) acc[r][hw] = fmaf(p[i], v[i][hw], acc[r][hw]);
-    }
+        for (int i = 0; i < ST; ++i) acc[r][hw] = fmaf(p[i][r], v[i][hw], acc[r][hw]);
   }
   for (; n > 0; --n) {
     const int j = __builtin_ctzll(todo);
     todo &= todo - 1;
-    float v[WPP];
+    float v[WPP], p[RC];
     levels(j, v);
+    probs(j, p);
 #pragma unroll
-    for (int r = 0; r < RC; ++r) {
-      const float p = prob(r, j);
+    for (int r = 0; r < RC; ++r)
 #pragma unroll
-      for (int hw = 0; hw < WPP; ++hw) acc[r][hw] = fmaf(p, v[hw], acc[r][hw]);
-    }
+      for (int hw = 0; hw < WPP; ++hw) acc[r][hw] = fmaf(p[r], v[hw], acc[r][hw]);
   }
 }
 
