@@ -74,6 +74,9 @@ ATT_GEOMS = [
     (33, 3, 2, 1, 128, 3, 5, 1, "none"),            # S beyond 32, no rotation
     (3, 17, 23, 2, 128, 2, 8, 4, "hadamard"),       # H, W beyond 16
     (2, 2, 40, 1, 64, 1, 8, 2, "hadamard"),         # W beyond 32
+    (4, 6, 5, 2, 64, 2, 8, 6, "hadamard"),          # 3 per kv head (one padded head)
+    (3, 5, 7, 1, 256, 2, 6, 5, "none"),             # 5 per kv head (three padded heads)
+    (2, 4, 4, 2, 128, 8, 8, 8, "hadamard"),         # every bin coded at 8 bits
 ]
 
 
