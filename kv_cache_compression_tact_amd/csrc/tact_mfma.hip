@@ -1480,17 +1480,6 @@ __device__ int block_exscan(int v, int* sh, int* total) {
   return before + incl - v;
 }
 
-__device__ int64_t block_sum64(int64_t v, long long* sh) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  __syncthreads();
-  if (threadIdx.x % kWave == 0) sh[threadIdx.x / kWave] = v;
-  __syncthreads();
-  int64_t t = 0;
-  for (int i = 0; i < static_cast<int>(blockDim.x) / kWave; ++i) t += sh[i];
-  return t;
-}
-
 // Largest bucket b of hist[0..nb) with sum_{y >= b} hist[y] >= need; the
 // count strictly above it goes to *above.  nb <= 4 * blockDim.x.
 __device__ void select_bucket(const uint32_t* hist, int nb, int64_t need, int* sh,
@@ -1645,7 +1634,6 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
   __shared__ uint32_t hist[4096];
   __shared__ float s_var[4 * kAllocThreads];   // one chunk of variances, bin order
   __shared__ int sh[kAllocThreads / kWave];
-  __shared__ long long sh64[kAllocThreads / kWave];
   const int64_t u = blockIdx.x;
   const float* v = var + u * var_stride;
   VarView vv;
@@ -1688,8 +1676,14 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
     int ebin;
     int64_t above;
     select_bucket(hist + 2048, 2048, T, sh, &ebin, &above);
+    // The keys hold the fp32 gains exactly in their top 35 bits, so tau, the
+    // T-th largest gain, is fixed by the three digits, and the counts of the
+    // gains above it and equal to it follow from the histograms.
+    int64_t gt_total, eq_cnt;
     if (ebin == 0) {
       tau = 0;
+      gt_total = above;
+      eq_cnt = hist[2048];
     } else {
       // ---- sweep 2: top 12 mantissa bits among gains with exponent ebin --
       for (int j = threadIdx.x; j < 4096; j += blockDim.x) hist[j] = 0;
@@ -1718,16 +1712,10 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
       select_bucket(hist, 2048, T - above - above2, sh, &b3, &above3);
       tau = (static_cast<uint64_t>(ebin) << 52) | (static_cast<uint64_t>(b2) << 40) |
             (static_cast<uint64_t>(b3) << 29);
+      gt_total = above + above2 + above3;
+      eq_cnt = hist[b3];
     }
-    int64_t gt = 0, eq = 0;
-    for_bins4(vv, var_scale, [&](float x) {
-      const uint64_t key = gain_key(x);
-      const int a1 = count_ge(key, tau + 1, bmax);
-      gt += a1;
-      eq += count_ge(key, tau, bmax) - a1;
-    });
-    const int64_t gt_total = block_sum64(gt, sh64);
-    eq_total = block_sum64(eq, sh64);
+    eq_total = eq_cnt;
     need = T - gt_total;
   }
   // ties at the cut need the bin-ordered prefix only when some are left out
