@@ -1011,9 +1011,14 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
   const int cbytes = static_cast<int>(a.C) * 4;
   const int row_bytes = W * cbytes;
   // LDS row stride in 64-float positions: the decode pass stages the side
-  // info of NPW bins (80 bytes each) in a row's area, so short rows are
-  // padded
-  const int RW = MODE == MODE_DEQUANT ? max(W, (NPW * 80 + 255) / 256) : W;
+  // info of NPW bins (80 bytes each, plus 112 bytes after every 8 bins) in a
+  // row's area, so short rows are padded
+  const int RW = MODE == MODE_DEQUANT ? max(W, (NPW * 80 + (NPW / 8 - 1) * 112 + 255) / 256) : W;
+  // 16-byte slot of bin kw's staging: 5 slots per bin and 7 more after every
+  // 8 bins, so that the four bins one read serves (kw, kw + 4, kw + 8,
+  // kw + 12 for kw % 8 < 4; 320 bytes apart without the gaps) start in
+  // distinct banks
+  auto stage_slot = [](int kw) { return kw * 5 + (kw >> 3) * 7; };
   // bin of (s, kh, kw) of a plane's head
   auto bin_of3 = [&](const PlaneId& id, int kh, int kw) -> int64_t {
     return ((static_cast<int64_t>(id.s) * H + kh) * W + kw) * a.kv_heads + id.head;
@@ -1278,12 +1283,13 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
         if (lane < NPW) {
           // {bits, gain (0 without bits), first level-table entry, 0}
           const int b = bj[q];
-          st[lane * 5] = uint4{static_cast<uint32_t>(b), b > 0 ? __float_as_uint(gjv[q]) : 0u,
+          const int sl = stage_slot(lane);
+          st[sl] = uint4{static_cast<uint32_t>(b), b > 0 ? __float_as_uint(gjv[q]) : 0u,
                                b > 0 ? (1u << b) - 1u : 0u, 0u};
-          st[lane * 5 + 1] = uint4{wd[q][0].x, wd[q][1].x, wd[q][2].x, wd[q][3].x};
-          st[lane * 5 + 2] = uint4{wd[q][4].x, wd[q][5].x, wd[q][6].x, wd[q][7].x};
-          st[lane * 5 + 3] = uint4{wd[q][0].y, wd[q][1].y, wd[q][2].y, wd[q][3].y};
-          st[lane * 5 + 4] = uint4{wd[q][4].y, wd[q][5].y, wd[q][6].y, wd[q][7].y};
+          st[sl + 1] = uint4{wd[q][0].x, wd[q][1].x, wd[q][2].x, wd[q][3].x};
+          st[sl + 2] = uint4{wd[q][4].x, wd[q][5].x, wd[q][6].x, wd[q][7].x};
+          st[sl + 3] = uint4{wd[q][0].y, wd[q][1].y, wd[q][2].y, wd[q][3].y};
+          st[sl + 4] = uint4{wd[q][4].y, wd[q][5].y, wd[q][6].y, wd[q][7].y};
         }
       }
       // (the last plane of the walk fetches itself again: same loads, unused)
@@ -1309,9 +1315,10 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
           for (int v = 0; v < FW::KV; ++v) {
             // (K rows kw >= W are staged as empty bins)
             const int kw = ks * FW::KPER + FW::KV * g + v;
-            const uint4 sb = st[kw * 5];
-            const uint4 w03 = st[kw * 5 + half];
-            const uint4 w47 = st[kw * 5 + half + 1];
+            const int sl = stage_slot(kw);
+            const uint4 sb = st[sl];
+            const uint4 w03 = st[sl + half];
+            const uint4 w47 = st[sl + half + 1];
             uint32_t wk[8] = {w03.x, w03.y, w03.z, w03.w, w47.x, w47.y, w47.z, w47.w};
             // (all three reads issue here, not one word per plane below)
             asm("" : "+v"(wk[0]), "+v"(wk[1]), "+v"(wk[2]), "+v"(wk[3]), "+v"(wk[4]), "+v"(wk[5]),
@@ -2007,10 +2014,11 @@ void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in,
   const dim3 block(64 * waves);
   const bool h16 = g.H <= 16, w16 = g.W <= 16;
   // the decode pass pads rows shorter than its staging (80 bytes per bin of
-  // the 16 or 32 K rows)
+  // the 16 or 32 K rows, plus 112 bytes after every 8 bins)
   int rw = g.W;
   if (mode == MODE_DEQUANT) {
-    const int need = ((w16 ? 16 : 32) * 80 + 255) / 256;
+    const int nk = w16 ? 16 : 32;
+    const int need = (nk * 80 + (nk / 8 - 1) * 112 + 255) / 256;
     if (rw < need) rw = need;
   }
   const size_t lds = static_cast<size_t>(g.H) * rw * 64 * sizeof(float);
