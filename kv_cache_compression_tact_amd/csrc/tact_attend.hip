@@ -476,8 +476,8 @@ __device__ __forceinline__ void out_group(OutStage<WPP, RC>& st, const uint32_t 
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // level values of bin j at this lane's channels: the lane reads the dword
-  // that holds its channel's code byte (four lanes share it: one broadcast,
-  // where byte reads of one dword by several lanes conflict) and extracts it
+  // that holds its channel's code byte (four lanes read the same dword) and
+  // extracts the byte
   const uint32_t* cw = st.code + lane / 4;
   const int byte_sh = 8 * (lane % 4);
   auto levels = [&](int j, float (&v)[WPP]) {
