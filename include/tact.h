@@ -51,6 +51,13 @@
  *                                        (sum_{k<i} b_k + q) * head_dim; bit j
  *                                        of a plane is bit q of code_j.
  * The record is position independent: it can be copied or stored as is.
+ * Decoding (tact_decompress, tact_attend) locates each bin's planes from the
+ * group index and the bit widths, so the index must agree with the widths,
+ * as it does in every record tact_compress writes.  A record whose index or
+ * widths are inconsistent decodes to unspecified values, but never makes a
+ * kernel read or write outside the record, the output or the workspace:
+ * widths above max_bits, and planes that would run past the T planes of the
+ * record, decode as zero.
  */
 #ifndef TACT_H_
 #define TACT_H_
