@@ -171,7 +171,7 @@ def test_attend_zero_budget_is_uniform_over_zero_values():
     assert torch.allclose(lse.cpu(), torch.full((1, 2), math.log(S * H * W)), atol=1e-6)
 
 
-@pytest.mark.parametrize("name", ["ct4b", "ct32b"])
+@pytest.mark.parametrize("name", ["ct4b", "ct7b", "ct32b", "video"])
 def test_attend_full_size_pair(name):
     """One layer's K and V at the workload's full unit size (the largest field
     that fits: 64 x 24 x 24 for ct32b), records written by the oracle."""
