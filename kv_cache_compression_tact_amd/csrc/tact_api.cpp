@@ -513,8 +513,7 @@ tact_status tact_attend(const tact_params* p, int64_t n_pairs, int32_t q_heads,
   const RecordView kv = view(g, const_cast<void*>(k_records));
   const RecordView vv = view(g, const_cast<void*>(v_records));
   launch_dct_tables(g, w.tab, stream);
-  launch_plane_offsets(g, n_pairs, kv, w.kpoff, stream);
-  launch_plane_offsets(g, n_pairs, vv, w.vpoff, stream);
+  launch_plane_offsets(g, n_pairs, kv, w.kpoff, stream, &vv, w.vpoff);
   launch_attend(g, n_pairs, q_heads, kv, vv, w.kpoff, w.vpoff, q, scale, w.qrot, w.field,
                 w.partial, out, lse, w.tab, w.frags, stream);
   return after_launch("tact_attend");

@@ -115,9 +115,12 @@ void launch_quant(const Geometry& g, int64_t n_units, const float* coef, int64_t
                   const float* inv_gain, int64_t var_stride, RecordView rec,
                   const uint32_t* plane_off, hipStream_t stream);
 
-// Per-bin first planes from the bits stored in records.
+// Per-bin first planes of n_units records (from each record's group index
+// and bit widths); with rec2, also those of n_units records of rec2 into
+// plane_off2, in the same launch.
 void launch_plane_offsets(const Geometry& g, int64_t n_units, RecordView rec,
-                          uint32_t* plane_off, hipStream_t stream);
+                          uint32_t* plane_off, hipStream_t stream,
+                          const RecordView* rec2 = nullptr, uint32_t* plane_off2 = nullptr);
 
 // Decoding fused into attention (tact_attend.hip): per unit pair the
 // projections, the field transforms and softmax, the output partial sums per

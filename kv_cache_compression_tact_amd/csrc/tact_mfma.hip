@@ -1820,11 +1820,18 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
 // (one 4-byte load of their bit counts), so 16 lanes cover a group and scan
 // it from that base.  The bit-count region is padded to 256 bytes and 4-byte
 // aligned in every record, so the load past n_bins stays in the record.
-__global__ __launch_bounds__(256) void k_plane_offsets(Geometry g, RecordView rec,
-                                                       uint32_t* __restrict__ plane_off) {
+__global__ __launch_bounds__(256) void k_plane_offsets(Geometry g, RecordView rec0,
+                                                       uint32_t* __restrict__ out0, RecordView rec1,
+                                                       uint32_t* __restrict__ out1, int64_t blocks0) {
+  // blocks [0, blocks0) scan the records of rec0 into out0, the rest those of
+  // rec1 into out1 (both sets of one call: the K and V records of attention)
+  const bool second = blockIdx.x >= blocks0;
+  const RecordView rec = second ? rec1 : rec0;
+  uint32_t* plane_off = second ? out1 : out0;
+  const int64_t bid = second ? blockIdx.x - blocks0 : blockIdx.x;
   const int64_t n = g.n_bins, per_unit = (n + 1023) / 1024;
-  const int64_t u = blockIdx.x / per_unit;
-  const int64_t bin = 4 * ((blockIdx.x - u * per_unit) * 256 + threadIdx.x);
+  const int64_t u = bid / per_unit;
+  const int64_t bin = 4 * ((bid - u * per_unit) * 256 + threadIdx.x);
   const bool live = bin < n;
   const uint8_t* r = rec.base + u * rec.stride;
   const uint32_t w = live ? *reinterpret_cast<const uint32_t*>(r + rec.off_bits + bin) : 0u;
@@ -2066,10 +2073,11 @@ void launch_allocate2(const Geometry& g, int64_t n_units, const float* var, int6
 }
 
 void launch_plane_offsets(const Geometry& g, int64_t n_units, RecordView rec, uint32_t* plane_off,
-                          hipStream_t s) {
-  hipLaunchKernelGGL(k_plane_offsets,
-                     dim3(static_cast<unsigned>((g.n_bins + 1023) / 1024 * n_units)),
-                     dim3(256), 0, s, g, rec, plane_off);
+                          hipStream_t s, const RecordView* rec2, uint32_t* plane_off2) {
+  const int64_t blocks = (g.n_bins + 1023) / 1024 * n_units;
+  const int64_t total = rec2 ? 2 * blocks : blocks;
+  hipLaunchKernelGGL(k_plane_offsets, dim3(static_cast<unsigned>(total)), dim3(256), 0, s, g, rec,
+                     plane_off, rec2 ? *rec2 : rec, rec2 ? plane_off2 : plane_off, blocks);
 }
 
 }  // namespace tact
