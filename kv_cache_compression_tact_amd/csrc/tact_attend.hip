@@ -47,7 +47,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t att_rsrc(const void* base, int
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufWord3);
 }
 constexpr int kChunk = 256;       // bins per wave in k_att_out
-constexpr int kFieldThreads = 512;
+constexpr int kFieldThreads = 768;
 
 struct AttArgs {
   RecordView krec, vrec;
