@@ -792,8 +792,8 @@ def attend(k_rec: np.ndarray, v_rec: np.ndarray, p: Params, q: np.ndarray,
            quantizer: str = "lloyd_max"):
     """One decoding step of attention over one unit pair's visual tokens.
 
-    [Method/dec]: decoding reverses the codec and can be fused into the
-    attention kernel, so that the reconstructed cache is never materialized.
+    [Method/dec]: decoding reverses the codec, and the page allows it to run
+    inside attention, reading only the records with no decoded cache written.
     This is the plain definition of what such a kernel returns, written on
     the decoded cache itself (fp64, no output rounding).
     READING: q holds one query per query head, shape (q_heads, head_dim),

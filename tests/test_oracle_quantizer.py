@@ -252,3 +252,37 @@ def test_heavy_tails_hurt_absmax_backends_most():
         g = gains_absmax_f32(c)
         r = dequantize(quantize(c, g, bits, kind=kind), g, bits, kind=kind)
         assert np.mean((r - c) ** 2) / np.mean(c ** 2) > 1.2 * e_lm
+
+
+def test_absmax_gain_is_taken_after_the_rotation():
+    # The uniform and NormalFloat backends scale by the largest |value| of
+    # the vector they quantize, which with the rotation on is R u.  Two hand
+    # cases fix the order.  (1) A spike 8 e_5 in the first 64-block: every
+    # coordinate of R(8 e_5) = H_64 diag(s) 8 e_5 / 8 is s_5 H[j][5] = +-1,
+    # so the rotated gain is 1 while the unrotated one is 8.  (2) The
+    # vector c_j = s_j (-1)^popcount(j & 9) (all +-1) is R^T (8 e_9): its
+    # rotated image is 8 at coordinate 9 and 0 elsewhere, so the rotated
+    # gain is 8 while the unrotated one is 1.  The second 64-block carries
+    # the same pattern shifted, so each block is rotated on its own.
+    from oracle import gains_absmax_f32, rotation_signs
+    s = rotation_signs()
+    spike = np.zeros((2, 128))
+    spike[0, 5] = 8.0
+    spike[1, 64 + 5] = 8.0
+    np.testing.assert_array_equal(gains_absmax_f32(spike, "none"), [8.0, 8.0])
+    np.testing.assert_array_equal(gains_absmax_f32(spike, "hadamard"), [1.0, 1.0])
+    par = np.array([(-1.0) ** bin(j & 9).count("1") for j in range(64)])
+    flat = np.zeros((2, 128))
+    flat[0, :64] = s * par
+    flat[1, 64:] = s * par
+    flat[1, :64] = 0.5 * s * par          # a second block below the first
+    np.testing.assert_array_equal(gains_absmax_f32(flat, "none"), [1.0, 1.0])
+    np.testing.assert_array_equal(gains_absmax_f32(flat, "hadamard"), [8.0, 8.0])
+    # and the quantizer decides on the rotated vector scaled by that gain:
+    # at 1 bit the uniform grid has levels +-1/2 and its threshold at 0, so
+    # the codes of the spike are the signs of s_5 H[j][5]
+    from oracle import quantize
+    codes = quantize(spike[:1, :64], np.float32([1.0]), np.array([1]), "hadamard",
+                     kind="uniform")
+    hcol = np.array([(-1.0) ** bin(j & 5).count("1") for j in range(64)])
+    np.testing.assert_array_equal(codes[0], (s[5] * hcol > 0).astype(np.uint8))
