@@ -58,16 +58,27 @@ def _parse():
 
 
 def calibrate_copy():
-    """Three copies of exactly 1 GiB between device buffers, nothing else."""
+    """Three copies of exactly 1 GiB between device buffers, nothing else,
+    each timed with HIP events: the reference for scaling the byte counters
+    of a profile, and the plain copy rate of this device."""
     dev = torch.device("cuda:0")
     src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ms = []
     for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
         dst.copy_(src)
-    torch.cuda.synchronize()
+        b.record(stream)
+        b.synchronize()
+        ms.append(a.elapsed_time(b))
+    best = min(ms)
     print(json.dumps({"calibration": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
-                      "repeats": 3}), flush=True)
+                      "repeats": 3, "ms": [round(m, 4) for m in ms],
+                      "copy_GBs_read_plus_write": round(2 * (1 << 30) / (best * 1e-3) / 1e9, 1)}),
+          flush=True)
 
 
 def cpu_baseline(wl, budget, n_units):
@@ -91,12 +102,19 @@ def cpu_baseline(wl, budget, n_units):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover - threadpoolctl is optional
         threads = 1
+    cores = len(os.sched_getaffinity(0))
+    names = {(0, 0, 0): "layer 0 K", (0, 0, 1): "layer 0 V", (1, 0, 0): "layer 1 K",
+             (1, 0, 1): "layer 1 V"}
+    per_unit = dt / len(xs)
     return {
-        "value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+        "value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores,
         "kind": "oracle",
-        "sample": f"{len(xs)} units (layer 0/1, sequence 0, K and V) of {wl.name}, "
-                  f"compress+decompress in {dt:.2f} s; host has "
-                  f"{len(os.sched_getaffinity(0))} usable cores, BLAS threads {threads}",
+        "sample": f"{len(xs)} units ({', '.join(names[k] for k in keys)}; sequence 0) of "
+                  f"{wl.name}, compress+decompress in {dt:.2f} s; BLAS threads {threads}",
+        "blas_threads": int(threads),
+        "extrapolated_full_config_s": round(per_unit * wl.n_units, 1),
+        "extrapolated_note": f"linear in units: {per_unit:.2f} s per unit x {wl.n_units} units "
+                             "(extrapolated, not measured)",
     }
 
 
@@ -331,8 +349,10 @@ def main():
         "metric": "KV codec GB/s (compress+decompress, bf16 in) and % of HBM roofline at 1 GPU",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32", "data": "synthetic",
         "config": {"workload": wl.name, "units": U, "unit_shape": list(wl.unit_shape),
+                   "arithmetic": "fp32 accumulation, split-fp16 matrix-core products",
                    "cache_dtype": str(wl.dtype).replace("torch.", ""),
                    "budget_bits": budget, "max_bits": wl.max_bits,
                    "rotation": "hadamard" if g.rotation else "none",

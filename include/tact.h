@@ -165,9 +165,9 @@ tact_status tact_roundtrip(const tact_params* p, int64_t n_units,
                            size_t workspace_bytes, hipStream_t stream);
 
 /* ---- Decoding fused into attention --------------------------------------
- * The page's decoding paragraph ("Methodology in Plain English") notes that
- * decoding can be fused into the attention kernel, so that the reconstructed
- * cache is never materialized.  tact_attend runs one decoding step of
+ * The page's decoding paragraph ("Methodology in Plain English") allows the
+ * decoder to live inside the attention kernel: tact_attend reads only the
+ * records and writes no decoded cache.  It runs one decoding step of
  * attention over the visual tokens of n_pairs unit pairs -- the K record and
  * the V record of one layer and sequence, both coded with *p -- reading only
  * the records:

@@ -10,7 +10,7 @@ functions take and return torch tensors on the GPU:
 
 The library is loaded from this package's directory; importing this module
 without it raises ImportError (build it with
-``python -m kv_cache_compression_tact_amd.build``).  There is no fallback.
+``python kv_cache_compression_tact_amd/build.py``).  There is no fallback.
 """
 from __future__ import annotations
 
@@ -42,7 +42,7 @@ class TactParams(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m kv_cache_compression_tact_amd.build`")
+                          "`python kv_cache_compression_tact_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(TactParams)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
@@ -180,6 +180,42 @@ def _unit_stride(t: torch.Tensor) -> int:
     return t.stride(0) if t.shape[0] > 1 else unit
 
 
+def _check_cache(t: torch.Tensor, geom: Geometry, n_units: int, name: str):
+    """A cache tensor of the call: on the GPU, of the geometry's dtype and
+    unit shape, with at least n_units units."""
+    if t.dtype != geom.dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, the geometry's is {geom.dtype}")
+    if t.dim() != 6 or tuple(t.shape[1:]) != geom.unit_shape:
+        raise ValueError(f"{name} must be (units,) + {geom.unit_shape}, got {tuple(t.shape)}")
+    if t.shape[0] < n_units:
+        raise ValueError(f"{name} holds {t.shape[0]} units, the call covers {n_units}")
+
+
+def _check_records(r: torch.Tensor, geom: Geometry, n_units: int, name: str = "records"):
+    """Records of the call: contiguous uint8 (units, record_bytes) on the GPU,
+    at least n_units rows (the library reads and writes them back to back)."""
+    rb = geom.record_bytes()
+    if r.dtype != torch.uint8 or r.dim() != 2 or r.shape[1] != rb:
+        raise ValueError(f"{name} must be uint8 (units, {rb}), got {r.dtype} {tuple(r.shape)}")
+    if r.shape[0] < n_units:
+        raise ValueError(f"{name} holds {r.shape[0]} records, the call covers {n_units}")
+    if not r.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(**tensors):
+    """Every tensor the call passes to the library lives on the GPU (checked
+    after the shapes and types, so those errors come first)."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+
+
+def _check_ws(ws: torch.Tensor):
+    if not ws.is_cuda or ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("the workspace must be a contiguous uint8 tensor on the GPU")
+
+
 def workspace(geom: Geometry, n_units: int, device=None) -> torch.Tensor:
     n = geom.workspace_bytes(n_units)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device or "cuda")
@@ -194,10 +230,14 @@ def compress(kv: torch.Tensor, budget_bits: int, max_bits: int = 8, *,
     g = Geometry.of(kv, budget_bits, max_bits=max_bits, axes=axes, alloc_mode=alloc_mode,
                     rotation=rotation, quantizer=quantizer)
     U = kv.shape[0]
+    _check_cache(kv, g, U, "kv")
     if records is None:
         records = torch.empty((U, g.record_bytes()), dtype=torch.uint8, device=kv.device)
+    _check_records(records, g, U)
+    _on_gpu(kv=kv, records=records)
     if ws is None:
         ws = workspace(g, U, kv.device)
+    _check_ws(ws)
     p = g.params()
     _check(_lib.tact_compress(ctypes.byref(p), U, _ptr(kv), _unit_stride(kv),
                               _ptr(records), _ptr(ws), ws.numel(), _stream()),
@@ -209,10 +249,14 @@ def decompress(records: torch.Tensor, geom: Geometry, *, out: torch.Tensor | Non
                ws: torch.Tensor | None = None) -> torch.Tensor:
     """records uint8 (U, record_bytes) -> cache (U, S, H, W, Hkv, d) of geom.dtype."""
     U = records.shape[0]
+    _check_records(records, geom, U)
     if out is None:
         out = torch.empty((U,) + geom.unit_shape, dtype=geom.dtype, device=records.device)
+    _check_cache(out, geom, U, "out")
+    _on_gpu(records=records, out=out)
     if ws is None:
         ws = workspace(geom, U, records.device)
+    _check_ws(ws)
     p = geom.params()
     _check(_lib.tact_decompress(ctypes.byref(p), U, _ptr(records), _ptr(out),
                                 _unit_stride(out), _ptr(ws), ws.numel(), _stream()),
@@ -229,12 +273,18 @@ def roundtrip(kv: torch.Tensor, budget_bits: int, max_bits: int = 8, *,
     g = Geometry.of(kv, budget_bits, max_bits=max_bits, axes=axes, alloc_mode=alloc_mode,
                     rotation=rotation, quantizer=quantizer)
     U = kv.shape[0]
+    _check_cache(kv, g, U, "kv")
     if out is None:
         out = torch.empty_like(kv)
+    _check_cache(out, g, U, "out")
     if records is None and keep_records:
         records = torch.empty((U, g.record_bytes()), dtype=torch.uint8, device=kv.device)
+    if records is not None:
+        _check_records(records, g, U)
+    _on_gpu(kv=kv, out=out, records=records)
     if ws is None:
         ws = workspace(g, U, kv.device)
+    _check_ws(ws)
     p = g.params()
     _check(_lib.tact_roundtrip(ctypes.byref(p), U, _ptr(kv), _unit_stride(kv), _ptr(out),
                                _unit_stride(out), _ptr(records), _ptr(ws), ws.numel(),
@@ -264,8 +314,11 @@ def attend(k_records: torch.Tensor, v_records: torch.Tensor, geom: Geometry,
     P, qh, d = q.shape
     if d != geom.head_dim or k_records.shape[0] != P or v_records.shape[0] != P:
         raise ValueError("q must be (pairs, q_heads, head_dim) with one K and V record per pair")
-    if q.dtype != torch.float32 or not q.is_contiguous():
-        raise TypeError("q must be contiguous float32")
+    if q.dtype != torch.float32 or not q.is_contiguous() or not q.is_cuda:
+        raise TypeError("q must be contiguous float32 on the GPU")
+    _check_records(k_records, geom, P, "k_records")
+    _check_records(v_records, geom, P, "v_records")
+    _on_gpu(k_records=k_records, v_records=v_records)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     p = geom.params()
@@ -273,6 +326,7 @@ def attend(k_records: torch.Tensor, v_records: torch.Tensor, geom: Geometry,
     lse = torch.empty((P, qh), dtype=torch.float32, device=q.device)
     if ws is None:
         ws = attend_workspace(geom, P, qh, q.device)
+    _check_ws(ws)
     _check(_lib.tact_attend(ctypes.byref(p), P, qh, _ptr(k_records), _ptr(v_records), _ptr(q),
                             float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream()),
            "tact_attend")
@@ -325,7 +379,8 @@ def dbg_allocate(var: torch.Tensor, geom: Geometry) -> torch.Tensor:
     U = var.shape[0]
     bits = torch.empty((U,) + geom.unit_shape[:-1], dtype=torch.uint8, device=var.device)
     p = geom.params()
-    _check(_lib.tact_dbg_allocate(ctypes.byref(p), U, _ptr(var.contiguous()), _ptr(bits),
+    var_c = var.contiguous()          # held until the call has been enqueued
+    _check(_lib.tact_dbg_allocate(ctypes.byref(p), U, _ptr(var_c), _ptr(bits),
                                   _stream()), "tact_dbg_allocate")
     return bits
 
@@ -335,9 +390,10 @@ def dbg_quantize(coef: torch.Tensor, gains: torch.Tensor, bits: torch.Tensor,
     U = coef.shape[0]
     rec = torch.empty((U, geom.record_bytes()), dtype=torch.uint8, device=coef.device)
     p = geom.params()
-    _check(_lib.tact_dbg_quantize(ctypes.byref(p), U, _ptr(coef.contiguous()),
-                                  _ptr(gains.contiguous()), _ptr(bits.contiguous()),
-                                  _ptr(rec), _stream()), "tact_dbg_quantize")
+    # the contiguous copies are held until the call has been enqueued
+    coef_c, gains_c, bits_c = coef.contiguous(), gains.contiguous(), bits.contiguous()
+    _check(_lib.tact_dbg_quantize(ctypes.byref(p), U, _ptr(coef_c), _ptr(gains_c),
+                                  _ptr(bits_c), _ptr(rec), _stream()), "tact_dbg_quantize")
     return rec
 
 

@@ -1,6 +1,6 @@
 """Build step of the TACT-KV library: codebook generation and libtact.so.
 
-    python -m kv_cache_compression_tact_amd.build
+    python kv_cache_compression_tact_amd/build.py
 
 1. Compiles the codebook generator (csrc/gen_codebooks.cpp) with the host
    compiler and regenerates csrc/generated/codebooks.inc.
@@ -52,11 +52,23 @@ def gen_codebooks() -> None:
 
 
 def build_library() -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Every source compiled to an object in parallel (hipcc per file), then
+    linked into the shared library."""
+    os.makedirs(BUILD, exist_ok=True)
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmd = [HIPCC, *HIP_FLAGS, "-c", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+               os.path.join(CSRC, src), "-o", obj]
+        print("+", " ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd))
+    failed = [src for src, pr in zip(SOURCES, procs) if pr.wait() != 0]
+    if failed:
+        raise RuntimeError(f"hipcc failed on {failed}")
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *HIP_FLAGS, "-shared", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *srcs, "-o", tmp]
-    _run(cmd, stderr=subprocess.STDOUT if False else None)
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

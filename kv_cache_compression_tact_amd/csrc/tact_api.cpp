@@ -32,11 +32,15 @@ tact_status ok() {
   return TACT_OK;
 }
 
-// Upper bound on the workspace one chunk of units may use; batches larger
-// than a chunk are processed chunk by chunk on the same stream.  Sized for
-// the 288 GB of HBM of an MI355X: whole launches of the large workloads fit
-// in one chunk, so every kernel runs once over all units.
-constexpr int64_t kChunkWorkspaceBytes = int64_t(24) << 30;
+int64_t elem_size(int dtype) { return dtype == TACT_F32 ? 4 : 2; }
+
+// Units of one chunk are at most this many (the kernels index units of a
+// launch in 16 bits of the grid).  Batches are processed chunk by chunk on
+// the same stream; the chunk is as many units as the caller's workspace
+// holds, so tact_workspace_bytes(p, n) (room for all n units) runs every
+// kernel once over the whole batch, and any smaller workspace that holds one
+// unit is accepted.
+constexpr int64_t kMaxChunkUnits = 65535;
 
 tact_status make_geometry(const tact_params* p, Geometry* g) {
   if (!p) return fail(TACT_ERR_INVALID_ARGUMENT, "params is NULL");
@@ -93,7 +97,6 @@ tact_status make_geometry(const tact_params* p, Geometry* g) {
   return TACT_OK;
 }
 
-int64_t elem_size(int dtype) { return dtype == TACT_F32 ? 4 : 2; }
 
 // Workspace of the codec calls: DCT tables once, then per unit of a chunk an
 // fp32 intermediate volume, fp32 variances, fp32 reciprocal gains, uint32
@@ -112,15 +115,18 @@ int64_t unit_ws_bytes(const Geometry& g) {
 
 constexpr int64_t kTableBytes = align256(4 * kDctTableFloats);
 
-int64_t chunk_units(const Geometry& g, int64_t n_units) {
-  int64_t c = kChunkWorkspaceBytes / unit_ws_bytes(g);
-  if (c < 1) c = 1;
-  if (c > 65535) c = 65535;
-  return n_units < c ? n_units : c;
+// Workspace for a chunk of `chunk` units.
+int64_t ws_bytes(const Geometry& g, int64_t chunk) {
+  return kTableBytes + chunk * unit_ws_bytes(g);
 }
 
-int64_t ws_bytes(const Geometry& g, int64_t n_units) {
-  return kTableBytes + chunk_units(g, n_units) * unit_ws_bytes(g);
+// Units per chunk that a workspace of `bytes` bytes holds (at least 1: the
+// caller has checked that one unit fits), at most n_units.
+int64_t chunk_units(const Geometry& g, int64_t n_units, size_t bytes) {
+  int64_t c = (static_cast<int64_t>(bytes) - kTableBytes) / unit_ws_bytes(g);
+  if (c < 1) c = 1;
+  if (c > kMaxChunkUnits) c = kMaxChunkUnits;
+  return n_units < c ? n_units : c;
 }
 
 struct Workspace {
@@ -177,13 +183,28 @@ tact_status check_buffer(const void* ptr, const char* name, uintptr_t align) {
   return TACT_OK;
 }
 
-tact_status check_workspace(const Geometry& g, int64_t n_units, const void* ws, size_t bytes) {
-  const int64_t need = ws_bytes(g, n_units);
+// The workspace must hold one unit; a larger one lets more units share each
+// launch (see chunk_units).
+tact_status check_workspace(const Geometry& g, const void* ws, size_t bytes) {
+  const int64_t need = ws_bytes(g, 1);
   if (!ws) return fail(TACT_ERR_WORKSPACE, "workspace is NULL (%lld bytes needed)", (long long)need);
   if (!aligned(ws, 256)) return fail(TACT_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
   if (static_cast<int64_t>(bytes) < need)
-    return fail(TACT_ERR_WORKSPACE, "workspace of %zu bytes, %lld needed", bytes, (long long)need);
+    return fail(TACT_ERR_WORKSPACE, "workspace of %zu bytes, at least %lld needed (one unit)",
+                bytes, (long long)need);
   return TACT_OK;
+}
+
+// Byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uint8_t* x = static_cast<const uint8_t*>(a);
+  const uint8_t* y = static_cast<const uint8_t*>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Bytes spanned by n_units unit tensors `stride` elements apart.
+int64_t tensor_span(const Geometry& g, int64_t n_units, int64_t stride) {
+  return ((n_units - 1) * stride + g.n_entries) * elem_size(g.dtype);
 }
 
 tact_status after_launch(const char* what) {
@@ -382,7 +403,7 @@ size_t tact_workspace_bytes(const tact_params* p, int64_t n_units) {
   Geometry g;
   if (make_geometry(p, &g) != TACT_OK) return 0;
   if (n_units <= 0) return 0;
-  return static_cast<size_t>(ws_bytes(g, n_units));
+  return static_cast<size_t>(ws_bytes(g, n_units < kMaxChunkUnits ? n_units : kMaxChunkUnits));
 }
 
 tact_status tact_compress(const tact_params* p, int64_t n_units, const void* kv,
@@ -395,8 +416,16 @@ tact_status tact_compress(const tact_params* p, int64_t n_units, const void* kv,
   if (n_units == 0) return ok();
   if ((st = check_tensor(g, kv, kv_unit_stride, "kv")) != TACT_OK) return st;
   if ((st = check_buffer(records, "records", 256)) != TACT_OK) return st;
-  if ((st = check_workspace(g, n_units, workspace, workspace_bytes)) != TACT_OK) return st;
-  const int64_t chunk = chunk_units(g, n_units);
+  if ((st = check_workspace(g, workspace, workspace_bytes)) != TACT_OK) return st;
+  {
+    const int64_t kv_span = tensor_span(g, n_units, kv_unit_stride);
+    const int64_t rec_span = n_units * g.record_bytes;
+    if (overlap(kv, kv_span, records, rec_span) ||
+        overlap(kv, kv_span, workspace, static_cast<int64_t>(workspace_bytes)) ||
+        overlap(records, rec_span, workspace, static_cast<int64_t>(workspace_bytes)))
+      return fail(TACT_ERR_INVALID_ARGUMENT, "kv, records and workspace must not overlap");
+  }
+  const int64_t chunk = chunk_units(g, n_units, workspace_bytes);
   const Workspace w = carve(g, chunk, workspace);
   const int64_t es = elem_size(g.dtype);
   launch_dct_tables(g, w.tab, stream);
@@ -419,8 +448,16 @@ tact_status tact_decompress(const tact_params* p, int64_t n_units, const void* r
   if (n_units == 0) return ok();
   if ((st = check_buffer(records, "records", 256)) != TACT_OK) return st;
   if ((st = check_tensor(g, kv_out, out_unit_stride, "kv_out")) != TACT_OK) return st;
-  if ((st = check_workspace(g, n_units, workspace, workspace_bytes)) != TACT_OK) return st;
-  const int64_t chunk = chunk_units(g, n_units);
+  if ((st = check_workspace(g, workspace, workspace_bytes)) != TACT_OK) return st;
+  {
+    const int64_t out_span = tensor_span(g, n_units, out_unit_stride);
+    const int64_t rec_span = n_units * g.record_bytes;
+    if (overlap(kv_out, out_span, records, rec_span) ||
+        overlap(kv_out, out_span, workspace, static_cast<int64_t>(workspace_bytes)) ||
+        overlap(records, rec_span, workspace, static_cast<int64_t>(workspace_bytes)))
+      return fail(TACT_ERR_INVALID_ARGUMENT, "records, kv_out and workspace must not overlap");
+  }
+  const int64_t chunk = chunk_units(g, n_units, workspace_bytes);
   const Workspace w = carve(g, chunk, workspace);
   const int64_t es = elem_size(g.dtype);
   launch_dct_tables(g, w.tab, stream);
@@ -445,15 +482,29 @@ tact_status tact_roundtrip(const tact_params* p, int64_t n_units, const void* kv
   if ((st = check_tensor(g, kv, kv_unit_stride, "kv")) != TACT_OK) return st;
   if ((st = check_tensor(g, kv_out, out_unit_stride, "kv_out")) != TACT_OK) return st;
   if (records && (st = check_buffer(records, "records", 256)) != TACT_OK) return st;
-  if ((st = check_workspace(g, n_units, workspace, workspace_bytes)) != TACT_OK) return st;
-  if (kv_out != kv && kv_unit_stride == out_unit_stride) {
-    const uint8_t* a = static_cast<const uint8_t*>(kv);
-    const uint8_t* b = static_cast<const uint8_t*>(kv_out);
-    const int64_t span = n_units * kv_unit_stride * elem_size(g.dtype);
-    if (a < b + span && b < a + span)
+  if ((st = check_workspace(g, workspace, workspace_bytes)) != TACT_OK) return st;
+  {
+    // in place (kv_out == kv) only with equal strides: a chunk's output
+    // must not land on input units of a later chunk
+    const int64_t kv_span = tensor_span(g, n_units, kv_unit_stride);
+    const int64_t out_span = tensor_span(g, n_units, out_unit_stride);
+    const int64_t wsb = static_cast<int64_t>(workspace_bytes);
+    if (kv_out == kv) {
+      if (kv_unit_stride != out_unit_stride)
+        return fail(TACT_ERR_INVALID_ARGUMENT,
+                    "in-place round trip (kv_out == kv) needs equal unit strides (%lld, %lld)",
+                    (long long)kv_unit_stride, (long long)out_unit_stride);
+    } else if (overlap(kv, kv_span, kv_out, out_span)) {
       return fail(TACT_ERR_INVALID_ARGUMENT, "kv and kv_out overlap without being equal");
+    }
+    const int64_t rec_span = records ? n_units * g.record_bytes : 0;
+    if (overlap(kv, kv_span, workspace, wsb) || overlap(kv_out, out_span, workspace, wsb) ||
+        (records && (overlap(records, rec_span, kv, kv_span) ||
+                     overlap(records, rec_span, kv_out, out_span) ||
+                     overlap(records, rec_span, workspace, wsb))))
+      return fail(TACT_ERR_INVALID_ARGUMENT, "kv, kv_out, records and workspace must not overlap");
   }
-  const int64_t chunk = chunk_units(g, n_units);
+  const int64_t chunk = chunk_units(g, n_units, workspace_bytes);
   const Workspace w = carve(g, chunk, workspace);
   const int64_t es = elem_size(g.dtype);
   launch_dct_tables(g, w.tab, stream);

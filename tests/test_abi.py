@@ -104,16 +104,28 @@ def test_null_and_misaligned_pointers_rejected():
     # unit stride below the unit size or not a multiple of 8
     assert L.tact_compress(ctypes.byref(p), 2, fake, 32767, fake, fake, ws, None) == 1
     assert L.tact_compress(ctypes.byref(p), 2, fake, 32772, fake, fake, ws, None) == 1
-    # workspace missing / too small
-    assert L.tact_compress(ctypes.byref(p), 2, fake, 32768, fake, None, ws, None) == 3
-    assert L.tact_compress(ctypes.byref(p), 2, fake, 32768, fake, fake, ws - 1, None) == 3
-    assert L.tact_decompress(ctypes.byref(p), 2, fake, fake, 32768, fake, ws - 1, None) == 3
-    assert L.tact_compress(ctypes.byref(p), -1, fake, 32768, fake, fake, ws, None) == 1
+    # workspace missing / too small: it must hold at least one unit (a
+    # smaller workspace than tact_workspace_bytes(p, n) splits the batch)
+    ws1 = L.tact_workspace_bytes(ctypes.byref(p), 1)
+    assert 0 < ws1 < ws
+    kv, rec, wsp = (ctypes.c_void_p(a << 30) for a in (1, 2, 3))   # disjoint fake buffers
+    assert L.tact_compress(ctypes.byref(p), 2, kv, 32768, rec, None, ws, None) == 3
+    assert L.tact_compress(ctypes.byref(p), 2, kv, 32768, rec, wsp, ws1 - 1, None) == 3
+    assert L.tact_decompress(ctypes.byref(p), 2, rec, kv, 32768, wsp, ws1 - 1, None) == 3
+    assert L.tact_compress(ctypes.byref(p), -1, kv, 32768, rec, wsp, ws, None) == 1
     # overlapping but distinct in/out for the round trip
-    assert L.tact_roundtrip(ctypes.byref(p), 2, fake, 32768,
-                            ctypes.c_void_p((1 << 20) + 4096), 32768, None, fake, ws,
+    assert L.tact_roundtrip(ctypes.byref(p), 2, kv, 32768,
+                            ctypes.c_void_p((1 << 30) + 4096), 32768, None, wsp, ws,
                             None) == 1
-    assert L.tact_compress(None, 2, fake, 32768, fake, fake, ws, None) == 1
+    # in place with unequal strides: a later chunk's input would be overwritten
+    assert L.tact_roundtrip(ctypes.byref(p), 2, kv, 32768, kv, 65536, None, wsp, ws, None) == 1
+    assert b"equal unit strides" in L.tact_last_error()
+    # records over the cache, the workspace over the records
+    assert L.tact_compress(ctypes.byref(p), 2, kv, 32768, ctypes.c_void_p((1 << 30) + 1024),
+                           wsp, ws, None) == 1
+    assert L.tact_decompress(ctypes.byref(p), 2, rec, kv, 32768,
+                             ctypes.c_void_p((2 << 30) + 256), ws, None) == 1
+    assert L.tact_compress(None, 2, kv, 32768, rec, wsp, ws, None) == 1
 
 
 def test_stage_quantizers_refuse_the_rotation():
@@ -174,8 +186,8 @@ def test_library_codebook_equals_oracle_table():
 def test_valid_call_without_device_reports_hip_error():
     p = _params()
     ws = lib().tact_workspace_bytes(ctypes.byref(p), 1)
-    fake = ctypes.c_void_p(1 << 20)
-    st = lib().tact_compress(ctypes.byref(p), 1, fake, 32768, fake, fake, ws, None)
+    kv, rec, wsp = (ctypes.c_void_p(a << 30) for a in (1, 2, 3))   # disjoint fake buffers
+    st = lib().tact_compress(ctypes.byref(p), 1, kv, 32768, rec, wsp, ws, None)
     assert st == 4
     assert b"tact_compress" in lib().tact_last_error()
 
@@ -212,3 +224,28 @@ def test_attend_validation():
     assert L.tact_attend(ctypes.byref(p), -1, 4, *args, None) == 1
     assert L.tact_attend(ctypes.byref(p), 0, 4, None, None, None, 1.0, None, None, None, 0,
                          None) == 0
+
+
+def test_binding_rejects_mismatched_tensors_before_any_launch():
+    # the checks run on the host before the library is called, so CPU
+    # tensors stand in for device ones here
+    g = tact.Geometry(4, 8, 8, 2, 64, 1, max_bits=3, dtype=torch.float32)
+    rb = g.record_bytes()
+    rec = torch.zeros((2, rb), dtype=torch.uint8)
+    with pytest.raises(TypeError, match="dtype"):
+        tact.decompress(rec, g, out=torch.empty((2,) + g.unit_shape, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="units"):
+        tact.decompress(rec, g, out=torch.empty((1,) + g.unit_shape, dtype=torch.float32))
+    with pytest.raises(ValueError, match="uint8"):
+        tact.decompress(rec[:, :-1], g)
+    with pytest.raises(ValueError, match="uint8"):
+        tact.decompress(rec.view(torch.int8), g)
+    with pytest.raises(ValueError, match="contiguous"):
+        tact.decompress(torch.zeros((2, 2 * rb), dtype=torch.uint8)[:, ::2], g)
+    kv = torch.zeros((2,) + g.unit_shape, dtype=torch.float32)
+    with pytest.raises(ValueError, match="records"):
+        tact.compress(kv, 1, 3, records=torch.zeros((1, rb), dtype=torch.uint8))
+    with pytest.raises(TypeError, match="dtype"):
+        tact.roundtrip(kv, 1, 3, out=torch.empty((2,) + g.unit_shape, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="GPU"):
+        tact.compress(kv, 1, 3)
