@@ -68,28 +68,6 @@ __global__ void k_dct_tables(float* __restrict__ tab, int n0, int n1, int n2, in
 }
 
 
-// max over the 4 lane groups that hold the K ranges of one column: the
-// permlane swaps exchange lanes l and l ^ 32 (then l ^ 16) between two
-// copies of v, so the max of the two results is the pairwise max
-__device__ __forceinline__ float column_max(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const uint32_t w = __float_as_uint(m);
-  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-// Sum over the 16 lanes of each row (every lane gets the row sum): adds of
-// rotated copies (DPP row rotate by 8, 4, 2, 1).
-__device__ __forceinline__ float row_sum16(float x) {
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, true));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xF, 0xF, true));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xF, 0xF, true));
-  return x;
-}
-
 __device__ __forceinline__ uint16_t bf16_rne_bits(float v) {
   const uint32_t u = __float_as_uint(v);
   return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
@@ -102,62 +80,7 @@ __device__ __forceinline__ uint16_t bf16_rne_bits(float v) {
 // register bits (4 values per lane).
 // ---------------------------------------------------------------------------
 #include "tact_rotation.h"
-
-// Partner values across the lanes of a 16-lane row: lane ^ 1, ^ 2 (quad
-// permutes), ^ 4 (swizzle, bit mask mode), ^ 8 (row rotate by 8).
-__device__ __forceinline__ float lane_xor1(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float lane_xor2(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float lane_xor4(float x) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
-}
-__device__ __forceinline__ float lane_xor8(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));
-}
-
-// Per-lane constants of the 16-point butterflies: sg[k] = -1 where lane bit
-// k is set; the product of the four is the sign the butterflies leave.
-struct LaneWht {
-  float sg[4];
-  float parity;    // (-1)^popcount(lane & 15)
-  float parity8;   // (-1)^popcount(lane & 7)
-  __device__ __forceinline__ explicit LaneWht(int lane) {
-    parity = 1.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      sg[k] = ((lane >> k) & 1) ? -1.f : 1.f;
-      parity *= sg[k];
-      if (k == 2) parity8 = parity;
-    }
-  }
-};
-
-// In-register butterflies over the 2 register bits, then the 4 lane
-// butterflies.  A lane butterfly keeps x + sg * x_partner: where the lane
-// bit is set that is x_self - x_partner, minus the Sylvester value, and the
-// partner carries the same sign history, so the result is
-// parity * (H_64 x) for each of the 4 values.
-__device__ __forceinline__ void wht64(float& a0, float& a1, float& a2, float& a3,
-                                      const LaneWht& w) {
-  float b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;
-  a0 = b0 + b2;
-  a2 = b0 - b2;
-  a1 = b1 + b3;
-  a3 = b1 - b3;
-  float* v[4] = {&a0, &a1, &a2, &a3};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float x = *v[q];
-    x = fmaf(lane_xor1(x), w.sg[0], x);
-    x = fmaf(lane_xor2(x), w.sg[1], x);
-    x = fmaf(lane_xor4(x), w.sg[2], x);
-    x = fmaf(lane_xor8(x), w.sg[3], x);
-    *v[q] = x;
-  }
-}
+#include "tact_lane_ops.h"
 
 // Raw buffer access (descriptor word 3 of gfx9 raw buffers): loads past
 // the descriptor's byte range return 0 and stores past it are dropped, so
@@ -916,47 +839,6 @@ struct PlaneWalk {
     return slice < n_slices ? static_cast<int64_t>(slice * n_slabs + k % n_slabs) : -1;
   }
 };
-
-// DCT fragments of one contraction (hi / lo per lane) kept in LDS: built
-// once per block, read back right before each contraction
-template <int NP>
-struct FragLds {
-  typename Frag<NP>::vec v[Frag<NP>::MT][Frag<NP>::KSTEPS][2][kWave];
-};
-
-template <int NP>
-__device__ __forceinline__ void frag_to_lds(FragLds<NP>& f, const float* tab, int inverse, int lane) {
-  typename Frag<NP>::vec hi[Frag<NP>::MT][Frag<NP>::KSTEPS], lo[Frag<NP>::MT][Frag<NP>::KSTEPS];
-  load_afrag<NP>(tab, inverse, lane % 16, lane / 16, hi, lo);
-#pragma unroll
-  for (int m = 0; m < Frag<NP>::MT; ++m)
-#pragma unroll
-    for (int ks = 0; ks < Frag<NP>::KSTEPS; ++ks) {
-      f.v[m][ks][0][lane] = hi[m][ks];
-      f.v[m][ks][1][lane] = lo[m][ks];
-    }
-}
-
-// lane offset hidden from the optimizer, so that the fragment reads stay
-// next to their contraction instead of being hoisted into registers
-__device__ __forceinline__ int opaque(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
-template <int NP>
-__device__ __forceinline__ void frag_from_lds(const FragLds<NP>& f, int lane,
-                                              typename Frag<NP>::vec (&hi)[Frag<NP>::MT][Frag<NP>::KSTEPS],
-                                              typename Frag<NP>::vec (&lo)[Frag<NP>::MT][Frag<NP>::KSTEPS]) {
-  const int l = opaque(lane);
-#pragma unroll
-  for (int m = 0; m < Frag<NP>::MT; ++m)
-#pragma unroll
-    for (int ks = 0; ks < Frag<NP>::KSTEPS; ++ks) {
-      hi[m][ks] = f.v[m][ks][0][l];
-      lo[m][ks] = f.v[m][ks][1][l];
-    }
-}
 
 // plane p -> (unit, slice s, 64-channel slab): slab fastest
 struct PlaneId {

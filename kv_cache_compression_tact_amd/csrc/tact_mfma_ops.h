@@ -104,4 +104,45 @@ __device__ __forceinline__ void load_afrag(const float* tab, int inverse, int t,
       }
 }
 
+// DCT fragments of one contraction (hi / lo per lane) kept in LDS: built
+// once per block, read back right before each contraction
+template <int NP>
+struct FragLds {
+  typename Frag<NP>::vec v[Frag<NP>::MT][Frag<NP>::KSTEPS][2][kWave];
+};
+
+template <int NP>
+__device__ __forceinline__ void frag_to_lds(FragLds<NP>& f, const float* tab, int inverse, int lane) {
+  typename Frag<NP>::vec hi[Frag<NP>::MT][Frag<NP>::KSTEPS], lo[Frag<NP>::MT][Frag<NP>::KSTEPS];
+  load_afrag<NP>(tab, inverse, lane % 16, lane / 16, hi, lo);
+#pragma unroll
+  for (int m = 0; m < Frag<NP>::MT; ++m)
+#pragma unroll
+    for (int ks = 0; ks < Frag<NP>::KSTEPS; ++ks) {
+      f.v[m][ks][0][lane] = hi[m][ks];
+      f.v[m][ks][1][lane] = lo[m][ks];
+    }
+}
+
+// lane offset hidden from the optimizer, so that the fragment reads stay
+// next to their contraction instead of being hoisted into registers
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+template <int NP>
+__device__ __forceinline__ void frag_from_lds(const FragLds<NP>& f, int lane,
+                                              typename Frag<NP>::vec (&hi)[Frag<NP>::MT][Frag<NP>::KSTEPS],
+                                              typename Frag<NP>::vec (&lo)[Frag<NP>::MT][Frag<NP>::KSTEPS]) {
+  const int l = opaque(lane);
+#pragma unroll
+  for (int m = 0; m < Frag<NP>::MT; ++m)
+#pragma unroll
+    for (int ks = 0; ks < Frag<NP>::KSTEPS; ++ks) {
+      hi[m][ks] = f.v[m][ks][0][l];
+      lo[m][ks] = f.v[m][ks][1][l];
+    }
+}
+
 #endif  // TACT_MFMA_OPS_H_
