@@ -181,8 +181,7 @@ def bench_ablations(args, tact, wl, budget, g, x):
     }
     res = {name: round(err(**kw), 6) for name, kw in variants.items()}
     # Theorem 1: D_uniform / D_waterfill against 1 / gamma, per unit
-    coef = tact.dbg_dct3(xs, g)
-    var = tact.dbg_bin_variance(coef, g).double().reshape(n, -1).clamp_min(1e-300)
+    var = tact.dbg_bin_variance(xs.contiguous(), g).double().reshape(n, -1).clamp_min(1e-300)
     gamma = torch.exp(torch.log(var).mean(1)) / var.mean(1)
     out_w, _ = tact.roundtrip(xs, budget, wl.max_bits, keep_records=False)
     out_u, _ = tact.roundtrip(xs, budget, wl.max_bits, keep_records=False,

@@ -61,11 +61,10 @@ def _load():
         "tact_attend": (i32, [P, i64, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]),
         "tact_dbg_workspace_bytes": (sz, [P, i64]),
         "tact_dbg_dct3": (i32, [P, i64, i32, vp, vp, vp, sz, vp]),
-        "tact_dbg_bin_variance": (i32, [P, i64, vp, vp, vp]),
+        "tact_dbg_bin_variance": (i32, [P, i64, vp, vp, vp, sz, vp]),
         "tact_dbg_allocate": (i32, [P, i64, vp, vp, vp]),
-        "tact_dbg_quantize": (i32, [P, i64, vp, vp, vp, vp, vp]),
-        "tact_dbg_unpack": (i32, [P, i64, vp, vp, vp]),
-        "tact_dbg_dequantize": (i32, [P, i64, vp, vp, vp]),
+        "tact_dbg_quantize": (i32, [P, i64, vp, vp, vp, vp, sz, vp]),
+        "tact_dbg_dequantize": (i32, [P, i64, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -80,8 +79,7 @@ EXPORTED = ("tact_params_init", "tact_record_bytes", "tact_workspace_bytes",
             "tact_status_string", "tact_last_error", "tact_codebook", "tact_quantizer_table",
             "tact_attend_workspace_bytes", "tact_attend",
             "tact_dbg_workspace_bytes", "tact_dbg_dct3", "tact_dbg_bin_variance",
-            "tact_dbg_allocate", "tact_dbg_quantize", "tact_dbg_unpack",
-            "tact_dbg_dequantize")
+            "tact_dbg_allocate", "tact_dbg_quantize", "tact_dbg_dequantize")
 
 
 def lib():
@@ -355,61 +353,91 @@ def codebook(bits: int):
 
 
 # ---- stage entry points ----------------------------------------------------
-def dbg_dct3(x: torch.Tensor, geom: Geometry, inverse: bool = False) -> torch.Tensor:
-    U = x.shape[0]
-    out = torch.empty((U,) + geom.unit_shape, dtype=torch.float32, device=x.device)
+# Each runs the codec's own kernels up to (or from) one step of the method;
+# the tensors are packed units on the GPU.
+def _dbg_ws(geom: Geometry, n_units: int, device) -> torch.Tensor:
     p = geom.params()
-    nws = _lib.tact_dbg_workspace_bytes(ctypes.byref(p), U)
-    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=x.device)
+    n = _lib.tact_dbg_workspace_bytes(ctypes.byref(p), n_units)
+    if n == 0:
+        raise ValueError(f"no stage workspace for {n_units} units of {geom}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _check_packed(t: torch.Tensor, shape, dtype, name: str):
+    if not t.is_cuda or t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} GPU tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def dbg_dct3(x: torch.Tensor, geom: Geometry, inverse: bool = False) -> torch.Tensor:
+    """Forward: the fp32 coefficients of the cache tensors x (the geometry's
+    dtype) as the coding passes compute them, without the rotation.
+    Inverse: the fp32 inverse transform of fp32 coefficients x."""
+    U = x.shape[0]
+    _check_packed(x, (U,) + geom.unit_shape, torch.float32 if inverse else geom.dtype, "x")
+    out = torch.empty((U,) + geom.unit_shape, dtype=torch.float32, device=x.device)
+    if U == 0:
+        return out
+    p = geom.params()
+    ws = _dbg_ws(geom, U, x.device)
     _check(_lib.tact_dbg_dct3(ctypes.byref(p), U, 1 if inverse else 0, _ptr(x), _ptr(out),
                               _ptr(ws), ws.numel(), _stream()), "tact_dbg_dct3")
     return out
 
 
-def dbg_bin_variance(coef: torch.Tensor, geom: Geometry) -> torch.Tensor:
-    U = coef.shape[0]
-    var = torch.empty((U,) + geom.unit_shape[:-1], dtype=torch.float32, device=coef.device)
+def dbg_bin_variance(x: torch.Tensor, geom: Geometry) -> torch.Tensor:
+    """Per-bin variances of the cache tensors x, as the allocation reads them."""
+    U = x.shape[0]
+    _check_packed(x, (U,) + geom.unit_shape, geom.dtype, "x")
+    var = torch.empty((U,) + geom.unit_shape[:-1], dtype=torch.float32, device=x.device)
+    if U == 0:
+        return var
     p = geom.params()
-    _check(_lib.tact_dbg_bin_variance(ctypes.byref(p), U, _ptr(coef), _ptr(var), _stream()),
-           "tact_dbg_bin_variance")
+    ws = _dbg_ws(geom, U, x.device)
+    _check(_lib.tact_dbg_bin_variance(ctypes.byref(p), U, _ptr(x), _ptr(var), _ptr(ws),
+                                      ws.numel(), _stream()), "tact_dbg_bin_variance")
     return var
 
 
 def dbg_allocate(var: torch.Tensor, geom: Geometry) -> torch.Tensor:
+    """Bit widths of every bin from fp32 variances (units, S, H, W, kv_heads)."""
     U = var.shape[0]
+    _check_packed(var, (U,) + geom.unit_shape[:-1], torch.float32, "var")
     bits = torch.empty((U,) + geom.unit_shape[:-1], dtype=torch.uint8, device=var.device)
+    if U == 0:
+        return bits
     p = geom.params()
-    var_c = var.contiguous()          # held until the call has been enqueued
-    _check(_lib.tact_dbg_allocate(ctypes.byref(p), U, _ptr(var_c), _ptr(bits),
+    _check(_lib.tact_dbg_allocate(ctypes.byref(p), U, _ptr(var), _ptr(bits),
                                   _stream()), "tact_dbg_allocate")
     return bits
 
 
-def dbg_quantize(coef: torch.Tensor, gains: torch.Tensor, bits: torch.Tensor,
-                 geom: Geometry) -> torch.Tensor:
+def dbg_quantize(coef: torch.Tensor, var: torch.Tensor, geom: Geometry) -> torch.Tensor:
+    """Records of fp32 coefficients, coded as given, with the allocation of
+    fp32 variances var (units, S, H, W, kv_heads)."""
     U = coef.shape[0]
+    _check_packed(coef, (U,) + geom.unit_shape, torch.float32, "coef")
+    _check_packed(var, (U,) + geom.unit_shape[:-1], torch.float32, "var")
     rec = torch.empty((U, geom.record_bytes()), dtype=torch.uint8, device=coef.device)
+    if U == 0:
+        return rec
     p = geom.params()
-    # the contiguous copies are held until the call has been enqueued
-    coef_c, gains_c, bits_c = coef.contiguous(), gains.contiguous(), bits.contiguous()
-    _check(_lib.tact_dbg_quantize(ctypes.byref(p), U, _ptr(coef_c), _ptr(gains_c),
-                                  _ptr(bits_c), _ptr(rec), _stream()), "tact_dbg_quantize")
+    ws = _dbg_ws(geom, U, coef.device)
+    _check(_lib.tact_dbg_quantize(ctypes.byref(p), U, _ptr(coef), _ptr(var), _ptr(rec),
+                                  _ptr(ws), ws.numel(), _stream()), "tact_dbg_quantize")
     return rec
 
 
-def dbg_unpack(records: torch.Tensor, geom: Geometry) -> torch.Tensor:
-    U = records.shape[0]
-    codes = torch.empty((U,) + geom.unit_shape, dtype=torch.uint8, device=records.device)
-    p = geom.params()
-    _check(_lib.tact_dbg_unpack(ctypes.byref(p), U, _ptr(records), _ptr(codes), _stream()),
-           "tact_dbg_unpack")
-    return codes
-
-
 def dbg_dequantize(records: torch.Tensor, geom: Geometry) -> torch.Tensor:
+    """fp32 g * level[code] of every coefficient of the records, by the first
+    decoding kernel (identity matrices in place of the DCT)."""
     U = records.shape[0]
+    _check_packed(records, (U, geom.record_bytes()), torch.uint8, "records")
     coef = torch.empty((U,) + geom.unit_shape, dtype=torch.float32, device=records.device)
+    if U == 0:
+        return coef
     p = geom.params()
-    _check(_lib.tact_dbg_dequantize(ctypes.byref(p), U, _ptr(records), _ptr(coef),
-                                    _stream()), "tact_dbg_dequantize")
+    ws = _dbg_ws(geom, U, records.device)
+    _check(_lib.tact_dbg_dequantize(ctypes.byref(p), U, _ptr(records), _ptr(coef), _ptr(ws),
+                                    ws.numel(), _stream()), "tact_dbg_dequantize")
     return coef

@@ -29,7 +29,7 @@ HIP_FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Wall", "-Wno-unused-function",
 ]
-SOURCES = ["tact_api.cpp", "tact_kernels.hip", "tact_mfma.hip", "tact_quant.hip",
+SOURCES = ["tact_api.cpp", "tact_codebooks.cpp", "tact_mfma.hip", "tact_quant.hip",
            "tact_attend.hip"]
 
 

@@ -236,29 +236,37 @@ int forward_axes(const Geometry& g, int* ax) {
   return m;
 }
 
-// compress `cn` units: kv chunk -> records chunk.  All axes but the last run
-// forward into the fp32 volume; the last axis runs twice, first producing
-// the per-bin variances, then (after the allocation) the codes.
-void compress_chunk(const Geometry& g, int64_t cn, const void* kv, int64_t kv_stride,
-                    uint8_t* recs, const Workspace& w, hipStream_t s) {
+// The fused layout: S on the matrix cores into the fp32 volume, then H and W
+// together in LDS (tact_mfma.hip k_plane), coding in one streaming pass
+// (tact_quant.hip).  Other geometries run the axes as separate passes.
+bool fused_path(const Geometry& g) {
+  return g.axes == TACT_AXES_ALL && plane_supported(g) && g.quantizer == TACT_QUANT_LLOYD_MAX;
+}
+
+// Where the forward stage leaves the per-bin sums of squares.
+struct StatsLayout {
+  int parts;      // partial sums per bin
+  bool planes;    // stored plane by plane ([slab][s][kh][kw]) rather than per bin
+};
+
+// Stage 2 and the sums of stage 3 for `cn` units.  Fused path: the S pass
+// writes the fp32 volume (and applies the quantizer's rotation to its output:
+// the rotation acts on the channels, so it commutes with the H and W axes and
+// leaves the bin variances unchanged); the plane pass replaces the volume by
+// the final coefficients and writes the partial sums.  Otherwise every axis
+// but the last runs forward into the volume, and the last one runs with the
+// sums-of-squares epilogue (no coefficients are written).  In both cases
+// w.var then holds what the allocation reads.
+StatsLayout forward_stats(const Geometry& g, int64_t cn, const void* kv, int64_t kv_stride,
+                          const Workspace& w, hipStream_t s) {
   const RecordView none{};
   const int in_pro = g.dtype == TACT_BF16 ? AX_PRO_BF16 : AX_PRO_F32;
   const int64_t vs = var_stride(g);
-  const float inv_d = 1.0f / static_cast<float>(g.head_dim);
-  if (g.axes == TACT_AXES_ALL && plane_supported(g) && g.quantizer == TACT_QUANT_LLOYD_MAX) {
-    // S on the matrix cores into the fp32 volume, then H and W fused in LDS
-    // (the final coefficients replace the volume), the allocation, and one
-    // streaming pass over the coded bins
-    // the S pass also applies the quantizer's rotation to its output (it acts
-    // on the channels, so it commutes with the H and W axes and leaves the
-    // bin variances unchanged)
+  if (fused_path(g)) {
     launch_axis(g, cn, 0, 0, in_pro, AX_EPI_F32, kv, kv_stride, w.coef, g.n_entries, w.tab,
                 nullptr, nullptr, 0, none, nullptr, s, /*rot_in=*/false, /*rot_out=*/true);
     launch_plane(g, cn, 0, w.coef, w.coef, g.n_entries, w.tab, w.var, vs, none, nullptr, s);
-    launch_allocate2(g, cn, w.var, vs, static_cast<int>(var_parts(g)), inv_d, nullptr,
-                     view(g, recs), w.poff, w.invg, s, /*planes=*/true);
-    launch_quant(g, cn, w.coef, g.n_entries, w.invg, vs, view(g, recs), w.poff, s);
-    return;
+    return {static_cast<int>(var_parts(g)), true};
   }
   int ax[3];
   const int m = forward_axes(g, ax);
@@ -270,16 +278,34 @@ void compress_chunk(const Geometry& g, int64_t cn, const void* kv, int64_t kv_st
       launch_axis(g, cn, ax[j], 0, AX_PRO_F32, AX_EPI_F32, w.coef, g.n_entries, w.coef,
                   g.n_entries, w.tab, nullptr, nullptr, 0, none, nullptr, s);
   }
-  const void* last_in = (m == 1) ? kv : static_cast<const void*>(w.coef);
-  const int64_t last_stride = (m == 1) ? kv_stride : g.n_entries;
-  const int last_pro = (m == 1) ? in_pro : AX_PRO_F32;
-  launch_axis(g, cn, ax[m - 1], 0, last_pro, AX_EPI_STATS, last_in, last_stride, nullptr, 0,
-              w.tab, w.var, nullptr, vs, none, nullptr, s);
-  // the variances are consumed by the allocation, which also leaves the
-  // reciprocal gains for the coding pass
-  launch_allocate2(g, cn, w.var, vs, 1, inv_d, nullptr, view(g, recs), w.poff, w.invg, s);
-  launch_axis(g, cn, ax[m - 1], 0, last_pro, AX_EPI_QUANT, last_in, last_stride, nullptr, 0,
-              w.tab, nullptr, w.invg, vs, view(g, recs), w.poff, s);
+  launch_axis(g, cn, ax[m - 1], 0, m == 1 ? in_pro : AX_PRO_F32, AX_EPI_STATS,
+              m == 1 ? kv : static_cast<const void*>(w.coef), m == 1 ? kv_stride : g.n_entries,
+              nullptr, 0, w.tab, w.var, nullptr, vs, none, nullptr, s);
+  return {1, false};
+}
+
+// compress `cn` units: kv chunk -> records chunk.  The allocation reads the
+// sums of the forward stage and leaves the record header, the first planes
+// and the reciprocal gains; the coding pass then reads the final
+// coefficients (fused path) or runs the last axis again with the coding
+// epilogue.
+void compress_chunk(const Geometry& g, int64_t cn, const void* kv, int64_t kv_stride,
+                    uint8_t* recs, const Workspace& w, hipStream_t s) {
+  const int64_t vs = var_stride(g);
+  const float inv_d = 1.0f / static_cast<float>(g.head_dim);
+  const StatsLayout sl = forward_stats(g, cn, kv, kv_stride, w, s);
+  launch_allocate2(g, cn, w.var, vs, sl.parts, inv_d, nullptr, view(g, recs), w.poff, w.invg, s,
+                   sl.planes);
+  if (fused_path(g)) {
+    launch_quant(g, cn, w.coef, g.n_entries, w.invg, vs, view(g, recs), w.poff, s);
+    return;
+  }
+  int ax[3];
+  const int m = forward_axes(g, ax);
+  const int in_pro = g.dtype == TACT_BF16 ? AX_PRO_BF16 : AX_PRO_F32;
+  launch_axis(g, cn, ax[m - 1], 0, m == 1 ? in_pro : AX_PRO_F32, AX_EPI_QUANT,
+              m == 1 ? kv : static_cast<const void*>(w.coef), m == 1 ? kv_stride : g.n_entries,
+              nullptr, 0, w.tab, nullptr, w.invg, vs, view(g, recs), w.poff, s);
 }
 
 // decompress `cn` records: the last forward axis runs first, reading and
@@ -290,7 +316,7 @@ void decompress_chunk(const Geometry& g, int64_t cn, const uint8_t* recs, void* 
   const RecordView rv = view(g, const_cast<uint8_t*>(recs));
   const int out_epi = g.dtype == TACT_BF16 ? AX_EPI_BF16 : AX_EPI_F32;
   launch_plane_offsets(g, cn, rv, w.poff, s);
-  if (g.axes == TACT_AXES_ALL && plane_supported(g) && g.quantizer == TACT_QUANT_LLOYD_MAX) {
+  if (fused_path(g)) {
     launch_plane(g, cn, 2, nullptr, w.coef, g.n_entries, w.tab, nullptr, 0, rv, w.poff, s);
     // the inverse S axis also undoes the quantizer's rotation (it acts on
     // the channels, so it commutes with the transform)
@@ -602,55 +628,98 @@ int32_t tact_codebook(int32_t bits, float* levels, float* thresholds) {
 }
 
 // ---------------------------------------------------------------------------
-// stage entry points (tact_debug.h)
+// stage entry points (tact_debug.h): each runs the kernels tact_compress and
+// tact_decompress launch, on the whole batch at once (no chunking)
 // ---------------------------------------------------------------------------
 size_t tact_dbg_workspace_bytes(const tact_params* p, int64_t n_units) {
   Geometry g;
-  if (make_geometry(p, &g) != TACT_OK) return 0;
-  (void)n_units;
-  return static_cast<size_t>(kTableBytes);
+  if (make_geometry(p, &g) != TACT_OK || n_units <= 0 || n_units > kMaxChunkUnits) return 0;
+  return static_cast<size_t>(ws_bytes(g, n_units));
 }
+
+namespace {
+
+// Common checks of the stage calls; on success *w is the carved workspace.
+tact_status dbg_prologue(const char* who, const tact_params* p, int64_t n_units, void* ws,
+                         size_t ws_bytes_given, Geometry* g, Workspace* w) {
+  tact_status st;
+  if ((st = make_geometry(p, g)) != TACT_OK) return st;
+  if ((st = check_units(n_units)) != TACT_OK) return st;
+  if (n_units > kMaxChunkUnits)
+    return fail(TACT_ERR_INVALID_ARGUMENT, "%s: n_units=%lld, at most %lld per stage call", who,
+                (long long)n_units, (long long)kMaxChunkUnits);
+  if (n_units == 0) return TACT_OK;
+  const int64_t need = ws_bytes(*g, n_units);
+  if (!ws) return fail(TACT_ERR_WORKSPACE, "%s: workspace is NULL (%lld bytes needed)", who,
+                       (long long)need);
+  if (!aligned(ws, 256))
+    return fail(TACT_ERR_INVALID_ARGUMENT, "%s: workspace is not 256-byte aligned", who);
+  if (static_cast<int64_t>(ws_bytes_given) < need)
+    return fail(TACT_ERR_WORKSPACE, "%s: workspace of %zu bytes, %lld needed", who,
+                ws_bytes_given, (long long)need);
+  *w = carve(*g, n_units, ws);
+  return TACT_OK;
+}
+
+}  // namespace
 
 tact_status tact_dbg_dct3(const tact_params* p, int64_t n_units, int32_t inverse,
                           const void* in, float* out, void* workspace,
                           size_t workspace_bytes, hipStream_t stream) {
   Geometry g;
+  Workspace w;
   tact_status st;
-  if ((st = make_geometry(p, &g)) != TACT_OK) return st;
-  if ((st = check_units(n_units)) != TACT_OK) return st;
+  if ((st = dbg_prologue("tact_dbg_dct3", p, n_units, workspace, workspace_bytes, &g, &w)) !=
+      TACT_OK)
+    return st;
   if (n_units == 0) return ok();
   if ((st = check_buffer(in, "in", 16)) != TACT_OK) return st;
   if ((st = check_buffer(out, "out", 16)) != TACT_OK) return st;
-  if (!workspace) return fail(TACT_ERR_WORKSPACE, "workspace is NULL");
-  if (!aligned(workspace, 256)) return fail(TACT_ERR_INVALID_ARGUMENT, "workspace not 256-byte aligned");
-  if (static_cast<int64_t>(workspace_bytes) < kTableBytes)
-    return fail(TACT_ERR_WORKSPACE, "workspace of %zu bytes, %lld needed", workspace_bytes,
-                (long long)kTableBytes);
-  float* tab = static_cast<float*>(workspace);
-  launch_dct_tables(g, tab, stream);
+  // the plain transform: the quantizer's rotation stays off
+  g.rotation = TACT_ROTATION_NONE;
+  launch_dct_tables(g, w.tab, stream);
+  const RecordView none{};
+  if (!inverse && fused_path(g)) {
+    // the product's S pass, then the plane pass in place in `out`
+    const int in_pro = g.dtype == TACT_BF16 ? AX_PRO_BF16 : AX_PRO_F32;
+    launch_axis(g, n_units, 0, 0, in_pro, AX_EPI_F32, in, g.n_entries, out, g.n_entries, w.tab,
+                nullptr, nullptr, 0, none, nullptr, stream);
+    launch_plane(g, n_units, 0, out, out, g.n_entries, w.tab, w.var, var_stride(g), none,
+                 nullptr, stream);
+    return after_launch("tact_dbg_dct3");
+  }
+  // axis by axis, as the decoding of every geometry and the coding of the
+  // others run them (the last forward axis of the coding pass runs there
+  // with its sums-of-squares and coding epilogues instead)
   int ax[3];
   const int m = forward_axes(g, ax);
-  const RecordView none{};
   for (int j = 0; j < m; ++j) {
     const int a = inverse ? ax[m - 1 - j] : ax[j];
     const int pro = (j == 0 && !inverse && g.dtype == TACT_BF16) ? AX_PRO_BF16 : AX_PRO_F32;
     const void* src = (j == 0) ? in : static_cast<const void*>(out);
     launch_axis(g, n_units, a, inverse ? 1 : 0, pro, AX_EPI_F32, src, g.n_entries, out,
-                g.n_entries, tab, nullptr, nullptr, 0, none, nullptr, stream);
+                g.n_entries, w.tab, nullptr, nullptr, 0, none, nullptr, stream);
   }
   return after_launch("tact_dbg_dct3");
 }
 
-tact_status tact_dbg_bin_variance(const tact_params* p, int64_t n_units, const float* coef,
-                                  float* var, hipStream_t stream) {
+tact_status tact_dbg_bin_variance(const tact_params* p, int64_t n_units, const void* kv,
+                                  float* var, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
   Geometry g;
+  Workspace w;
   tact_status st;
-  if ((st = make_geometry(p, &g)) != TACT_OK) return st;
-  if ((st = check_units(n_units)) != TACT_OK) return st;
+  if ((st = dbg_prologue("tact_dbg_bin_variance", p, n_units, workspace, workspace_bytes, &g,
+                         &w)) != TACT_OK)
+    return st;
   if (n_units == 0) return ok();
-  if ((st = check_buffer(coef, "coef", 16)) != TACT_OK) return st;
+  if ((st = check_tensor(g, kv, g.n_entries, "kv")) != TACT_OK) return st;
   if ((st = check_buffer(var, "var", 4)) != TACT_OK) return st;
-  launch_bin_variance(g, n_units, coef, var, stream);
+  launch_dct_tables(g, w.tab, stream);
+  const StatsLayout sl = forward_stats(g, n_units, kv, g.n_entries, w, stream);
+  // the allocation's own sum of the partials, scaled by 1/d, is the output
+  launch_allocate2(g, n_units, w.var, var_stride(g), sl.parts, 1.0f / static_cast<float>(g.head_dim),
+                   nullptr, RecordView{}, nullptr, nullptr, stream, sl.planes, var);
   return after_launch("tact_dbg_bin_variance");
 }
 
@@ -660,6 +729,9 @@ tact_status tact_dbg_allocate(const tact_params* p, int64_t n_units, const float
   tact_status st;
   if ((st = make_geometry(p, &g)) != TACT_OK) return st;
   if ((st = check_units(n_units)) != TACT_OK) return st;
+  if (n_units > kMaxChunkUnits)
+    return fail(TACT_ERR_INVALID_ARGUMENT, "tact_dbg_allocate: n_units=%lld, at most %lld",
+                (long long)n_units, (long long)kMaxChunkUnits);
   if (n_units == 0) return ok();
   if ((st = check_buffer(var, "var", 4)) != TACT_OK) return st;
   if ((st = check_buffer(bits, "bits", 1)) != TACT_OK) return st;
@@ -669,55 +741,60 @@ tact_status tact_dbg_allocate(const tact_params* p, int64_t n_units, const float
 }
 
 tact_status tact_dbg_quantize(const tact_params* p, int64_t n_units, const float* coef,
-                              const float* gains, const uint8_t* bits, void* records,
-                              hipStream_t stream) {
+                              const float* var, void* records, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
   Geometry g;
+  Workspace w;
   tact_status st;
-  if ((st = make_geometry(p, &g)) != TACT_OK) return st;
+  if ((st = dbg_prologue("tact_dbg_quantize", p, n_units, workspace, workspace_bytes, &g, &w)) !=
+      TACT_OK)
+    return st;
   if (g.rotation != TACT_ROTATION_NONE)
-    return fail(TACT_ERR_UNSUPPORTED, "tact_dbg_quantize: the stage entry point quantizes without the "
-                "shared rotation; set rotation = TACT_ROTATION_NONE");
+    return fail(TACT_ERR_UNSUPPORTED, "tact_dbg_quantize: the stage entry point codes the "
+                "values as given; set rotation = TACT_ROTATION_NONE");
   if (g.quantizer != TACT_QUANT_LLOYD_MAX)
-    return fail(TACT_ERR_UNSUPPORTED, "tact_dbg_quantize: the stage entry point uses the Lloyd-Max table");
-  if ((st = check_units(n_units)) != TACT_OK) return st;
+    return fail(TACT_ERR_UNSUPPORTED, "tact_dbg_quantize: the coding kernel uses the Lloyd-Max table");
   if (n_units == 0) return ok();
   if ((st = check_buffer(coef, "coef", 16)) != TACT_OK) return st;
-  if ((st = check_buffer(gains, "gains", 4)) != TACT_OK) return st;
-  if ((st = check_buffer(bits, "bits", 1)) != TACT_OK) return st;
+  if ((st = check_buffer(var, "var", 4)) != TACT_OK) return st;
   if ((st = check_buffer(records, "records", 256)) != TACT_OK) return st;
-  launch_header(g, n_units, gains, bits, view(g, records), stream);
-  launch_quantize(g, n_units, coef, view(g, records), stream);
+  // the allocation writes the header, the first planes and 1/gain (stride
+  // n_bins, which the workspace's per-unit stride covers), then the coding
+  // pass of the fused path
+  const RecordView rv = view(g, records);
+  launch_allocate2(g, n_units, var, g.n_bins, 1, 1.0f, nullptr, rv, w.poff, w.invg, stream);
+  launch_quant(g, n_units, coef, g.n_entries, w.invg, g.n_bins, rv, w.poff, stream);
   return after_launch("tact_dbg_quantize");
 }
 
-tact_status tact_dbg_unpack(const tact_params* p, int64_t n_units, const void* records,
-                            uint8_t* codes, hipStream_t stream) {
-  Geometry g;
-  tact_status st;
-  if ((st = make_geometry(p, &g)) != TACT_OK) return st;
-  if ((st = check_units(n_units)) != TACT_OK) return st;
-  if (n_units == 0) return ok();
-  if ((st = check_buffer(records, "records", 256)) != TACT_OK) return st;
-  if ((st = check_buffer(codes, "codes", 1)) != TACT_OK) return st;
-  launch_unpack(g, n_units, view(g, const_cast<void*>(records)), codes, nullptr, stream);
-  return after_launch("tact_dbg_unpack");
-}
-
 tact_status tact_dbg_dequantize(const tact_params* p, int64_t n_units, const void* records,
-                                float* coef, hipStream_t stream) {
+                                float* coef, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
   Geometry g;
+  Workspace w;
   tact_status st;
-  if ((st = make_geometry(p, &g)) != TACT_OK) return st;
+  if ((st = dbg_prologue("tact_dbg_dequantize", p, n_units, workspace, workspace_bytes, &g, &w)) !=
+      TACT_OK)
+    return st;
   if (g.rotation != TACT_ROTATION_NONE)
-    return fail(TACT_ERR_UNSUPPORTED, "tact_dbg_dequantize: the stage entry point quantizes without the "
-                "shared rotation; set rotation = TACT_ROTATION_NONE");
-  if (g.quantizer != TACT_QUANT_LLOYD_MAX)
-    return fail(TACT_ERR_UNSUPPORTED, "tact_dbg_dequantize: the stage entry point uses the Lloyd-Max table");
-  if ((st = check_units(n_units)) != TACT_OK) return st;
+    return fail(TACT_ERR_UNSUPPORTED, "tact_dbg_dequantize: the stage entry point returns the "
+                "coefficients without the inverse rotation; set rotation = TACT_ROTATION_NONE");
   if (n_units == 0) return ok();
   if ((st = check_buffer(records, "records", 256)) != TACT_OK) return st;
   if ((st = check_buffer(coef, "coef", 16)) != TACT_OK) return st;
-  launch_unpack(g, n_units, view(g, const_cast<void*>(records)), nullptr, coef, stream);
+  // the first decoding kernel of tact_decompress with identity matrices in
+  // place of the DCT: its output is then g * level for every coefficient
+  const RecordView rv = view(g, const_cast<void*>(records));
+  launch_dct_tables(g, w.tab, stream, /*identity=*/7);
+  launch_plane_offsets(g, n_units, rv, w.poff, stream);
+  if (fused_path(g)) {
+    launch_plane(g, n_units, 2, nullptr, coef, g.n_entries, w.tab, nullptr, 0, rv, w.poff, stream);
+  } else {
+    int ax[3];
+    const int m = forward_axes(g, ax);
+    launch_axis(g, n_units, ax[m - 1], 1, AX_PRO_DEQUANT, AX_EPI_F32, w.coef, g.n_entries, coef,
+                g.n_entries, w.tab, nullptr, nullptr, 0, rv, w.poff, stream);
+  }
   return after_launch("tact_dbg_dequantize");
 }
 

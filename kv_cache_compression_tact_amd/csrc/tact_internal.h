@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI host layer (tact_api.cpp) and the
-// gfx950 kernels (tact_kernels.hip).  Not installed, not part of the ABI.
+// gfx950 kernels (tact_mfma.hip, tact_quant.hip, tact_attend.hip).  Not
+// installed, not part of the ABI.
 #ifndef TACT_INTERNAL_H_
 #define TACT_INTERNAL_H_
 
@@ -33,51 +34,16 @@ struct RecordView {
 
 constexpr int64_t align256(int64_t n) { return (n + 255) / 256 * 256; }
 
-// ---- launchers (tact_kernels.hip); all asynchronous on `stream` -----------
-
-// Separable DCT-II (inverse: DCT-III) along the axes in `axes`, over
-// `n_units` unit tensors.  in: element type in_dtype, unit stride in_stride
-// (elements).  out: element type out_dtype, unit stride out_stride.  Passes
-// after the first run in place in `out`, so `out` must be able to hold fp32
-// intermediates unless exactly one axis is transformed; when out_dtype is
-// not fp32 and more than one axis is transformed, `scratch` (fp32, n_units
-// * n_entries) holds the intermediates.
-void launch_dct3(const Geometry& g, int64_t n_units, int inverse,
-                 const void* in, int in_dtype, int64_t in_stride,
-                 void* out, int out_dtype, int64_t out_stride,
-                 float* scratch, hipStream_t stream);
-
-// var[u*n_bins + i] = mean_j coef[(u*n_bins + i)*d + j]^2.
-void launch_bin_variance(const Geometry& g, int64_t n_units, const float* coef,
-                         float* var, hipStream_t stream);
-
-// Bit allocation of every unit from its variances; writes the bits into
-// `bits_out` (stride n_bins per unit) if non-null, and the record header
-// (gains, bits, group index, zeroed padding) into `rec` if rec.base != null.
-void launch_allocate(const Geometry& g, int64_t n_units, const float* var,
-                     uint8_t* bits_out, RecordView rec, hipStream_t stream);
-
-// Record header (gains, bits, group index, padding) from caller's gains/bits.
-void launch_header(const Geometry& g, int64_t n_units, const float* gains,
-                   const uint8_t* bits, RecordView rec, hipStream_t stream);
-
-// Quantize + bit-plane pack: reads coef and the record header, writes codes.
-void launch_quantize(const Geometry& g, int64_t n_units, const float* coef,
-                     RecordView rec, hipStream_t stream);
-
-// Unpack (+ dequantize): codes_out (uint8 per coefficient) and/or coef_out
-// (fp32 g * level) from records; either may be null.
-void launch_unpack(const Geometry& g, int64_t n_units, RecordView rec,
-                   uint8_t* codes_out, float* coef_out, hipStream_t stream);
-
-// ---- MFMA path (tact_mfma.hip) ---------------------------------------------
+// ---- launchers; all asynchronous on `stream` --------------------------------
 // Prologue / epilogue selectors of launch_axis.
 enum { AX_PRO_BF16 = 0, AX_PRO_F32 = 1, AX_PRO_DEQUANT = 2 };
 enum { AX_EPI_F32 = 0, AX_EPI_BF16 = 1, AX_EPI_STATS = 2, AX_EPI_QUANT = 3 };
 constexpr int64_t kDctTableFloats = 3 * 64 * 64;
 
 // DCT-II matrices of the three axes into tab[3][64][64] (fp32, zero padded).
-void launch_dct_tables(const Geometry& g, float* tab, hipStream_t stream);
+// Bit a of `identity` puts the identity in place of axis a's matrix; the
+// default (-1) does so for the S axis of a geometry that transforms no axis.
+void launch_dct_tables(const Geometry& g, float* tab, hipStream_t stream, int identity = -1);
 
 // One axis (0 = S, 1 = H, 2 = W) of the transform on the matrix cores over
 // n_units units; see tact_mfma.hip for the prologue / epilogue contracts.
@@ -92,14 +58,15 @@ void launch_axis(const Geometry& g, int64_t n_units, int axis, int inverse, int 
                  bool rot_in = false, bool rot_out = false);
 
 // Allocation by exact radix selection; writes bits_out and/or the record
-// header, and per-bin first planes into plane_off (each may be null).
-// var holds `parts` partial sums per bin, scaled by var_scale: consecutive
-// per bin, or (planes) stored plane by plane as the plane pass writes them,
-// [slab][s][kh][kw] per unit.
+// header, per-bin first planes into plane_off, reciprocal gains into
+// inv_gain (stride var_stride) and the variances it allocated from into
+// var_out ([u][bin]); each may be null.  var holds `parts` partial sums per
+// bin, scaled by var_scale: consecutive per bin, or (planes) stored plane by
+// plane as the plane pass writes them, [slab][s][kh][kw] per unit.
 void launch_allocate2(const Geometry& g, int64_t n_units, const float* var, int64_t var_stride,
                       int parts, float var_scale, uint8_t* bits_out, RecordView rec,
                       uint32_t* plane_off, float* inv_gain, hipStream_t stream,
-                      bool planes = false);
+                      bool planes = false, float* var_out = nullptr);
 
 // Fused H and W axes (see tact_mfma.hip); mode 0 = forward: coefficients
 // to `out` (may equal `in`) and variance partial sums; 2 = decode + inverse.
@@ -141,7 +108,7 @@ void launch_attend(const Geometry& g, int64_t n_pairs, int q_heads, RecordView k
                    const float* tab, uint32_t* frags, hipStream_t stream);
 
 // Host copy of the fp32 codebooks (Lloyd-Max), and of every quantizer's,
-// indexed [quantizer][...].
+// indexed [quantizer][...] (tact_codebooks.cpp).
 extern const float kHostLevels[];
 extern const float kHostThresholds[];
 extern const float* const kHostLevelsQ[3];

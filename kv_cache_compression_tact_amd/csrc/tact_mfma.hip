@@ -47,16 +47,18 @@ constexpr float kLevelScale = 2048.0f;
 // ---------------------------------------------------------------------------
 // DCT-II matrices of the three axes, fp32, zero padded to 64 x 64:
 // tab[a][k][n] = a_k cos(pi (2n+1) k / 2N_a), a_0 = sqrt(1/N), a_k = sqrt(2/N).
-// With identity0 the S table is the identity instead (no-transform coding).
+// Axis a takes the identity instead when bit a of `identity` is set (the S
+// axis for no-transform coding; every axis for the decoding stage call, which
+// then returns the dequantized coefficients).
 // ---------------------------------------------------------------------------
-__global__ void k_dct_tables(float* __restrict__ tab, int n0, int n1, int n2, int identity0) {
+__global__ void k_dct_tables(float* __restrict__ tab, int n0, int n1, int n2, int identity) {
   const int a = blockIdx.x;
   const int N = a == 0 ? n0 : (a == 1 ? n1 : n2);
   for (int e = threadIdx.x; e < 64 * 64; e += blockDim.x) {
     const int k = e / 64, n = e % 64;
     float v = 0.f;
     if (k < N && n < N) {
-      if (a == 0 && identity0) {
+      if ((identity >> a) & 1) {
         v = k == n ? 1.f : 0.f;
       } else {
         const double al = (k == 0) ? sqrt(1.0 / N) : sqrt(2.0 / N);
@@ -1519,7 +1521,8 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
                                                              uint32_t* __restrict__ plane_off,
                                                              float* __restrict__ inv_gain,
                                                              int parts, float var_scale,
-                                                             int planes) {
+                                                             int planes,
+                                                             float* __restrict__ var_out) {
   __shared__ uint32_t hist[4096];
   __shared__ float s_var[4 * kAllocThreads];   // one chunk of variances, bin order
   __shared__ int sh[kAllocThreads / kWave];
@@ -1675,6 +1678,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
       if (i < nb) {
         if (bo) bo[i] = static_cast<uint8_t>(b[j]);
         if (po) po[i] = static_cast<uint32_t>(p);
+        if (var_out) var_out[u * nb + i] = vi[j];
         const float gn = sqrtf(vi[j]);
         if (inv_gain) inv_gain[u * var_stride + i] = gn > 0.f ? 1.0f / gn : 0.f;
         if (r) {
@@ -1796,8 +1800,9 @@ void launch_axis_np(const AxisArgs& a, int pro, int epi, int tpw, hipStream_t s)
 // ---------------------------------------------------------------------------
 // host-facing launchers (declared in tact_internal.h)
 // ---------------------------------------------------------------------------
-void launch_dct_tables(const Geometry& g, float* tab, hipStream_t s) {
-  hipLaunchKernelGGL(k_dct_tables, dim3(3), dim3(256), 0, s, tab, g.S, g.H, g.W, g.axes == 0 ? 1 : 0);
+void launch_dct_tables(const Geometry& g, float* tab, hipStream_t s, int identity) {
+  if (identity < 0) identity = g.axes == 0 ? 1 : 0;
+  hipLaunchKernelGGL(k_dct_tables, dim3(3), dim3(256), 0, s, tab, g.S, g.H, g.W, identity);
 }
 
 // axis: 0 = S, 1 = H, 2 = W
@@ -1948,10 +1953,11 @@ void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in,
 
 void launch_allocate2(const Geometry& g, int64_t n_units, const float* var, int64_t var_stride,
                       int parts, float var_scale, uint8_t* bits_out, RecordView rec,
-                      uint32_t* plane_off, float* inv_gain, hipStream_t s, bool planes) {
+                      uint32_t* plane_off, float* inv_gain, hipStream_t s, bool planes,
+                      float* var_out) {
   hipLaunchKernelGGL(k_allocate2, dim3(static_cast<unsigned>(n_units)), dim3(kAllocThreads), 0, s,
                      g, var, var_stride, bits_out, rec, plane_off, inv_gain, parts, var_scale,
-                     planes ? 1 : 0);
+                     planes ? 1 : 0, var_out);
 }
 
 void launch_plane_offsets(const Geometry& g, int64_t n_units, RecordView rec, uint32_t* plane_off,

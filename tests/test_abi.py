@@ -131,11 +131,33 @@ def test_null_and_misaligned_pointers_rejected():
 def test_stage_quantizers_refuse_the_rotation():
     # the stage entry points quantize and dequantize without the rotation
     fake = ctypes.c_void_p(1 << 20)
+    ws = ctypes.c_void_p(1 << 30)
     L = lib()
     p = _params()
-    assert L.tact_dbg_quantize(ctypes.byref(p), 1, fake, fake, fake, fake, None) == 2
-    assert L.tact_dbg_dequantize(ctypes.byref(p), 1, fake, fake, None) == 2
+    assert L.tact_dbg_quantize(ctypes.byref(p), 1, fake, fake, fake, ws, 1 << 40, None) == 2
+    assert L.tact_dbg_dequantize(ctypes.byref(p), 1, fake, fake, ws, 1 << 40, None) == 2
     assert b"rotation" in L.tact_last_error()
+
+
+def test_stage_workspace_is_checked_first():
+    fake = ctypes.c_void_p(1 << 20)
+    L = lib()
+    p = _params(rotation=0)
+    need = L.tact_dbg_workspace_bytes(ctypes.byref(p), 2)
+    # tables, then per unit the volume, variances, 1/gain, first planes, a record
+    assert need >= 2 * (4 * 4 * 8 * 8 * 2 * 64)
+    assert L.tact_dbg_workspace_bytes(ctypes.byref(p), 0) == 0
+    assert L.tact_dbg_workspace_bytes(ctypes.byref(p), 65536) == 0
+    ws = ctypes.c_void_p(1 << 30)
+    for call in (lambda w, n: L.tact_dbg_dct3(ctypes.byref(p), 2, 0, fake, fake, w, n, None),
+                 lambda w, n: L.tact_dbg_bin_variance(ctypes.byref(p), 2, fake, fake, w, n, None),
+                 lambda w, n: L.tact_dbg_quantize(ctypes.byref(p), 2, fake, fake, fake, w, n, None),
+                 lambda w, n: L.tact_dbg_dequantize(ctypes.byref(p), 2, fake, fake, w, n, None)):
+        assert call(None, need) == 3
+        assert call(ws, need - 1) == 3
+        assert call(ctypes.c_void_p((1 << 30) + 16), need) == 1      # not 256-byte aligned
+    assert L.tact_dbg_dct3(ctypes.byref(p), 65536, 0, fake, fake, ws, 1 << 45, None) == 1
+    assert L.tact_dbg_allocate(ctypes.byref(p), 65536, fake, fake, None) == 1
 
 
 def test_zero_units_is_a_noop():
@@ -168,8 +190,9 @@ def test_quantizer_parameter():
     fake = ctypes.c_void_p(1 << 20)
     L = lib()
     q1 = _params(quantizer=1, rotation=0)
-    assert L.tact_dbg_quantize(ctypes.byref(q1), 1, fake, fake, fake, fake, None) == 2
-    assert L.tact_dbg_dequantize(ctypes.byref(q1), 1, fake, fake, None) == 2
+    ws = ctypes.c_void_p(1 << 30)
+    # the coding kernel of the fused layout holds the Lloyd-Max table
+    assert L.tact_dbg_quantize(ctypes.byref(q1), 1, fake, fake, fake, ws, 1 << 40, None) == 2
 
 
 def test_library_codebook_equals_oracle_table():
