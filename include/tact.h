@@ -164,6 +164,27 @@ tact_status tact_roundtrip(const tact_params* p, int64_t n_units,
                            void* records, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/* tact_roundtrip for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc.  It
+ * takes no workspace argument: the workspace is a library-owned static
+ * device array of TACT_STATIC_WORKSPACE_BYTES, one per GPU, held from the
+ * library's first use on that GPU until the process ends, and the call
+ * allocates nothing.  Same arguments, results (bit for bit), aliasing rules
+ * and errors as tact_roundtrip; a batch runs as many units per chunk as the
+ * array holds.  Geometries whose single unit needs more workspace than the
+ * array (tact_workspace_bytes(p, 1) > TACT_STATIC_WORKSPACE_BYTES; the
+ * 64 x 24 x 24 x 8 x 128 unit needs about 163 MB) are rejected with
+ * TACT_ERR_UNSUPPORTED before anything is enqueued.  Every call on one GPU
+ * uses that GPU's one array: calls that overlap on a GPU (other streams,
+ * other host threads) race and must be serialized by the caller.  No part of
+ * the array needs to start at zero: each kernel writes what a later one
+ * reads. */
+#define TACT_STATIC_WORKSPACE_BYTES ((size_t)192 << 20)
+tact_status tact_roundtrip_noalloc(const tact_params* p, int64_t n_units,
+                                   const void* kv, int64_t kv_unit_stride,
+                                   void* kv_out, int64_t out_unit_stride,
+                                   void* records, hipStream_t stream);
+
 /* ---- Decoding fused into attention --------------------------------------
  * The page's decoding paragraph ("Methodology in Plain English") allows the
  * decoder to live inside the attention kernel: tact_attend reads only the

@@ -53,6 +53,7 @@ def _load():
         "tact_compress": (i32, [P, i64, vp, i64, vp, vp, sz, vp]),
         "tact_decompress": (i32, [P, i64, vp, vp, i64, vp, sz, vp]),
         "tact_roundtrip": (i32, [P, i64, vp, i64, vp, i64, vp, vp, sz, vp]),
+        "tact_roundtrip_noalloc": (i32, [P, i64, vp, i64, vp, i64, vp, vp]),
         "tact_status_string": (ctypes.c_char_p, [i32]),
         "tact_last_error": (ctypes.c_char_p, []),
         "tact_codebook": (i32, [i32, vp, vp]),
@@ -75,7 +76,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("tact_params_init", "tact_record_bytes", "tact_workspace_bytes",
-            "tact_compress", "tact_decompress", "tact_roundtrip",
+            "tact_compress", "tact_decompress", "tact_roundtrip", "tact_roundtrip_noalloc",
             "tact_status_string", "tact_last_error", "tact_codebook", "tact_quantizer_table",
             "tact_attend_workspace_bytes", "tact_attend",
             "tact_dbg_workspace_bytes", "tact_dbg_dct3", "tact_dbg_bin_variance",
@@ -288,6 +289,32 @@ def roundtrip(kv: torch.Tensor, budget_bits: int, max_bits: int = 8, *,
                                _unit_stride(out), _ptr(records), _ptr(ws), ws.numel(),
                                _stream()), "tact_roundtrip")
     return out, records
+
+
+def roundtrip_noalloc(kv: torch.Tensor, budget_bits: int, max_bits: int = 8, *,
+                      out: torch.Tensor, records: torch.Tensor | None = None,
+                      axes: int = AXES_ALL, alloc_mode: int = ALLOC_WATERFILL,
+                      rotation: int = ROTATION_HADAMARD, quantizer: int = QUANT_LLOYD_MAX):
+    """roundtrip without any device allocation: the caller passes `out` (and
+    `records`, or None to keep them in the library's static workspace), and
+    the library's own per-GPU workspace serves the call.  Returns (out,
+    records)."""
+    g = Geometry.of(kv, budget_bits, max_bits=max_bits, axes=axes, alloc_mode=alloc_mode,
+                    rotation=rotation, quantizer=quantizer)
+    U = kv.shape[0]
+    _check_cache(kv, g, U, "kv")
+    _check_cache(out, g, U, "out")
+    if records is not None:
+        _check_records(records, g, U)
+    _on_gpu(kv=kv, out=out, records=records)
+    p = g.params()
+    _check(_lib.tact_roundtrip_noalloc(ctypes.byref(p), U, _ptr(kv), _unit_stride(kv), _ptr(out),
+                                       _unit_stride(out), _ptr(records), _stream()),
+           "tact_roundtrip_noalloc")
+    return out, records
+
+
+STATIC_WORKSPACE_BYTES = 192 << 20    # TACT_STATIC_WORKSPACE_BYTES of tact.h
 
 
 def attend_workspace(geom: Geometry, n_pairs: int, q_heads: int, device=None) -> torch.Tensor:

@@ -30,7 +30,7 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 SOURCES = ["tact_api.cpp", "tact_codebooks.cpp", "tact_mfma.hip", "tact_quant.hip",
-           "tact_attend.hip"]
+           "tact_attend.hip", "tact_static_ws.hip"]
 
 
 def _run(cmd, **kw):

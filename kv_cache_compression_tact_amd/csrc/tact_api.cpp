@@ -545,6 +545,30 @@ tact_status tact_roundtrip(const tact_params* p, int64_t n_units, const void* kv
   return after_launch("tact_roundtrip");
 }
 
+tact_status tact_roundtrip_noalloc(const tact_params* p, int64_t n_units, const void* kv,
+                                   int64_t kv_unit_stride, void* kv_out, int64_t out_unit_stride,
+                                   void* records, hipStream_t stream) {
+  Geometry g;
+  tact_status st;
+  if ((st = make_geometry(p, &g)) != TACT_OK) return st;
+  if ((st = check_units(n_units)) != TACT_OK) return st;
+  if (n_units == 0) return ok();
+  const int64_t need = ws_bytes(g, 1);
+  if (need > static_cast<int64_t>(TACT_STATIC_WORKSPACE_BYTES))
+    return fail(TACT_ERR_UNSUPPORTED,
+                "tact_roundtrip_noalloc: one unit of this geometry needs %lld bytes of "
+                "workspace; the library's static workspace holds %lld (use tact_roundtrip "
+                "with a caller workspace)",
+                (long long)need, (long long)TACT_STATIC_WORKSPACE_BYTES);
+  void* ws = nullptr;
+  const hipError_t e = static_workspace(&ws);
+  if (e != hipSuccess)
+    return fail(TACT_ERR_HIP, "tact_roundtrip_noalloc: static workspace: %s (%s)",
+                hipGetErrorName(e), hipGetErrorString(e));
+  return tact_roundtrip(p, n_units, kv, kv_unit_stride, kv_out, out_unit_stride, records, ws,
+                        TACT_STATIC_WORKSPACE_BYTES, stream);
+}
+
 size_t tact_attend_workspace_bytes(const tact_params* p, int64_t n_pairs, int32_t q_heads) {
   Geometry g;
   if (make_geometry(p, &g) != TACT_OK || check_attend(g, n_pairs, q_heads) != TACT_OK) return 0;

@@ -107,6 +107,11 @@ void launch_attend(const Geometry& g, int64_t n_pairs, int q_heads, RecordView k
                    float scale, float* qrot, float* field, float* partial, float* out, float* lse,
                    const float* tab, uint32_t* frags, hipStream_t stream);
 
+// Device address of the current GPU's copy of the library-owned workspace
+// (TACT_STATIC_WORKSPACE_BYTES, 256-byte aligned; tact_static_ws.hip),
+// looked up on the first call on each GPU.
+hipError_t static_workspace(void** ptr);
+
 // Host copy of the fp32 codebooks (Lloyd-Max), and of every quantizer's,
 // indexed [quantizer][...] (tact_codebooks.cpp).
 extern const float kHostLevels[];
