@@ -1317,7 +1317,7 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
         for (int m = 0; m < FH::MT; ++m)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr)
-            buf_st4(rout, voff, (16 * m + rr) * row_bytes,
+            buf_st4<2>(rout, voff, (16 * m + rr) * row_bytes,
                     float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
       }
       __syncthreads();                       // LDS free for the next plane
