@@ -11,7 +11,8 @@
 // lane c is channel c of a 64-channel word, so a bin's codes for one bit
 // plane are one ballot.  The cell index is found most significant bit
 // first (binary search over the sorted thresholds), and the ballot of each
-// step is directly the word of that bit plane.  The coded bins of a wave
+// step is directly the word of that bit plane.  The coefficients of the next
+// eight coded bins are loaded while eight are coded.  The coded bins of a wave
 // own one contiguous run of record words (bin by bin, plane by plane, word
 // of the plane fastest), so the words are gathered into lanes by their
 // position in that run and written up to 64 at a time.
@@ -31,6 +32,7 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kQuantWaves = 4;
+constexpr int kAhead = 8;          // coded bins fetched ahead per wave
 
 struct QuantArgs {
   const float* coef;         // final DCT coefficients, [u][bin][head_dim]
@@ -119,42 +121,66 @@ __global__ __launch_bounds__(kWave * kQuantWaves) void k_quant(QuantArgs a) {
     cnt = 0;
   };
 
-  // coded bins of this wave, lowest first; the coefficients of the next one
-  // are in flight while the current one is coded
+  // coded bins of this wave, lowest first, in groups of kAhead: the
+  // coefficients of the next group are in flight while a group is coded
+  // (one bin ahead leaves too little in flight to stream the coefficients)
   uint64_t todo = __ballot(bj > 0);
-  float nxt[4] = {0.f, 0.f, 0.f, 0.f};
-  auto fetch = [&](int j) {
+  float nxt[kAhead][4];
+  int jn[kAhead];
+  int nn = 0;
+  auto fetch_group = [&]() {
+    nn = 0;
 #pragma unroll
-    for (int h = 0; h < WPP; ++h) nxt[h] = cu[j * kHeadDim + 64 * h];
-  };
-  if (todo) fetch(__builtin_ctzll(todo));
-  while (todo) {
-    const int j = __builtin_ctzll(todo);
-    todo &= todo - 1;
-    float v[4];
+    for (int i = 0; i < kAhead; ++i) {
+      jn[i] = todo ? __builtin_ctzll(todo) : 0;
+      if (todo) {
+        todo &= todo - 1;
+        ++nn;
+      }
 #pragma unroll
-    for (int h = 0; h < 4; ++h) v[h] = nxt[h];
-    if (todo) fetch(__builtin_ctzll(todo));
-    const int b = __builtin_amdgcn_readlane(bj, j);
-    const int64_t w0 = static_cast<int64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(pj, j))) * WPP;
-    const float inv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ij), j));
-#pragma unroll
-    for (int h = 0; h < WPP; ++h) v[h] *= inv;
-    // this bin's b * WPP words must follow the gathered ones in the record
-    // and fit beside them
-    if (cnt > 0 && (w0 != first + cnt || cnt + b * WPP > kWave)) flush();
-    if (cnt == 0) first = w0;
-    switch (b) {
-      case 1: code_bin<WPP, 1>(v, s_thr, cnt, wlo, whi); break;
-      case 2: code_bin<WPP, 2>(v, s_thr, cnt, wlo, whi); break;
-      case 3: code_bin<WPP, 3>(v, s_thr, cnt, wlo, whi); break;
-      case 4: code_bin<WPP, 4>(v, s_thr, cnt, wlo, whi); break;
-      case 5: code_bin<WPP, 5>(v, s_thr, cnt, wlo, whi); break;
-      case 6: code_bin<WPP, 6>(v, s_thr, cnt, wlo, whi); break;
-      case 7: code_bin<WPP, 7>(v, s_thr, cnt, wlo, whi); break;
-      default: code_bin<WPP, 8>(v, s_thr, cnt, wlo, whi); break;
+      for (int h = 0; h < WPP; ++h) nxt[i][h] = i < nn ? cu[jn[i] * kHeadDim + 64 * h] : 0.f;
     }
-    cnt += b * WPP;
+  };
+  fetch_group();
+  while (nn > 0) {
+    float cur[kAhead][4];
+    int jc[kAhead];
+    const int nc = nn;
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      jc[i] = jn[i];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) cur[i][h] = nxt[i][h];
+    }
+    fetch_group();
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      if (i >= nc) break;
+      const int j = jc[i];
+      float v[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) v[h] = cur[i][h];
+      const int b = __builtin_amdgcn_readlane(bj, j);
+      const int64_t w0 = static_cast<int64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(pj, j))) * WPP;
+      const float inv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ij), j));
+#pragma unroll
+      for (int h = 0; h < WPP; ++h) v[h] *= inv;
+      // this bin's b * WPP words must follow the gathered ones in the record
+      // and fit beside them
+      if (cnt > 0 && (w0 != first + cnt || cnt + b * WPP > kWave)) flush();
+      if (cnt == 0) first = w0;
+      switch (b) {
+        case 1: code_bin<WPP, 1>(v, s_thr, cnt, wlo, whi); break;
+        case 2: code_bin<WPP, 2>(v, s_thr, cnt, wlo, whi); break;
+        case 3: code_bin<WPP, 3>(v, s_thr, cnt, wlo, whi); break;
+        case 4: code_bin<WPP, 4>(v, s_thr, cnt, wlo, whi); break;
+        case 5: code_bin<WPP, 5>(v, s_thr, cnt, wlo, whi); break;
+        case 6: code_bin<WPP, 6>(v, s_thr, cnt, wlo, whi); break;
+        case 7: code_bin<WPP, 7>(v, s_thr, cnt, wlo, whi); break;
+        default: code_bin<WPP, 8>(v, s_thr, cnt, wlo, whi); break;
+      }
+      cnt += b * WPP;
+    }
   }
   flush();
 }
