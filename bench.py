@@ -51,6 +51,9 @@ def _parse():
                     help="units of the workload used by --ablations")
     ap.add_argument("--q-per-kv", type=int, default=4,
                     help="query heads per kv head for --attend")
+    ap.add_argument("--calibrate-bandwidth", action="store_true",
+                    help="only measure this device's plain read-only, write-only and copy "
+                         "rates on 8 GiB buffers (torch's kernels)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times): the "
                          "reference for scaling the HBM byte counters of a profile")
@@ -78,6 +81,41 @@ def calibrate_copy():
     print(json.dumps({"calibration": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
                       "repeats": 3, "ms": [round(m, 4) for m in ms],
                       "copy_GBs_read_plus_write": round(2 * (1 << 30) / (best * 1e-3) / 1e9, 1)}),
+          flush=True)
+
+
+def calibrate_bandwidth():
+    """The plain HBM rates of this device with torch's own kernels on 8 GiB
+    buffers (far beyond the 256 MB Infinity Cache): read-only (a sum),
+    write-only (a fill) and a copy (read + write), three repeats each, the
+    best taken.  The reference rates the codec's kernels are compared with."""
+    dev = torch.device("cuda:0")
+    n = 1 << 31                                   # 8 GiB of fp32
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def best_ms(fn):
+        ms = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        return min(ms)
+
+    nbytes = 4 * n
+    torch.cuda.synchronize()
+    r = best_ms(lambda: x.sum())
+    w = best_ms(lambda: y.fill_(2.0))
+    c = best_ms(lambda: y.copy_(x))
+    print(json.dumps({"calibration": "bandwidth", "bytes": nbytes,
+                      "read_only_GBs": round(nbytes / (r * 1e-3) / 1e9, 1),
+                      "write_only_GBs": round(nbytes / (w * 1e-3) / 1e9, 1),
+                      "copy_GBs_read_plus_write": round(2 * nbytes / (c * 1e-3) / 1e9, 1),
+                      "ms": {"read": round(r, 3), "write": round(w, 3), "copy": round(c, 3)}}),
           flush=True)
 
 
@@ -273,6 +311,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.calibrate_bandwidth:
+        calibrate_bandwidth()
         return
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import kv_cache_compression_tact_amd as tact
