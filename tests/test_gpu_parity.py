@@ -442,6 +442,30 @@ def _random_geometries(n, seed):
 
 
 @pytest.mark.parametrize("geo", _random_geometries(12, 2026))
+def test_stages_random_geometries(geo):
+    """Every stage entry point on the seeded random geometries: variances
+    (against the same kernels' coefficients and the exact ones), bits given
+    the GPU's variances, records given identical inputs (geometries whose
+    coding runs in the plane pass) and the decoding stage."""
+    *shape, rot = geo
+    g = _geom(*shape, rotation=rot)
+    g0 = _geom(*shape, rotation=0)
+    say("stages random", geo)
+    op = _oparams(g)
+    x = _units(g, 2, seed=sum(shape[:5]) + 1)
+    var = _check_variances(x, g).astype(np.float32)
+    bits = tact.dbg_allocate(_gpu(var), g).cpu().numpy().reshape(2, -1)
+    for u in range(2):
+        ref = O.allocate_bits(var[u].astype(np.float64).ravel(), O.total_bits(op), g.max_bits)
+        assert np.array_equal(bits[u].astype(np.int64), ref), u
+    xs = x.float().cpu().numpy().astype(np.float64)
+    coef = np.stack([O.dct3_forward(xs[u]) for u in range(2)]).astype(np.float32)
+    if g.H <= 32 and g.W <= 32 and g.H * g.W * 256 <= 150 * 1024:
+        _check_records_given_inputs(coef, g0)
+    _check_dequantize(np.stack([O.compress(xs[u], op, rotation="none") for u in range(2)]), g0)
+
+
+@pytest.mark.parametrize("geo", _random_geometries(12, 2026))
 def test_roundtrip_random_geometries(geo):
     *shape, rot = geo
     g = _geom(*shape, rotation=rot)

@@ -64,4 +64,14 @@ def test_noalloc_matches_roundtrip_on_consecutive_calls():
     tact.roundtrip_noalloc(z, 2, out=z, records=rec)
     torch.cuda.synchronize()
     assert torch.equal(z, ref_out)
-    say("noalloc: equal to tact_roundtrip on both calls")
+    # the per-axis path (W beyond 32) and fp32 caches share the array too
+    for shape, dt in (((3, 5, 40, 1, 128), torch.bfloat16), ((2, 6, 7, 2, 64), torch.float32)):
+        say("noalloc:", shape, dt)
+        z = torch.randn((2,) + shape, generator=gen).to(dt).cuda()
+        ref_out, ref_rec = tact.roundtrip(z, 1)
+        out = torch.empty_like(z)
+        rec = torch.empty_like(ref_rec)
+        tact.roundtrip_noalloc(z, 1, out=out, records=rec)
+        torch.cuda.synchronize()
+        assert torch.equal(rec, ref_rec) and torch.equal(out, ref_out)
+    say("noalloc: equal to tact_roundtrip on every call")
