@@ -112,8 +112,11 @@ enum { TACT_ROTATION_NONE = 0, TACT_ROTATION_HADAMARD = 1 };
 enum { TACT_QUANT_LLOYD_MAX = 0, TACT_QUANT_UNIFORM = 1, TACT_QUANT_NF = 2 };
 
 typedef struct {
-  /* A unit (S * H * W * kv_heads * head_dim entries) holds at most 2^29
-   * entries; larger units are TACT_ERR_UNSUPPORTED. */
+  /* A unit is S * H * W * kv_heads * head_dim entries.  With each of S, H
+   * and W rounded up to 16, 32 or 64 (the first that holds it), the padded
+   * unit in fp32, 4 * S' * H' * W' * kv_heads * head_dim bytes, must not
+   * exceed 2^30 bytes (so at most 2^28 entries per unit); larger units are
+   * TACT_ERR_UNSUPPORTED. */
   int32_t S, H, W;      /* grid of the vision encoder, each 1..64            */
   int32_t kv_heads;     /* 1..64                                             */
   int32_t head_dim;     /* 64, 128 or 256                                    */

@@ -42,6 +42,15 @@ int64_t elem_size(int dtype) { return dtype == TACT_F32 ? 4 : 2; }
 // unit is accepted.
 constexpr int64_t kMaxChunkUnits = 65535;
 
+// rows of the matrix tile an axis of length n is padded to
+int64_t padded_axis(int n) { return n <= 16 ? 16 : n <= 32 ? 32 : 64; }
+// fp32 bytes of a unit with every grid axis padded to its tile
+int64_t padded_unit_bytes(const Geometry& g) {
+  return 4 * padded_axis(g.S) * padded_axis(g.H) * padded_axis(g.W) *
+         static_cast<int64_t>(g.kv_heads) * g.head_dim;
+}
+constexpr int64_t kMaxPaddedUnitBytes = int64_t(1) << 30;
+
 tact_status make_geometry(const tact_params* p, Geometry* g) {
   if (!p) return fail(TACT_ERR_INVALID_ARGUMENT, "params is NULL");
   auto in = [](int v, int lo, int hi) { return v >= lo && v <= hi; };
@@ -82,10 +91,18 @@ tact_status make_geometry(const tact_params* p, Geometry* g) {
   G.dtype = p->dtype;
   G.n_bins = int64_t(p->S) * p->H * p->W * p->kv_heads;
   G.n_entries = G.n_bins * p->head_dim;
-  if (G.n_entries > (int64_t(1) << 29))
+  // The kernels address a unit's fp32 volume through buffer descriptors with
+  // 32-bit offsets, rows of an axis padded to the 16, 32 or 64 rows of its
+  // matrix tile, and send dropped lanes to an offset just under 2^31.  With
+  // the padded volume at most 2^30 bytes, every offset a kernel forms (a
+  // padded row plus a column, below twice that) stays under 2^31, every
+  // descriptor range stays under the dropped offset, and no sum of offsets
+  // wraps past 2^32 into a range.
+  if (padded_unit_bytes(G) > kMaxPaddedUnitBytes)
     return fail(TACT_ERR_UNSUPPORTED,
-                "unit of %lld entries: at most 2^29 per unit (32-bit byte offsets)",
-                static_cast<long long>(G.n_entries));
+                "unit S=%d H=%d W=%d x %d x %d: padded fp32 volume of %lld bytes, at most 2^30",
+                p->S, p->H, p->W, p->kv_heads, p->head_dim,
+                static_cast<long long>(padded_unit_bytes(G)));
   G.total_bits = int64_t(p->budget_bits) * G.n_bins;
   G.n_groups = (G.n_bins + 63) / 64;
   G.code_bytes = G.total_bits * p->head_dim / 8;

@@ -88,7 +88,9 @@ __device__ __forceinline__ uint16_t bf16_rne_bits(float v) {
 // the descriptor's byte range return 0 and stores past it are dropped, so
 // padded rows need no branch.  voff is per lane, soff uniform.
 constexpr int kBufWord3 = 0x00020000;
-// a lane offset past every buffer the kernels address (all under 2^31 bytes)
+// a lane offset past every buffer the kernels address: a unit's padded fp32
+// volume is at most 2^30 bytes, so descriptor ranges stay below it and a
+// uniform offset added to it does not wrap past 2^32
 constexpr int kPastBuffer = 0x7FFFFFF0;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufWord3);
@@ -279,7 +281,8 @@ __global__ __launch_bounds__(256) void k_axis(AxisArgs a) {
 
   // Plain passes (interleaved columns): rows n of this (unit, o) through a
   // buffer of N rows, so rows n >= N read 0 and output rows k >= N are
-  // dropped; byte offsets fit 32 bits (a unit holds at most 2^29 entries).
+  // dropped; byte offsets, padded rows included, fit 31 bits (a unit's
+  // padded fp32 volume is at most 2^30 bytes).
   // The next column group's rows are fetched while this one is computed.
   constexpr bool PF = INTL && PRO != PRO_DEQUANT;
   constexpr int ES_IN = (PRO == PRO_BF16) ? 2 : 4;

@@ -78,15 +78,34 @@ def test_no_transform_axes_accepted():
     assert lib().tact_workspace_bytes(ctypes.byref(p), 4) > 0
 
 
-def test_unit_size_cap():
-    # at most 2^29 entries per unit
-    big = _params(S=64, H=64, W=64, kv_heads=32, head_dim=64)     # 2^29: allowed
-    assert lib().tact_record_bytes(ctypes.byref(big)) > 0
-    bigger = _params(S=64, H=64, W=64, kv_heads=64, head_dim=64)  # 2^30
-    assert lib().tact_record_bytes(ctypes.byref(bigger)) == 0
-    fake = ctypes.c_void_p(1 << 20)
-    assert lib().tact_compress(ctypes.byref(bigger), 1, fake, 1 << 30, fake, fake, 1 << 40,
-                               None) == 2
+def _padded_unit_bytes(S, H, W, kv_heads, head_dim):
+    pad = lambda n: 16 if n <= 16 else 32 if n <= 32 else 64
+    return 4 * pad(S) * pad(H) * pad(W) * kv_heads * head_dim
+
+
+@pytest.mark.parametrize("shape,ok", [
+    ((64, 64, 64, 16, 64), True),     # 2^28 entries, padded 2^30 bytes: the largest unit
+    ((64, 64, 64, 32, 64), False),    # 2^29 entries: fp32 volume 2^31 bytes
+    ((64, 64, 64, 64, 64), False),
+    ((40, 20, 18, 32, 128), True),    # ragged on every axis, padded exactly 2^30
+    ((33, 32, 32, 32, 128), True),    # S pads to 64: 2^30
+    ((33, 33, 32, 32, 128), False),   # H pads to 64 too: 2^31, though only 2^27.1 entries
+    ((2, 64, 64, 64, 64), True),      # S pads 2 -> 16: 2^30
+    ((2, 64, 64, 64, 128), False),    # 2^27 entries, but padded 2^31 (rows past S would wrap)
+    ((1, 1, 1, 64, 256), True),       # degenerate grid
+])
+def test_unit_size_cap(shape, ok):
+    # the padded fp32 unit (each grid axis rounded up to 16, 32 or 64) is at
+    # most 2^30 bytes; the worked sizes above are computed by hand
+    assert (_padded_unit_bytes(*shape) <= 1 << 30) == ok
+    S, H, W, kv, d = shape
+    p = _params(S=S, H=H, W=W, kv_heads=kv, head_dim=d)
+    assert (lib().tact_record_bytes(ctypes.byref(p)) > 0) == ok
+    if not ok:
+        fake = ctypes.c_void_p(1 << 20)
+        assert lib().tact_compress(ctypes.byref(p), 1, fake, 1 << 31, fake, fake, 1 << 40,
+                                   None) == 2
+        assert "padded" in lib().tact_last_error().decode()
 
 
 def test_null_and_misaligned_pointers_rejected():

@@ -149,27 +149,37 @@ def _check_variances(x, g, units=None):
     worst_red = worst_ex = 0.0
     for u in (range(x.shape[0]) if units is None else units):
         xs = x[u].float().cpu().numpy().astype(np.float64)
-        ref_c = O.dct3_forward(xs, axes)
-        ref = O.bin_variance(ref_c)
-        cu = c[u].astype(np.float64)
-        pos = ref > 0
-        if g.rotation == 0:
-            # the reduction alone: the same kernels' coefficients, summed in fp64
-            mine = O.bin_variance(cu)
-            red = np.abs(var[u] - mine)[pos] / mine[pos]
-            worst_red = max(worst_red, float(red.max()))
-            assert np.all(red <= 1e-6)
-        # against the exact coefficients: |(|a| - |b|)| <= |a - b| for the bin
-        # vectors, over sqrt(d); the rotation (orthonormal) adds its fp32
-        # rounding (six butterfly stages) to that of the sums
-        dc = np.sqrt(np.mean((cu - ref_c) ** 2, axis=-1))
-        slack = (1e-6 if g.rotation == 0 else 2e-6) * np.sqrt(ref)
-        lhs = np.abs(np.sqrt(var[u]) - np.sqrt(ref))
-        worst_ex = max(worst_ex, float(np.max((lhs / (dc + slack))[pos])))
-        assert np.all(lhs <= dc + slack)
+        r, e = _variance_bounds(var[u], c[u], O.dct3_forward(xs, axes), g.rotation)
+        worst_red, worst_ex = max(worst_red, r), max(worst_ex, e)
     red = f"reduction {worst_red:.2e} relative, " if g.rotation == 0 else ""
     say(f"  variances: {red}exact-coefficient bound used to {worst_ex:.2f}")
     return var
+
+
+def _variance_bounds(var, c, ref_c, rotation):
+    """Variances var (..., bins) the kernels computed, against the
+    coefficients c the same kernels computed (unrotated, fp32) and the exact
+    ones ref_c (fp64), both (..., head_dim).  Returns the worst relative
+    reduction error and the worst use of the exact-coefficient bound."""
+    var = np.asarray(var, dtype=np.float64)
+    ref = O.bin_variance(ref_c)
+    cu = np.asarray(c, dtype=np.float64)
+    pos = ref > 0
+    worst_red = 0.0
+    if rotation == 0:
+        # the reduction alone: the same kernels' coefficients, summed in fp64
+        mine = O.bin_variance(cu)
+        red = np.abs(var - mine)[pos] / mine[pos]
+        worst_red = float(red.max())
+        assert np.all(red <= 1e-6)
+    # against the exact coefficients: |(|a| - |b|)| <= |a - b| for the bin
+    # vectors, over sqrt(d); the rotation (orthonormal) adds its fp32
+    # rounding (six butterfly stages) to that of the sums
+    dc = np.sqrt(np.mean((cu - ref_c) ** 2, axis=-1))
+    slack = (1e-6 if rotation == 0 else 2e-6) * np.sqrt(ref)
+    lhs = np.abs(np.sqrt(var) - np.sqrt(ref))
+    assert np.all(lhs <= dc + slack)
+    return worst_red, float(np.max((lhs / (dc + slack))[pos]))
 
 
 @pytest.mark.parametrize("rot", [0, 1])
@@ -293,35 +303,40 @@ def test_decompress_from_oracle_records(geo, rot):
     recs = np.stack([O.compress(x[u], op, rotation=_orot(g)) for u in range(2)])
     out = tact.decompress(torch.from_numpy(recs).cuda(), g).float().cpu().numpy()
     for u in range(2):
+        exact = O.decompress(recs[u], op, None, rotation=_orot(g))
         if g.dtype == torch.bfloat16:
-            exact = O.decompress(recs[u], op, None, rotation=_orot(g))
-            ref = O.round_to_bf16(exact)
-            a, b = O.bf16_bits(out[u]), O.bf16_bits(ref)
-            diff = a != b
-            rms = math.sqrt(np.mean(exact ** 2))
-            tol = 1e-5 * rms                     # the transform's error bound
-            # an entry may round differently only where its exact value lies
-            # within the error bound of a bf16 rounding boundary: half an ulp
-            # above |ref|, half an ulp below it (the smaller ulp when |ref| is
-            # a power of two)
-            mag_r = np.maximum(np.abs(ref), np.finfo(np.float32).tiny)
-            e = np.floor(np.log2(mag_r))
-            ulp_up = np.ldexp(1.0, (e - 7).astype(int))
-            ulp_dn = np.where(mag_r == np.ldexp(1.0, e.astype(int)), 0.5 * ulp_up, ulp_up)
-            ax = np.abs(exact)
-            dist = np.minimum(mag_r + 0.5 * ulp_up - ax, ax - (mag_r - 0.5 * ulp_dn))
-            near = dist <= tol
-            assert np.all(near[diff]), np.argwhere(diff & ~near)[:4]
-            # and it is then a rounding-boundary case: the GPU value is within
-            # half a bf16 ulp of the exact value, up to the error bound
-            mag = np.maximum(np.abs(exact[diff]), np.abs(out[u][diff]))
-            ulp = np.ldexp(1.0, (np.floor(np.log2(mag)) - 7).astype(int))
-            assert np.all(np.abs(out[u][diff] - exact[diff]) <= 0.5 * ulp + tol)
-            say(f"  unit {u}: bf16 mismatches {diff.mean():.2e} of entries, "
-                f"near a boundary {near.mean():.2e}")
+            _check_bf16_decode(out[u], exact, f"unit {u}")
         else:
-            ref = O.decompress(recs[u], op, None, rotation=_orot(g))
-            assert _rel(out[u], ref) <= 1e-5
+            assert _rel(out[u], exact) <= 1e-5
+
+
+def _check_bf16_decode(out, exact, what):
+    """bf16 decoder output (as float) against the exact decoded values
+    (fp64): equal to their bf16 rounding except where the exact value lies
+    within the transform's error bound (1e-5 of the RMS) of a rounding
+    boundary, and then within half a bf16 ulp of it, up to that bound."""
+    ref = O.round_to_bf16(exact)
+    diff = O.bf16_bits(out) != O.bf16_bits(ref)
+    rms = math.sqrt(np.mean(exact ** 2))
+    tol = 1e-5 * rms                             # the transform's error bound
+    # an entry may round differently only where its exact value lies within
+    # the error bound of a bf16 rounding boundary: half an ulp above |ref|,
+    # half an ulp below it (the smaller ulp when |ref| is a power of two)
+    mag_r = np.maximum(np.abs(ref), np.finfo(np.float32).tiny)
+    e = np.floor(np.log2(mag_r))
+    ulp_up = np.ldexp(1.0, (e - 7).astype(int))
+    ulp_dn = np.where(mag_r == np.ldexp(1.0, e.astype(int)), 0.5 * ulp_up, ulp_up)
+    ax = np.abs(exact)
+    dist = np.minimum(mag_r + 0.5 * ulp_up - ax, ax - (mag_r - 0.5 * ulp_dn))
+    near = dist <= tol
+    assert np.all(near[diff]), np.argwhere(diff & ~near)[:4]
+    # and it is then a rounding-boundary case: the GPU value is within half a
+    # bf16 ulp of the exact value, up to the error bound
+    mag = np.maximum(np.abs(exact[diff]), np.abs(out[diff]))
+    ulp = np.ldexp(1.0, (np.floor(np.log2(mag)) - 7).astype(int))
+    assert np.all(np.abs(out[diff] - exact[diff]) <= 0.5 * ulp + tol)
+    say(f"  {what}: bf16 mismatches {diff.mean():.2e} of entries, "
+        f"near a boundary {near.mean():.2e}")
 
 
 def _compare_records(rec_gpu, rec_ref, op, coef_ref, rotation="hadamard", quantizer="lloyd_max"):
@@ -634,6 +649,132 @@ def test_full_size_stages_one_ct32b_unit():
     _check_records_given_inputs(ref_c.astype(np.float32)[None], g0)
     _check_dequantize(O.compress(xs, op, rotation="none")[None], g0)
     del x
+    torch.cuda.empty_cache()
+
+
+# ---- units at the size cap --------------------------------------------------
+# A unit's fp32 volume, with each grid axis rounded up to the 16, 32 or 64
+# rows of its matrix tile, may be at most 2^30 bytes; the kernels' largest
+# buffer offsets (padded rows included) occur at that cap.
+CAP_GEOMS = [
+    (2, 64, 64, 64, 64, 1, 8, torch.bfloat16),    # S pads 2 -> 16; H, W > 32: axis passes
+    (40, 20, 18, 32, 128, 2, 8, torch.bfloat16),  # ragged on every axis; the plane pass
+]
+
+
+@pytest.mark.parametrize("geo", CAP_GEOMS)
+def test_padded_units_at_the_size_cap(geo):
+    """A unit whose padded fp32 volume is exactly 2^30 bytes, against the
+    whole-unit oracle: coefficients, records and MSE of the round trip, and
+    the decoder on the oracle's records."""
+    g = _geom(*geo)
+    say("size cap", geo)
+    x = _units(g, 1, seed=31)
+    _roundtrip_check(x, g)
+    op = _oparams(g)
+    xs = x[0].float().cpu().numpy().astype(np.float64)
+    del x
+    rec = O.compress(xs, op, rotation=_orot(g))
+    out = tact.decompress(_gpu(rec[None]), g)[0].float().cpu().numpy()
+    _check_bf16_decode(out, O.decompress(rec, op, None, rotation=_orot(g)), "decoder")
+    torch.cuda.empty_cache()
+
+
+# The largest units: 2^28 entries, padded volume 2^30 bytes (no padding).
+# The oracle checks them where it works channel by channel (the transform
+# acts on each channel alone) or head by head (the variances): sampled
+# channels of the coefficients, codes, dequantized values and decoded
+# output, one whole head of variances, and every bin's bits and gain.
+LARGEST = [
+    (64, 32, 32, 32, 128),   # the fused layout: the S pass, then the H/W plane pass
+    (64, 64, 64, 16, 64),    # H and W beyond 32: three axis passes
+]
+
+
+def _correlated_unit_on_gpu(g, seed):
+    """One correlated unit (AR(1) along S, H and W), drawn on the GPU."""
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    x = torch.randn((1,) + g.unit_shape, generator=gen, device="cuda")
+    for ax, rho in ((1, 0.9), (2, 0.85), (3, 0.8)):
+        for i in range(1, x.shape[ax]):
+            x.select(ax, i).mul_(math.sqrt(1 - rho * rho)).add_(x.select(ax, i - 1), alpha=rho)
+    return x.to(g.dtype)
+
+
+@pytest.mark.parametrize("shape", LARGEST)
+def test_largest_units_sampled(shape):
+    kv, d = shape[3], shape[4]
+    g = tact.Geometry(*shape, budget_bits=1, max_bits=8, dtype=torch.bfloat16, rotation=0)
+    op = _oparams(g)
+    fused = shape[1] <= 32 and shape[2] <= 32
+    say("largest unit", shape, "fused" if fused else "axis passes")
+    x = _correlated_unit_on_gpu(g, 41)
+    chans = [(0, 0), (kv - 1, d - 1), (kv // 2, 63), (1, d // 2 + 1)]
+    ks = torch.tensor([k for k, _ in chans], device="cuda")
+    js = torch.tensor([j for _, j in chans], device="cuda")
+
+    def pick(t):
+        """(1, S, H, W, kv, d) on the GPU -> the sampled channels (S, H, W, n), fp64."""
+        return t[0][..., ks, js].double().cpu().numpy()
+
+    xs = pick(x)
+    c = tact.dbg_dct3(x, g)
+    cs = pick(c)
+    for i, ch in enumerate(chans):
+        e = _rel(cs[..., i], O.dct3_forward(xs[..., i]))
+        assert e <= 1e-5, (ch, e)
+    # the variances of one whole head
+    hk = kv - 1
+    c_head = c[0, ..., hk, :].double().cpu().numpy()
+    del c
+    var = tact.dbg_bin_variance(x, g)
+    ref_head = O.dct3_forward(x[0, ..., hk, :].double().cpu().numpy())
+    red, ex = _variance_bounds(var[0, ..., hk].cpu().numpy(), c_head, ref_head, 0)
+    say(f"  head {hk}: variance reduction {red:.2e}, exact bound used to {ex:.2f}")
+    # every bin's bits (from those variances) and gain, in the codec's record
+    v = var[0].double().cpu().numpy()
+    bits_ref = O.allocate_bits(v, O.total_bits(op), g.max_bits).reshape(v.shape)
+    assert np.array_equal(tact.dbg_allocate(var, g)[0].cpu().numpy(), bits_ref)
+    out, rec = tact.roundtrip(x, 1, 8, rotation=0)
+    del x
+    lay = O.record_layout(op)
+    r0 = rec[0].cpu().numpy()
+    bits = r0[lay["bits"]:lay["bits"] + op.n_bins].reshape(v.shape)
+    gains = r0[lay["gains"]:lay["gains"] + 4 * op.n_bins].view("<f4").reshape(v.shape)
+    assert np.array_equal(bits, bits_ref)
+    assert np.array_equal(gains, O.gains_f32(v))
+    # the sampled channels' codes (read back through the decoding stage),
+    # their values and the decoded output
+    deq = pick(tact.dbg_dequantize(rec, g))
+    outs = pick(out)
+    del out, rec
+    sigma = float(np.sqrt(np.mean(cs ** 2)))
+    for i, (k, j) in enumerate(chans):
+        b, gk = bits[..., k], gains[..., k]
+        g64 = gk.astype(np.float64)
+        codes = np.zeros(b.shape, dtype=np.uint8)
+        for nb in range(1, 9):
+            sel = (b == nb) & (g64 > 0)
+            if sel.any():
+                lv, _ = O.codebook_f32(nb)
+                val = deq[..., i][sel] / g64[sel]
+                codes[sel] = np.argmin(np.abs(val[:, None] - lv.astype(np.float64)), axis=-1)
+        exact = O.dequantize(codes[..., None], gk, b)[..., 0]
+        assert np.all(np.abs(deq[..., i] - exact) <= 2.0 ** -19 * np.abs(exact))
+        ref_codes = O.quantize(cs[..., i:i + 1], gk, b)[..., 0]
+        miss = (codes != ref_codes) & (b > 0)
+        if fused:
+            # the coding pass reads the very coefficients the stage call returned
+            assert not miss.any(), int(miss.sum())
+        else:
+            # the coding epilogue recomputes the last axis: a code may differ
+            # only next to a threshold (the end-to-end rule)
+            for idx in zip(*np.nonzero(miss)):
+                _, thr = O.codebook_f32(int(b[idx]))
+                u = float(np.float32(cs[idx + (i,)]) * (np.float32(1) / gk[idx]))
+                t = float(thr[np.argmin(np.abs(thr - u))])
+                assert abs(u - t) <= 1e-5 * max(abs(t), sigma / float(gk[idx])), (idx, u, t)
+        _check_bf16_decode(outs[..., i], O.dct3_inverse(exact), f"channel ({k}, {j})")
     torch.cuda.empty_cache()
 
 
