@@ -51,6 +51,9 @@ def _parse():
                     help="units of the workload used by --ablations")
     ap.add_argument("--q-per-kv", type=int, default=4,
                     help="query heads per kv head for --attend")
+    ap.add_argument("--ws-units", type=int, default=None,
+                    help="give the codec a workspace for this many units, so the batch "
+                         "runs in chunks of that size (default: the whole batch at once)")
     ap.add_argument("--calibrate-bandwidth", action="store_true",
                     help="only measure this device's plain read-only, write-only and copy "
                          "rates on 8 GiB buffers (torch's kernels)")
@@ -337,7 +340,8 @@ def main():
         return
     rec = torch.empty((U, g.record_bytes()), dtype=torch.uint8, device=dev)
     out = torch.empty_like(x)
-    ws = tact.workspace(g, U, dev)
+    chunk = U if args.ws_units is None else max(1, min(args.ws_units, U))
+    ws = tact.workspace(g, chunk, dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -381,7 +385,8 @@ def main():
         ("tact_decompress", alg_d, ms_d)
     achieved = alg / (ms * 1e-3) / 1e9
     roofline_step = (alg_c + alg_d) / ((ms_c + ms_d) * 1e-3) / 1e9
-    tr = measured_traffic(wl.name) if budget == wl.budgets[0] else None
+    # the counter record was taken on the whole batch in one chunk
+    tr = measured_traffic(wl.name) if budget == wl.budgets[0] and chunk == U else None
     traffic = None
     if tr is not None:
         traffic = tr["compress_bytes"] if dom == "tact_compress" else tr["decompress_bytes"]
@@ -396,7 +401,7 @@ def main():
                    "cache_dtype": str(wl.dtype).replace("torch.", ""),
                    "budget_bits": budget, "max_bits": wl.max_bits,
                    "rotation": "hadamard" if g.rotation else "none",
-                   "input_bytes": in_bytes},
+                   "input_bytes": in_bytes, "units_per_chunk": chunk},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

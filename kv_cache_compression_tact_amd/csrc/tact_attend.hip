@@ -68,20 +68,31 @@ struct AttArgs {
   int shw, n_chunks;
 };
 
-// q' = scale * R q (R per 64-channel block) or scale * q
+// q' = scale * R q (R per 64-channel block) or scale * q; one thread per
+// channel (blockDim.x == head_dim), LDS: two head_dim rows.  R = H diag(s) / 8
+// with H by the six-stage butterfly network of k_att_final.
 __global__ void k_att_qrot(AttArgs a) {
+  extern __shared__ float s_q[];
   const int64_t row = static_cast<int64_t>(blockIdx.y) * a.q_heads + blockIdx.x;
-  const float* q = a.q + row * a.head_dim;
-  for (int i = threadIdx.x; i < a.head_dim; i += blockDim.x) {
-    float v = q[i];
-    if (a.rotate) {
-      const int b0 = i & ~63;
-      v = 0.f;
-      for (int j = 0; j < 64; ++j) v = fmaf(hadamard64(i & 63, j) * rotation_sign(j), q[b0 + j], v);
-      v *= 0.125f;
+  const int i = threadIdx.x;
+  float v = a.q[row * a.head_dim + i];
+  if (a.rotate) {
+    float* x = s_q;
+    float* y = s_q + a.head_dim;
+    x[i] = v * rotation_sign(i & 63);
+    __syncthreads();
+#pragma unroll
+    for (int bit = 1; bit < 64; bit <<= 1) {
+      const float u = x[i], w = x[i ^ bit];
+      y[i] = (i & bit) ? w - u : u + w;
+      __syncthreads();
+      float* t = x;
+      x = y;
+      y = t;
     }
-    a.qrot[row * a.head_dim + i] = a.scale * v;
+    v = x[i] * 0.125f;
   }
+  a.qrot[row * a.head_dim + i] = a.scale * v;
 }
 
 // ---- projections: lane = bin f of kv head h --------------------------------
@@ -214,9 +225,14 @@ __device__ __forceinline__ int frag_slot(int axis, int inverse, int m, int ks, i
   return ((((axis * 2 + inverse) * 4 + m) * 2 + ks) * 2 + hl) * kWave + lane;
 }
 
-template <int NP>
-__device__ void mfma_axis_pass(float* fld, int n_lines, int N, int inner, const uint4* frags, int axis,
-                               int inverse, int e) {
+// in_mul multiplies the inputs (with the pass's scale, inside the split);
+// with MAX the pass returns the largest value it wrote (per thread), else
+// -inf.  With gout the outputs go to gout (same indexing) instead of back
+// into the field: 16-byte stores of a lane's four consecutive outputs when
+// the lines are contiguous and their length a multiple of 4.
+template <int NP, bool MAX>
+__device__ float mfma_axis_pass(float* fld, int n_lines, int N, int inner, const uint4* frags, int axis,
+                                int inverse, int e, float in_mul, float* gout) {
   using F = Frag<NP>;
   using vec = typename F::vec;
   const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
@@ -236,8 +252,9 @@ __device__ void mfma_axis_pass(float* fld, int n_lines, int N, int inner, const 
         alo[m][ks] = __builtin_bit_cast(vec, uint2{l.x, l.y});
       }
     }
-  const float sc = ldexpf(1.0f, 14 - e);
-  const float post = ldexpf(1.0f, e - 26);         // 2^-12 (matrix) / sc
+  const float sc = ldexpf(1.0f, 14 - e) * in_mul;
+  const float post = ldexpf(1.0f, e - 26);         // 2^-12 (matrix) / 2^(14 - e)
+  float mx = -INFINITY;
   const int n_tiles = (n_lines + 15) / 16;
   const int nw = static_cast<int>(blockDim.x / kWave);
   for (int ti = wv; ti < n_tiles; ti += nw) {
@@ -270,25 +287,53 @@ __device__ void mfma_axis_pass(float* fld, int n_lines, int N, int inner, const 
         acc[m] = mfma<NP>(ahi[m][ks], blo, acc[m]);
       }
     }
+    if (gout != nullptr) {
+      float* q = gout + (p - fld);
+      if (inner == 1 && (N & 3) == 0) {
+#pragma unroll
+        for (int m = 0; m < F::MT; ++m) {
+          const int n = 16 * m + 4 * g;
+          if (ok && n < N)
+            *reinterpret_cast<float4*>(q + n) =
+                make_float4(acc[m][0] * post, acc[m][1] * post, acc[m][2] * post, acc[m][3] * post);
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < F::MT; ++m)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int n = 16 * m + 4 * g + rr;
+            if (ok && n < N) q[n * inner] = acc[m][rr] * post;
+          }
+      }
+      continue;
+    }
 #pragma unroll
     for (int m = 0; m < F::MT; ++m)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int n = 16 * m + 4 * g + rr;
-        if (ok && n < N) p[n * inner] = acc[m][rr] * post;
+        if (ok && n < N) {
+          const float y = acc[m][rr] * post;
+          p[n * inner] = y;
+          if constexpr (MAX) mx = fmaxf(mx, y);
+        }
       }
   }
+  return mx;
 }
 
-__device__ void axis_pass(float* fld, const AttArgs& a, int axis, int inverse, int e) {
+template <bool MAX>
+__device__ float axis_pass(float* fld, const AttArgs& a, int axis, int inverse, int e, float in_mul,
+                           float* gout = nullptr) {
   // field [S][H][W]; axis 0: lines over (h, w), elements H*W apart; axis 1:
   // lines over (s, w), W apart; axis 2: lines over (s, h), contiguous
   const int N = axis == 0 ? a.S : (axis == 1 ? a.H : a.W);
   const int n_lines = a.shw / N;
   const int inner = axis == 0 ? a.H * a.W : (axis == 1 ? a.W : 1);
-  if (N <= 16) mfma_axis_pass<16>(fld, n_lines, N, inner, a.frags, axis, inverse, e);
-  else if (N <= 32) mfma_axis_pass<32>(fld, n_lines, N, inner, a.frags, axis, inverse, e);
-  else mfma_axis_pass<64>(fld, n_lines, N, inner, a.frags, axis, inverse, e);
+  if (N <= 16) return mfma_axis_pass<16, MAX>(fld, n_lines, N, inner, a.frags, axis, inverse, e, in_mul, gout);
+  if (N <= 32) return mfma_axis_pass<32, MAX>(fld, n_lines, N, inner, a.frags, axis, inverse, e, in_mul, gout);
+  return mfma_axis_pass<64, MAX>(fld, n_lines, N, inner, a.frags, axis, inverse, e, in_mul, gout);
 }
 
 // The DCT tables as split fp16 A fragments of the field passes, one block
@@ -393,27 +438,51 @@ __global__ __launch_bounds__(kFieldThreads) void k_att_field(AttArgs a) {
   int e_in = 0;
   if (ss > 0.f) frexpf(sqrtf(ss) * 1.0001f, &e_in);
   if (!(ss < INFINITY)) e_in = 128;         // the sum overflowed: the largest scale
-  for (int axis = 2; axis >= 0; --axis)
+  // the inverse passes, W then H then S; the last one (the lowest axis
+  // transformed) also yields the scores' maximum
+  const int last_inv = a.axes ? __builtin_ctz(a.axes) : 3;
+  float m = -INFINITY;
+  for (int axis = 2; axis > last_inv; --axis)
     if (a.axes & (1 << axis)) {
-      axis_pass(fld, a, axis, 1, e_in);
+      axis_pass<false>(fld, a, axis, 1, e_in, 1.0f);
       __syncthreads();
     }
-  float m = -INFINITY;
-  for (int e = threadIdx.x; e < a.shw; e += blockDim.x) m = fmaxf(m, fld[e]);
+  if (last_inv < 3) {
+    m = axis_pass<true>(fld, a, last_inv, 1, e_in, 1.0f);
+    __syncthreads();
+  } else {
+    for (int e = threadIdx.x; e < a.shw; e += blockDim.x) m = fmaxf(m, fld[e]);
+  }
   m = block_reduce(m, true, red);
+  // p = exp(x - m) / l: each exponential once; the division by l is folded
+  // into the first forward pass's input scale
   float l = 0.f;
-  for (int e = threadIdx.x; e < a.shw; e += blockDim.x) l += expf(fld[e] - m);
+  for (int e = threadIdx.x; e < a.shw; e += blockDim.x) {
+    const float v = expf(fld[e] - m);
+    fld[e] = v;
+    l += v;
+  }
   l = block_reduce(l, false, red);
   const float lse = m + logf(l);
-  for (int e = threadIdx.x; e < a.shw; e += blockDim.x) fld[e] = expf(fld[e] - lse);
-  __syncthreads();
-  // probabilities: L2 norm at most 1
-  for (int axis = 0; axis < 3; ++axis)
+  const float il = 1.0f / l;
+  if (a.axes == 0) {
+    for (int e = threadIdx.x; e < a.shw; e += blockDim.x) fld[e] *= il;
+    __syncthreads();
+  }
+  // probabilities: L2 norm at most 1; the last forward pass (the highest
+  // axis transformed) writes straight to the global field
+  const int last_fwd = a.axes ? 31 - __builtin_clz(a.axes) : -1;
+  float in_mul = il;
+  for (int axis = 0; axis < last_fwd; ++axis)
     if (a.axes & (1 << axis)) {
-      axis_pass(fld, a, axis, 0, 1);
+      axis_pass<false>(fld, a, axis, 0, 1, in_mul);
+      in_mul = 1.0f;
       __syncthreads();
     }
-  for (int e = threadIdx.x; e < a.shw; e += blockDim.x) gf[e] = fld[e];
+  if (last_fwd >= 0)
+    axis_pass<false>(fld, a, last_fwd, 0, 1, in_mul, gf);
+  else
+    for (int e = threadIdx.x; e < a.shw; e += blockDim.x) gf[e] = fld[e];
   if (threadIdx.x == 0) a.lse[row] = lse;
 }
 
@@ -634,31 +703,46 @@ __global__ __launch_bounds__(kWave) void k_att_out(AttArgs a) {
 }
 
 // ---- sum over chunks, undo the rotation ----------------------------------
+// One thread per channel (blockDim.x == head_dim); LDS: two head_dim rows.
+// R^T = diag(s) H / 8 on each 64-block: H by a six-stage butterfly network
+// (Sylvester order: stage `bit` maps (a, b) at (i, i | bit) to (a + b, a - b)).
 __global__ void k_att_final(AttArgs a) {
   extern __shared__ float s_o[];
   const int qh = blockIdx.x;
   const int64_t pair = blockIdx.y;
   const int h = qh / a.rep, r = qh % a.rep;
   const int d = a.head_dim;
-  const float* src = a.partial + (pair * a.kv_heads + h) * a.n_chunks * a.rep * d;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) {
-    float v = 0.f;
-    for (int c = 0; c < a.n_chunks; ++c) v += src[(static_cast<int64_t>(c) * a.rep + r) * d + i];
-    s_o[i] = v;
+  const int i = threadIdx.x;
+  const float* src = a.partial + (pair * a.kv_heads + h) * a.n_chunks * a.rep * d + r * d + i;
+  const int64_t cs = static_cast<int64_t>(a.rep) * d;       // between chunks
+  // four independent partial sums, so the loads are in flight together
+  float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
+  int c = 0;
+  for (; c + 4 <= a.n_chunks; c += 4) {
+    v0 += src[c * cs];
+    v1 += src[(c + 1) * cs];
+    v2 += src[(c + 2) * cs];
+    v3 += src[(c + 3) * cs];
   }
-  __syncthreads();
-  float* o = a.out + (pair * a.q_heads + qh) * d;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) {
-    float v = s_o[i];
-    if (a.rotate) {
-      // (R^T v)_j = s_j / 8 * sum_i H[j][i] v_i within the 64-block
-      const int b0 = i & ~63;
-      v = 0.f;
-      for (int k = 0; k < 64; ++k) v = fmaf(hadamard64(i & 63, k), s_o[b0 + k], v);
-      v *= 0.125f * rotation_sign(i & 63);
+  for (; c < a.n_chunks; ++c) v0 += src[c * cs];
+  float v = (v0 + v1) + (v2 + v3);
+  if (a.rotate) {
+    float* x = s_o;
+    float* y = s_o + d;
+    x[i] = v;
+    __syncthreads();
+#pragma unroll
+    for (int bit = 1; bit < 64; bit <<= 1) {
+      const float u = x[i], w = x[i ^ bit];
+      y[i] = (i & bit) ? w - u : u + w;
+      __syncthreads();
+      float* t = x;
+      x = y;
+      y = t;
     }
-    o[i] = v;
+    v = x[i] * (0.125f * rotation_sign(i & 63));
   }
+  a.out[(pair * a.q_heads + qh) * d + i] = v;
 }
 
 }  // namespace
@@ -733,7 +817,8 @@ void launch_attend(const Geometry& g, int64_t n_pairs, int q_heads, RecordView k
   a.n_chunks = attend_chunks(g);
   const unsigned np = static_cast<unsigned>(n_pairs);
   hipLaunchKernelGGL(k_att_frags, dim3(6), dim3(kWave), 0, s, a);
-  hipLaunchKernelGGL(k_att_qrot, dim3(q_heads, np), dim3(g.head_dim), 0, s, a);
+  hipLaunchKernelGGL(k_att_qrot, dim3(q_heads, np), dim3(g.head_dim),
+                     2 * g.head_dim * sizeof(float), s, a);
   const dim3 gp((a.shw + 255) / 256, g.kv_heads, np), go(a.n_chunks, g.kv_heads, np);
   if (g.head_dim == 64) {
     launch_proj<1>(gp, a, s);
@@ -754,7 +839,7 @@ void launch_attend(const Geometry& g, int64_t n_pairs, int q_heads, RecordView k
     launch_out<4>(go, a, s);
   }
   hipLaunchKernelGGL(k_att_final, dim3(q_heads, np), dim3(g.head_dim),
-                     g.head_dim * sizeof(float), s, a);
+                     2 * g.head_dim * sizeof(float), s, a);
 }
 
 }  // namespace tact

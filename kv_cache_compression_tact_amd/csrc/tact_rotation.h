@@ -24,11 +24,6 @@ __device__ __forceinline__ float rotation_sign(int j) {
   return (splitmix64(kRotationSeed + static_cast<uint64_t>(j)) >> 63) ? -1.0f : 1.0f;
 }
 
-// H_64[i][j] as +1 / -1
-__device__ __forceinline__ float hadamard64(int i, int j) {
-  return (__builtin_popcount(i & j) & 1) ? -1.0f : 1.0f;
-}
-
 }  // namespace
 
 #endif  // TACT_ROTATION_H_
