@@ -40,6 +40,7 @@ namespace {
 constexpr int kWave = 64;
 
 #include "tact_mfma_ops.h"
+#include "tact_bitplanes.h"
 // raw buffer descriptor (gfx9 word 3): loads past its byte range return 0
 constexpr int kBufWord3 = 0x00020000;
 constexpr int kPastBuffer = 0x7FFFFFF0;
@@ -168,6 +169,8 @@ __global__ __launch_bounds__(256) void k_att_proj(AttArgs a) {
   float acc[RQ];
 #pragma unroll
   for (int r = 0; r < RQ; ++r) acc[r] = 0.f;
+  // planes decoded per bin: the wave's widest bin rounded up to 1, 2, 4 or 8
+  const int nbc = bw <= 1 ? 1 : bw <= 2 ? 2 : bw <= 4 ? 4 : 8;
 #pragma unroll
   for (int hw = 0; hw < WPP; ++hw) {
     uint32_t wl[8], wh[8];
@@ -178,19 +181,32 @@ __global__ __launch_bounds__(256) void k_att_proj(AttArgs a) {
       wl[k] = w.x;
       wh[k] = w.y;
     }
-    // channels in groups of 4: each plane gives a nibble, spread into one
-    // byte per channel (byte i of `codes` collects channel 4 t4 + i; the
-    // spread stays a 24-bit multiply)
+    // one code byte per channel: cq[t4] byte i = channel 4 t4 + i
+    uint32_t cq[16];
+    {
+      uint32_t ql[8], qh[8];
+      if (nbc == 1) {
+        planes_to_codes<1>(wl, ql);
+        planes_to_codes<1>(wh, qh);
+      } else if (nbc == 2) {
+        planes_to_codes<2>(wl, ql);
+        planes_to_codes<2>(wh, qh);
+      } else if (nbc == 4) {
+        planes_to_codes<4>(wl, ql);
+        planes_to_codes<4>(wh, qh);
+      } else {
+        planes_to_codes<8>(wl, ql);
+        planes_to_codes<8>(wh, qh);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        cq[j] = ql[j];
+        cq[8 + j] = qh[j];
+      }
+    }
 #pragma unroll 4
     for (int t4 = 0; t4 < 16; ++t4) {
-      uint32_t codes = 0;
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (k < bw) {
-          uint32_t sp = __builtin_amdgcn_ubfe(t4 < 8 ? wl[k] : wh[k], (4 * t4) & 31, 4) * 0x204081u;
-          asm("" : "+v"(sp));
-          codes |= (sp & 0x01010101u) << k;
-        }
+      const uint32_t codes = cq[t4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int jj = 4 * t4 + i;
