@@ -505,8 +505,8 @@ __global__ __launch_bounds__(kFieldThreads) void k_att_field(AttArgs a) {
 // ---- output partial sums: lane = channel, one wave per chunk of bins ------
 // Bins are taken 64 at a time.  Lane j loads bin j's side info, its query
 // heads' probabilities (folded with the bin's gain) and its plane words, and
-// turns the planes into one byte of code per channel (each plane's nibble
-// spread into four bytes, as in the projections), written to LDS.  The wave
+// turns the planes into one byte of code per channel (the planes transposed,
+// as in the projections), written to LDS.  The wave
 // then walks the coded bins: a lane reads its channel's code byte, looks up
 // the level and accumulates.  Planes at or past a bin's width were loaded as
 // zeros, so the batch is decoded over NB planes (its largest width rounded up
@@ -527,26 +527,19 @@ template <int WPP, int RC, int NB>
 __device__ __forceinline__ void out_group(OutStage<WPP, RC>& st, const uint32_t (&wk)[8][2 * WPP],
                                           uint64_t todo, int bj, const float (&pg)[RC],
                                           float (&acc)[RC][WPP], int lane) {
-  // codes of bin `lane`, one byte per channel
+  // codes of bin `lane`, one byte per channel (the planes of each 32-channel
+  // half transposed)
 #pragma unroll
   for (int hw = 0; hw < WPP; ++hw)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t c4[4];
+    for (int half = 0; half < 2; ++half) {
+      uint32_t pl[NB], c8[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t4 = 4 * q + i;
-        uint32_t codes = 0;
-#pragma unroll
-        for (int k = 0; k < NB; ++k) {
-          uint32_t sp = __builtin_amdgcn_ubfe(wk[k][2 * hw + (t4 >= 8)], (4 * t4) & 31, 4) * 0x204081u;
-          asm("" : "+v"(sp));
-          codes |= (sp & 0x01010101u) << k;
-        }
-        c4[i] = codes;
-      }
-      *reinterpret_cast<uint4*>(st.code + lane * st.kRow + hw * 16 + 4 * q) =
-          make_uint4(c4[0], c4[1], c4[2], c4[3]);
+      for (int k = 0; k < NB; ++k) pl[k] = wk[k][2 * hw + half];
+      planes_to_codes<NB>(pl, c8);
+      uint4* dst = reinterpret_cast<uint4*>(st.code + lane * st.kRow + hw * 16 + 8 * half);
+      dst[0] = make_uint4(c8[0], c8[1], c8[2], c8[3]);
+      dst[1] = make_uint4(c8[4], c8[5], c8[6], c8[7]);
     }
   float* prow = reinterpret_cast<float*>(st.code + lane * st.kRow + st.kCodes);
   if constexpr (RC >= 4) {
