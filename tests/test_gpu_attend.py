@@ -144,10 +144,12 @@ def test_attend_quantizer_backends(quant):
         assert np.max(np.abs(o[r] - o_ref[r])) <= 1e-5 * vrms * (1 + abs(l_ref[r]))
 
 
-@pytest.mark.parametrize("axes", [(0, 2), ()])
+@pytest.mark.parametrize("axes", [(0, 2), (0, 1), (1, 2), (1,), ()])
 def test_attend_axis_subset(axes):
-    # records coded with two of the three axes, or with none: the field
-    # transforms follow
+    # records coded with a subset of the axes, or with none: the field
+    # transforms follow (the last inverse pass, which also yields the scores'
+    # maximum, and the last forward pass, which writes the field out, are
+    # then other axes than S and W)
     S, H, W, hk, d = 6, 5, 7, 2, 64
     p = O.Params(S, H, W, hk, d, 2, 8)
     g = tact.Geometry(S, H, W, hk, d, 2, axes=sum(1 << a for a in axes))
