@@ -49,10 +49,11 @@ tact_status tact_dbg_bin_variance(const tact_params* p, int64_t n_units, const v
                                   hipStream_t stream);
 
 /* Stage 3, second half: bits[n_units * n_bins] (uint8) from variances
- * var[n_units * n_bins] (fp32), by the allocation kernel of tact_compress. */
+ * var[n_units * n_bins] (fp32), by the allocation kernels of tact_compress
+ * (the workspace holds their scratch). */
 tact_status tact_dbg_allocate(const tact_params* p, int64_t n_units,
-                              const float* var, uint8_t* bits,
-                              hipStream_t stream);
+                              const float* var, uint8_t* bits, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /* Stage 4: complete records (gains, bits, group index, codes) of the fp32
  * coefficients `coef` (n_units unit tensors, packed) with the allocation of

@@ -63,7 +63,7 @@ def _load():
         "tact_dbg_workspace_bytes": (sz, [P, i64]),
         "tact_dbg_dct3": (i32, [P, i64, i32, vp, vp, vp, sz, vp]),
         "tact_dbg_bin_variance": (i32, [P, i64, vp, vp, vp, sz, vp]),
-        "tact_dbg_allocate": (i32, [P, i64, vp, vp, vp]),
+        "tact_dbg_allocate": (i32, [P, i64, vp, vp, vp, sz, vp]),
         "tact_dbg_quantize": (i32, [P, i64, vp, vp, vp, vp, sz, vp]),
         "tact_dbg_dequantize": (i32, [P, i64, vp, vp, vp, sz, vp]),
     }
@@ -434,7 +434,8 @@ def dbg_allocate(var: torch.Tensor, geom: Geometry) -> torch.Tensor:
     if U == 0:
         return bits
     p = geom.params()
-    _check(_lib.tact_dbg_allocate(ctypes.byref(p), U, _ptr(var), _ptr(bits),
+    ws = _dbg_ws(geom, U, var.device)
+    _check(_lib.tact_dbg_allocate(ctypes.byref(p), U, _ptr(var), _ptr(bits), _ptr(ws), ws.numel(),
                                   _stream()), "tact_dbg_allocate")
     return bits
 

@@ -127,7 +127,7 @@ int64_t var_stride(const Geometry& g) { return align256(4 * g.n_bins * var_parts
 
 int64_t unit_ws_bytes(const Geometry& g) {
   return align256(4 * g.n_entries) + 4 * 2 * var_stride(g) + align256(4 * g.n_bins) +
-         g.record_bytes;
+         kAllocScratchBytes + g.record_bytes;
 }
 
 constexpr int64_t kTableBytes = align256(4 * kDctTableFloats);
@@ -152,6 +152,7 @@ struct Workspace {
   float* var;
   float* invg;
   uint32_t* poff;
+  uint8_t* alloc;      // the allocation's scratch
   uint8_t* recs;
 };
 
@@ -168,6 +169,8 @@ Workspace carve(const Geometry& g, int64_t chunk, void* ws) {
   b += chunk * 4 * var_stride(g);
   w.poff = reinterpret_cast<uint32_t*>(b);
   b += chunk * align256(4 * g.n_bins);
+  w.alloc = b;
+  b += chunk * kAllocScratchBytes;
   w.recs = b;
   return w;
 }
@@ -311,8 +314,8 @@ void compress_chunk(const Geometry& g, int64_t cn, const void* kv, int64_t kv_st
   const int64_t vs = var_stride(g);
   const float inv_d = 1.0f / static_cast<float>(g.head_dim);
   const StatsLayout sl = forward_stats(g, cn, kv, kv_stride, w, s);
-  launch_allocate2(g, cn, w.var, vs, sl.parts, inv_d, nullptr, view(g, recs), w.poff, w.invg, s,
-                   sl.planes);
+  launch_allocate2(g, cn, w.var, vs, sl.parts, inv_d, nullptr, view(g, recs), w.poff, w.invg,
+                   w.alloc, s, sl.planes);
   if (fused_path(g)) {
     launch_quant(g, cn, w.coef, g.n_entries, w.invg, vs, view(g, recs), w.poff, s);
     return;
@@ -760,24 +763,25 @@ tact_status tact_dbg_bin_variance(const tact_params* p, int64_t n_units, const v
   const StatsLayout sl = forward_stats(g, n_units, kv, g.n_entries, w, stream);
   // the allocation's own sum of the partials, scaled by 1/d, is the output
   launch_allocate2(g, n_units, w.var, var_stride(g), sl.parts, 1.0f / static_cast<float>(g.head_dim),
-                   nullptr, RecordView{}, nullptr, nullptr, stream, sl.planes, var);
+                   nullptr, RecordView{}, nullptr, nullptr, w.alloc, stream, sl.planes, var);
   return after_launch("tact_dbg_bin_variance");
 }
 
 tact_status tact_dbg_allocate(const tact_params* p, int64_t n_units, const float* var,
-                              uint8_t* bits, hipStream_t stream) {
+                              uint8_t* bits, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
   Geometry g;
+  Workspace w;
   tact_status st;
-  if ((st = make_geometry(p, &g)) != TACT_OK) return st;
-  if ((st = check_units(n_units)) != TACT_OK) return st;
-  if (n_units > kMaxChunkUnits)
-    return fail(TACT_ERR_INVALID_ARGUMENT, "tact_dbg_allocate: n_units=%lld, at most %lld",
-                (long long)n_units, (long long)kMaxChunkUnits);
+  if ((st = dbg_prologue("tact_dbg_allocate", p, n_units, workspace, workspace_bytes, &g, &w)) !=
+      TACT_OK)
+    return st;
   if (n_units == 0) return ok();
   if ((st = check_buffer(var, "var", 4)) != TACT_OK) return st;
   if ((st = check_buffer(bits, "bits", 1)) != TACT_OK) return st;
   RecordView none{};
-  launch_allocate2(g, n_units, var, g.n_bins, 1, 1.0f, bits, none, nullptr, nullptr, stream);
+  launch_allocate2(g, n_units, var, g.n_bins, 1, 1.0f, bits, none, nullptr, nullptr, w.alloc,
+                   stream);
   return after_launch("tact_dbg_allocate");
 }
 
@@ -803,7 +807,7 @@ tact_status tact_dbg_quantize(const tact_params* p, int64_t n_units, const float
   // n_bins, which the workspace's per-unit stride covers), then the coding
   // pass of the fused path
   const RecordView rv = view(g, records);
-  launch_allocate2(g, n_units, var, g.n_bins, 1, 1.0f, nullptr, rv, w.poff, w.invg, stream);
+  launch_allocate2(g, n_units, var, g.n_bins, 1, 1.0f, nullptr, rv, w.poff, w.invg, w.alloc, stream);
   launch_quant(g, n_units, coef, g.n_entries, w.invg, g.n_bins, rv, w.poff, stream);
   return after_launch("tact_dbg_quantize");
 }

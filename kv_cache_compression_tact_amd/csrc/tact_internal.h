@@ -62,10 +62,14 @@ void launch_axis(const Geometry& g, int64_t n_units, int axis, int inverse, int 
 // inv_gain (stride var_stride) and the variances it allocated from into
 // var_out ([u][bin]); each may be null.  var holds `parts` partial sums per
 // bin, scaled by var_scale: consecutive per bin, or (planes) stored plane by
-// plane as the plane pass writes them, [slab][s][kh][kw] per unit.
+// plane as the plane pass writes them, [slab][s][kh][kw] per unit.  Each unit
+// runs on up to kAllocMaxSlices workgroups; scratch (kAllocScratchBytes per
+// unit, 256-byte aligned) holds their shared histograms and totals.
+constexpr int kAllocMaxSlices = 64;
+constexpr int64_t kAllocScratchBytes = 4 * 8192 + 256 + 16 * kAllocMaxSlices;
 void launch_allocate2(const Geometry& g, int64_t n_units, const float* var, int64_t var_stride,
                       int parts, float var_scale, uint8_t* bits_out, RecordView rec,
-                      uint32_t* plane_off, float* inv_gain, hipStream_t stream,
+                      uint32_t* plane_off, float* inv_gain, void* scratch, hipStream_t stream,
                       bool planes = false, float* var_out = nullptr);
 
 // Fused H and W axes (see tact_mfma.hip); mode 0 = forward: coefficients

@@ -19,10 +19,10 @@
 //               statistics pass), or quantization + bit-plane packing (last
 //               forward axis, coding pass).
 //
-// k_allocate2: reverse water-filling as an exact radix selection of the
-// T-th largest marginal gain (3 histogram sweeps instead of a long
-// bisection), then the index-ordered tie rule, record header and per-bin
-// plane offsets.
+// k_alloc_*: reverse water-filling as an exact radix selection of the T-th
+// largest marginal gain (3 histogram sweeps instead of a long bisection), on
+// several workgroups per unit, then the index-ordered tie rule, record
+// header and per-bin plane offsets.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -1340,7 +1340,7 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
 // breaking ties at the cut by bin index, and writes the record header and
 // per-bin plane offsets.
 // ---------------------------------------------------------------------------
-constexpr int kAllocThreads = 1024;
+constexpr int kAllocThreads = 512;
 
 __device__ __forceinline__ uint64_t gain_key(float v) {
   return v > 0.f ? static_cast<uint64_t>(__double_as_longlong(static_cast<double>(v))) : 0ull;
@@ -1458,41 +1458,44 @@ struct VarView {
   }
 };
 
-// Calls f(v_i) for every bin of one unit, in no particular order: 4
-// consecutive entries per thread per step, in the order of the storage.
+// Calls f(v_i) for the bins of one slice of a unit, in no particular order:
+// 4 consecutive entries per thread per step, in the order of the storage.
+// The slice is [lo, hi) in storage units: bins, or (plane by plane)
+// positions of every head; lo is a multiple of 4, hi too unless it is the end.
 template <typename Fn>
-__device__ __forceinline__ void for_bins4(const VarView& vv, float scale, Fn f) {
-  const int64_t nb = vv.nb;
+__device__ __forceinline__ void for_bins4(const VarView& vv, float scale, int64_t lo, int64_t hi,
+                                          Fn f) {
   if (!vv.planes) {
-    for (int64_t i0 = 4 * static_cast<int64_t>(threadIdx.x); i0 < nb; i0 += 4 * blockDim.x) {
+    for (int64_t i0 = lo + 4 * static_cast<int64_t>(threadIdx.x); i0 < hi; i0 += 4 * blockDim.x) {
       float q[4];
-      var4(vv.v, nb, vv.parts, scale, vv.vec, i0, q);
+      var4(vv.v, vv.nb, vv.parts, scale, vv.vec, i0, q);
       for (int j = 0; j < 4; ++j)
-        if (i0 + j < nb) f(q[j]);
+        if (i0 + j < hi) f(q[j]);
     }
     return;
   }
   // head by head, positions in storage order
   if (vv.vec && (vv.npos & 3) == 0) {
     // four groups of 4 positions per thread per step, all loads first (the
-    // sweep is otherwise one load latency per group); indices past the end
+    // sweep is otherwise one load latency per group); indices past the slice
     // are clamped and their values unused
-    const int64_t n4 = vv.npos / 4;
+    const int64_t n4 = vv.npos / 4, g_lo = lo / 4, g_hi = hi / 4;
+    if (g_hi <= g_lo) return;
     for (int h = 0; h < vv.kv; ++h) {
       const float4* q = reinterpret_cast<const float4*>(vv.v + static_cast<int64_t>(h) * vv.parts * vv.npos);
-      for (int64_t g0 = threadIdx.x; g0 < n4; g0 += 4 * static_cast<int64_t>(blockDim.x)) {
+      for (int64_t g0 = g_lo + threadIdx.x; g0 < g_hi; g0 += 4 * static_cast<int64_t>(blockDim.x)) {
         float4 x0[4], x1[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           int64_t g = g0 + u * static_cast<int64_t>(blockDim.x);
-          g = g < n4 ? g : n4 - 1;
+          g = g < g_hi ? g : g_hi - 1;
           x0[u] = q[g];
           x1[u] = vv.parts > 1 ? q[n4 + g] : float4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int64_t g = g0 + u * static_cast<int64_t>(blockDim.x);
-          if (g >= n4) break;
+          if (g >= g_hi) break;
           float4 acc = x0[u];
           if (vv.parts > 1) {
             acc.x += x1[u].x; acc.y += x1[u].y; acc.z += x1[u].z; acc.w += x1[u].w;
@@ -1507,7 +1510,7 @@ __device__ __forceinline__ void for_bins4(const VarView& vv, float scale, Fn f) 
     }
   } else {
     for (int h = 0; h < vv.kv; ++h)
-      for (int64_t pos = threadIdx.x; pos < vv.npos; pos += blockDim.x) f(vv.at(h, pos, scale));
+      for (int64_t pos = lo + threadIdx.x; pos < hi; pos += blockDim.x) f(vv.at(h, pos, scale));
   }
 }
 
@@ -1517,117 +1520,265 @@ __device__ __forceinline__ bool has_gain_at(int E, int e, int bmax) {
   return E > 0 && d >= 0 && (d & 1) == 0 && d / 2 < bmax;
 }
 
-__global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const float* __restrict__ var,
-                                                             int64_t var_stride,
-                                                             uint8_t* __restrict__ bits_out,
-                                                             RecordView rec,
-                                                             uint32_t* __restrict__ plane_off,
-                                                             float* __restrict__ inv_gain,
-                                                             int parts, float var_scale,
-                                                             int planes,
-                                                             float* __restrict__ var_out) {
+// Several workgroups per unit, each on a slice of its bins.  A unit's
+// scratch holds the three sweeps' histograms, summed over the slices with
+// integer atomics (so the sums do not depend on the order), the cut and the
+// slices' totals; every kernel re-derives the cut from the histograms it
+// needs, so all slices agree on it.
+struct AllocArgs {
+  Geometry g;
+  const float* var;            // partial sums of squares, unit stride var_stride
+  int64_t var_stride;
+  int parts;                   // partial sums per bin
+  float var_scale;
+  int planes;                  // partials stored plane by plane (else per bin)
+  uint8_t* scratch;            // kAllocScratchBytes per unit
+  int64_t slice;               // bins per workgroup (a multiple of kAllocChunk and of 4 kv_heads)
+  uint8_t* bits_out;
+  RecordView rec;
+  uint32_t* plane_off;
+  float* inv_gain;
+  float* var_out;
+};
+constexpr int kAllocChunk = 4 * kAllocThreads;      // bins per step of the final pass
+// scratch layout (bytes): sweep histograms at 0 (2048 + 4096 + 2048 words),
+// the cut at kAllocCutOff, the slice totals at kAllocTotOff
+constexpr int64_t kAllocCutOff = 4 * 8192;
+constexpr int64_t kAllocTotOff = kAllocCutOff + 256;
+static_assert(kAllocTotOff + 16 * kAllocMaxSlices <= kAllocScratchBytes, "allocation scratch");
+
+struct AllocCut {
+  unsigned long long tau;      // the T-th largest gain's key
+  long long need;              // gains equal to tau that get their bit
+  long long eq_total;          // gains equal to tau
+  int all_ties;                // need == eq_total
+};
+
+__device__ __forceinline__ VarView alloc_view(const AllocArgs& a, int64_t u) {
+  VarView vv;
+  vv.v = a.var + u * a.var_stride;
+  vv.nb = a.g.n_bins;
+  vv.npos = static_cast<int64_t>(a.g.S) * a.g.H * a.g.W;
+  vv.parts = a.parts;
+  vv.kv = a.g.kv_heads;
+  vv.planes = a.planes != 0;
+  vv.vec = (reinterpret_cast<uintptr_t>(vv.v) & 15) == 0;
+  return vv;
+}
+
+// the storage slice [lo, hi) of workgroup w: bins, or positions of every head
+__device__ __forceinline__ void alloc_storage_slice(const AllocArgs& a, const VarView& vv, int64_t w,
+                                                    int64_t* lo, int64_t* hi) {
+  if (vv.planes) {
+    const int64_t per = a.slice / vv.kv;
+    *lo = w * per;
+    *hi = *lo + per < vv.npos ? *lo + per : vv.npos;
+  } else {
+    *lo = w * a.slice;
+    *hi = *lo + a.slice < vv.nb ? *lo + a.slice : vv.nb;
+  }
+}
+
+// The cut from the histograms of sweeps 1..stages (hist: 4096 words of LDS).
+// Returns the stage reached: 1 with *ebin == 0 when the T-th largest gain is
+// 0 (the cut is then complete), else the stages asked for.
+__device__ __forceinline__ void alloc_cut(const uint32_t* G, int stages, int bmax, int64_t T, uint32_t* hist,
+                          int* sh, int* ebin, int64_t* above, int* b2, int64_t* above2,
+                          AllocCut* cut) {
+  for (int j = threadIdx.x; j < 2048; j += blockDim.x) hist[j] = G[j];
+  __syncthreads();
+  // gains per exponent e: bins with E in {e, e+2, ..., e+2(bmax-1)} (E > 0);
+  // all bmax gains of zero bins sit at e = 0
+  for (int e = threadIdx.x; e < 2048; e += blockDim.x) {
+    uint32_t c = 0;
+    if (e == 0) {
+      c = hist[0] * static_cast<uint32_t>(bmax);
+    } else {
+      for (int k = 0; k < bmax; ++k) {
+        const int E = e + 2 * k;
+        if (E < 2048) c += hist[E];
+      }
+    }
+    hist[2048 + e] = c;
+  }
+  __syncthreads();
+  select_bucket(hist + 2048, 2048, T, sh, ebin, above);
+  if (*ebin == 0) {
+    if (cut) {
+      cut->tau = 0;
+      cut->eq_total = hist[2048];
+      cut->need = T - *above;
+    }
+    return;
+  }
+  if (stages < 2) return;
+  // The keys hold the fp32 gains exactly in their top 35 bits, so tau, the
+  // T-th largest gain, is fixed by the three digits, and the counts of the
+  // gains above it and equal to it follow from the histograms.
+  for (int j = threadIdx.x; j < 4096; j += blockDim.x) hist[j] = G[2048 + j];
+  __syncthreads();
+  select_bucket(hist, 4096, T - *above, sh, b2, above2);
+  if (stages < 3) return;
+  for (int j = threadIdx.x; j < 2048; j += blockDim.x) hist[j] = G[6144 + j];
+  __syncthreads();
+  int b3;
+  int64_t above3;
+  select_bucket(hist, 2048, T - *above - *above2, sh, &b3, &above3);
+  cut->tau = (static_cast<uint64_t>(*ebin) << 52) | (static_cast<uint64_t>(*b2) << 40) |
+             (static_cast<uint64_t>(b3) << 29);
+  cut->need = T - (*above + *above2 + above3);
+  cut->eq_total = hist[b3];
+}
+
+__global__ __launch_bounds__(256) void k_alloc_clear(uint8_t* scratch) {
+  uint32_t* G = reinterpret_cast<uint32_t*>(scratch + blockIdx.x * kAllocScratchBytes);
+  for (int j = threadIdx.x; j < 8192; j += blockDim.x) G[j] = 0;
+}
+
+// Sweep STAGE over one slice: the histogram of the gains' exponents (1), of
+// the next 12 bits among gains at the cut's exponent (2), of the next 11 bits
+// among those with the cut's 12 bits (3), added into the unit's histogram.
+template <int STAGE>
+__global__ __launch_bounds__(kAllocThreads) void k_alloc_hist(AllocArgs a) {
   __shared__ uint32_t hist[4096];
+  __shared__ int sh[kAllocThreads / kWave];
+  const int64_t u = blockIdx.y;
+  uint32_t* G = reinterpret_cast<uint32_t*>(a.scratch + u * kAllocScratchBytes);
+  const int bmax = a.g.max_bits;
+  int ebin = 0, b2 = 0;
+  int64_t above = 0, above2 = 0;
+  if constexpr (STAGE >= 2) {
+    alloc_cut(G, STAGE - 1, bmax, a.g.total_bits, hist, sh, &ebin, &above, &b2, &above2, nullptr);
+    if (ebin == 0) return;                   // the cut is complete
+    __syncthreads();
+  }
+  constexpr int NH = STAGE == 2 ? 4096 : 2048;
+  for (int j = threadIdx.x; j < NH; j += blockDim.x) hist[j] = 0;
+  __syncthreads();
+  const VarView vv = alloc_view(a, u);
+  int64_t lo, hi;
+  alloc_storage_slice(a, vv, blockIdx.x, &lo, &hi);
+  for_bins4(vv, a.var_scale, lo, hi, [&](float x) {
+    const uint64_t key = gain_key(x);
+    if constexpr (STAGE == 1) {
+      atomicAdd(&hist[key >> 52], 1u);
+    } else if constexpr (STAGE == 2) {
+      if (has_gain_at(static_cast<int>(key >> 52), ebin, bmax)) atomicAdd(&hist[(key >> 40) & 0xFFF], 1u);
+    } else {
+      if (has_gain_at(static_cast<int>(key >> 52), ebin, bmax) &&
+          static_cast<int>((key >> 40) & 0xFFF) == b2)
+        atomicAdd(&hist[(key >> 29) & 0x7FF], 1u);
+    }
+  });
+  __syncthreads();
+  uint32_t* Gs = G + (STAGE == 1 ? 0 : STAGE == 2 ? 2048 : 6144);
+  for (int j = threadIdx.x; j < NH; j += blockDim.x)
+    if (hist[j]) atomicAdd(&Gs[j], hist[j]);
+}
+
+// Per slice: its bins' bits below the cut (count_ge(key, tau + 1)) and its
+// gains equal to the cut; workgroup 0 of a unit also stores the cut.
+__global__ __launch_bounds__(kAllocThreads) void k_alloc_count(AllocArgs a) {
+  __shared__ uint32_t hist[4096];
+  __shared__ int sh[kAllocThreads / kWave];
+  __shared__ long long red[2][kAllocThreads / kWave];
+  const int64_t u = blockIdx.y;
+  uint8_t* sc = a.scratch + u * kAllocScratchBytes;
+  const Geometry& g = a.g;
+  const int bmax = g.max_bits;
+  const bool wf = g.alloc_mode == TACT_ALLOC_WATERFILL && g.total_bits > 0;
+  AllocCut cut{0ull, 0, 0, 1};
+  if (wf) {
+    int ebin, b2 = 0;
+    int64_t above, above2 = 0;
+    alloc_cut(reinterpret_cast<const uint32_t*>(sc), 3, bmax, g.total_bits, hist, sh, &ebin, &above,
+              &b2, &above2, &cut);
+    cut.all_ties = cut.need == cut.eq_total;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *reinterpret_cast<AllocCut*>(sc + kAllocCutOff) = cut;
+  const VarView vv = alloc_view(a, u);
+  int64_t lo, hi;
+  alloc_storage_slice(a, vv, blockIdx.x, &lo, &hi);
+  long long nbits = 0, neq = 0;
+  if (wf) {
+    const uint64_t tau = cut.tau;
+    for_bins4(vv, a.var_scale, lo, hi, [&](float x) {
+      const uint64_t key = gain_key(x);
+      const int b = count_ge(key, tau + 1, bmax);
+      nbits += b;
+      neq += count_ge(key, tau, bmax) - b;
+    });
+  } else if (g.alloc_mode == TACT_ALLOC_UNIFORM) {
+    const int64_t bins = vv.planes ? (hi - lo) * vv.kv : hi - lo;
+    if (threadIdx.x == 0) nbits = (hi > lo ? bins : 0) * static_cast<long long>(g.budget_bits);
+  }
+  // the slice's sums over the block
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    nbits += __shfl_xor(nbits, o, kWave);
+    neq += __shfl_xor(neq, o, kWave);
+  }
+  const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+  if (lane == 0) {
+    red[0][wv] = nbits;
+    red[1][wv] = neq;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long tb = 0, te = 0;
+    for (int j = 0; j < kAllocThreads / kWave; ++j) {
+      tb += red[0][j];
+      te += red[1][j];
+    }
+    long long* tot = reinterpret_cast<long long*>(sc + kAllocTotOff) + 2 * blockIdx.x;
+    tot[0] = tb;
+    tot[1] = te;
+  }
+}
+
+// The final pass over one slice, in bin order: bits (ties at the cut by bin
+// index, continuing the count of the slices before), record header, first
+// planes, reciprocal gains and the variances; workgroup 0 also clears the
+// record's padding.
+__global__ __launch_bounds__(kAllocThreads) void k_alloc_write(AllocArgs a) {
   __shared__ float s_var[4 * kAllocThreads];   // one chunk of variances, bin order
   __shared__ int sh[kAllocThreads / kWave];
-  const int64_t u = blockIdx.x;
-  const float* v = var + u * var_stride;
-  VarView vv;
-  vv.v = v;
-  vv.nb = g.n_bins;
-  vv.npos = static_cast<int64_t>(g.S) * g.H * g.W;
-  vv.parts = parts;
-  vv.kv = g.kv_heads;
-  vv.planes = planes != 0;
-  vv.vec = (reinterpret_cast<uintptr_t>(v) & 15) == 0;
+  const int64_t u = blockIdx.y;
+  const uint8_t* sc = a.scratch + u * kAllocScratchBytes;
+  const Geometry& g = a.g;
+  const VarView vv = alloc_view(a, u);
   const int bmax = g.max_bits;
-  const int64_t T = g.total_bits;
   const int64_t nb = g.n_bins;
-
-  uint64_t tau = 0;
-  int64_t need = 0;        // tied gains (== tau) to hand out in bin order
-  int64_t eq_total = 0;    // all gains == tau
-  const bool wf = g.alloc_mode == TACT_ALLOC_WATERFILL && T > 0;
-  if (wf) {
-    // ---- sweep 1: exponent of the T-th largest gain --------------------
-    for (int j = threadIdx.x; j < 4096; j += blockDim.x) hist[j] = 0;
-    __syncthreads();
-    for_bins4(vv, var_scale, [&](float x) { atomicAdd(&hist[gain_key(x) >> 52], 1u); });
-    __syncthreads();
-    // gains per exponent e: bins with E in {e, e+2, ..., e+2(bmax-1)} (E > 0);
-    // all bmax gains of zero bins sit at e = 0
-    for (int e = threadIdx.x; e < 2048; e += blockDim.x) {
-      uint32_t c = 0;
-      if (e == 0) {
-        c = hist[0] * static_cast<uint32_t>(bmax);
-      } else {
-        for (int k = 0; k < bmax; ++k) {
-          const int E = e + 2 * k;
-          if (E < 2048) c += hist[E];
-        }
-      }
-      hist[2048 + e] = c;
-    }
-    __syncthreads();
-    int ebin;
-    int64_t above;
-    select_bucket(hist + 2048, 2048, T, sh, &ebin, &above);
-    // The keys hold the fp32 gains exactly in their top 35 bits, so tau, the
-    // T-th largest gain, is fixed by the three digits, and the counts of the
-    // gains above it and equal to it follow from the histograms.
-    int64_t gt_total, eq_cnt;
-    if (ebin == 0) {
-      tau = 0;
-      gt_total = above;
-      eq_cnt = hist[2048];
-    } else {
-      // ---- sweep 2: top 12 mantissa bits among gains with exponent ebin --
-      for (int j = threadIdx.x; j < 4096; j += blockDim.x) hist[j] = 0;
-      __syncthreads();
-      for_bins4(vv, var_scale, [&](float x) {
-        const uint64_t key = gain_key(x);
-        if (has_gain_at(static_cast<int>(key >> 52), ebin, bmax))
-          atomicAdd(&hist[(key >> 40) & 0xFFF], 1u);
-      });
-      __syncthreads();
-      int b2;
-      int64_t above2;
-      select_bucket(hist, 4096, T - above, sh, &b2, &above2);
-      // ---- sweep 3: next 11 mantissa bits ---------------------------------
-      for (int j = threadIdx.x; j < 4096; j += blockDim.x) hist[j] = 0;
-      __syncthreads();
-      for_bins4(vv, var_scale, [&](float x) {
-        const uint64_t key = gain_key(x);
-        if (has_gain_at(static_cast<int>(key >> 52), ebin, bmax) &&
-            static_cast<int>((key >> 40) & 0xFFF) == b2)
-          atomicAdd(&hist[(key >> 29) & 0x7FF], 1u);
-      });
-      __syncthreads();
-      int b3;
-      int64_t above3;
-      select_bucket(hist, 2048, T - above - above2, sh, &b3, &above3);
-      tau = (static_cast<uint64_t>(ebin) << 52) | (static_cast<uint64_t>(b2) << 40) |
-            (static_cast<uint64_t>(b3) << 29);
-      gt_total = above + above2 + above3;
-      eq_cnt = hist[b3];
-    }
-    eq_total = eq_cnt;
-    need = T - gt_total;
-  }
-  // ties at the cut need the bin-ordered prefix only when some are left out
-  const bool all_ties = (need == eq_total);
-
-  // ---- final sweep: bits, ties by bin index, header, plane offsets --------
-  uint8_t* bo = bits_out ? bits_out + u * nb : nullptr;
-  uint8_t* r = rec.base ? rec.base + u * rec.stride : nullptr;
-  uint32_t* po = plane_off ? plane_off + u * nb : nullptr;
+  const bool wf = g.alloc_mode == TACT_ALLOC_WATERFILL && g.total_bits > 0;
+  const AllocCut cut = *reinterpret_cast<const AllocCut*>(sc + kAllocCutOff);
+  const uint64_t tau = cut.tau;
+  const int64_t need = cut.need;
+  const bool all_ties = cut.all_ties != 0;
+  // ties and planes of the slices before this one
+  const long long* tot = reinterpret_cast<const long long*>(sc + kAllocTotOff);
   int64_t tie_carry = 0, plane_carry = 0;
-  for (int64_t base = 0; base < nb; base += 4 * blockDim.x) {
+  for (int w = 0; w < static_cast<int>(blockIdx.x); ++w) {
+    const long long nbits = tot[2 * w], neq = tot[2 * w + 1];
+    long long take = neq;
+    if (!all_ties) {
+      take = need - tie_carry;
+      take = take < 0 ? 0 : (take > neq ? neq : take);
+    }
+    tie_carry += neq;
+    plane_carry += nbits + take;
+  }
+  const int64_t lo = static_cast<int64_t>(blockIdx.x) * a.slice;
+  const int64_t hi = lo + a.slice < nb ? lo + a.slice : nb;
+  uint8_t* bo = a.bits_out ? a.bits_out + u * nb : nullptr;
+  uint8_t* r = a.rec.base ? a.rec.base + u * a.rec.stride : nullptr;
+  uint32_t* po = a.plane_off ? a.plane_off + u * nb : nullptr;
+  for (int64_t base = lo; base < hi; base += 4 * blockDim.x) {
     const int64_t i0 = base + 4 * static_cast<int64_t>(threadIdx.x);
     float vi[4];
     if (vv.planes) {
       // the chunk's variances into LDS in bin order, read position by
       // position (consecutive threads, consecutive positions of one head)
-      const int64_t end = base + 4 * blockDim.x < nb ? base + 4 * blockDim.x : nb;
+      const int64_t end = base + 4 * blockDim.x < hi ? base + 4 * blockDim.x : hi;
       const int64_t pos_lo = base / vv.kv;
       const uint32_t np = static_cast<uint32_t>((end - 1) / vv.kv - pos_lo + 1);
       __syncthreads();                       // the previous chunk is read
@@ -1635,17 +1786,17 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
         const uint32_t h = e / np;
         const int64_t pos = pos_lo + (e - h * np);
         const int64_t i = pos * vv.kv + h;
-        if (i >= base && i < end) s_var[i - base] = vv.at(static_cast<int>(h), pos, var_scale);
+        if (i >= base && i < end) s_var[i - base] = vv.at(static_cast<int>(h), pos, a.var_scale);
       }
       __syncthreads();
-      for (int j = 0; j < 4; ++j) vi[j] = i0 + j < nb ? s_var[4 * threadIdx.x + j] : 0.f;
+      for (int j = 0; j < 4; ++j) vi[j] = i0 + j < hi ? s_var[4 * threadIdx.x + j] : 0.f;
     } else {
-      var4(v, nb, parts, var_scale, vv.vec, i0, vi);
+      var4(vv.v, nb, vv.parts, a.var_scale, vv.vec, i0, vi);
     }
     int b[4] = {0, 0, 0, 0}, eqv[4] = {0, 0, 0, 0};
     int eq_sum = 0;
     for (int j = 0; j < 4; ++j) {
-      if (i0 + j >= nb) continue;
+      if (i0 + j >= hi) continue;
       if (g.alloc_mode == TACT_ALLOC_UNIFORM) {
         b[j] = g.budget_bits;
       } else if (wf) {
@@ -1659,8 +1810,8 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
       if (all_ties) {
         for (int j = 0; j < 4; ++j) b[j] += eqv[j];
       } else {
-        int tot;
-        const int ex = block_exscan(eq_sum, sh, &tot);
+        int tot_eq;
+        const int ex = block_exscan(eq_sum, sh, &tot_eq);
         int64_t before = tie_carry + ex;
         for (int j = 0; j < 4; ++j) {
           int64_t avail = need - before;
@@ -1669,7 +1820,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
           b[j] += take;
           before += eqv[j];
         }
-        tie_carry += tot;
+        tie_carry += tot_eq;
       }
     }
     const int bsum = b[0] + b[1] + b[2] + b[3];
@@ -1678,12 +1829,12 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
     int64_t p = plane_carry + pex;
     for (int j = 0; j < 4; ++j) {
       const int64_t i = i0 + j;
-      if (i < nb) {
+      if (i < hi) {
         if (bo) bo[i] = static_cast<uint8_t>(b[j]);
         if (po) po[i] = static_cast<uint32_t>(p);
-        if (var_out) var_out[u * nb + i] = vi[j];
+        if (a.var_out) a.var_out[u * nb + i] = vi[j];
         const float gn = sqrtf(vi[j]);
-        if (inv_gain) inv_gain[u * var_stride + i] = gn > 0.f ? 1.0f / gn : 0.f;
+        if (a.inv_gain) a.inv_gain[u * a.var_stride + i] = gn > 0.f ? 1.0f / gn : 0.f;
         if (r) {
           reinterpret_cast<float*>(r + g.off_gains)[i] = gn;
           r[g.off_bits + i] = static_cast<uint8_t>(b[j]);
@@ -1694,7 +1845,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_allocate2(Geometry g, const f
     }
     plane_carry += ptot;
   }
-  if (r) {
+  if (r && blockIdx.x == 0) {
     for (int64_t k = g.off_gains + 4 * nb + threadIdx.x; k < g.off_bits; k += blockDim.x) r[k] = 0;
     for (int64_t k = g.off_bits + nb + threadIdx.x; k < g.off_groups; k += blockDim.x) r[k] = 0;
     for (int64_t k = g.off_groups + 4 * g.n_groups + threadIdx.x; k < g.off_codes; k += blockDim.x)
@@ -1954,13 +2105,51 @@ void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in,
 #undef TACT_PLANE_ONE
 }
 
+// Bins per allocation workgroup: about 16K, at most kAllocMaxSlices slices
+// per unit, a multiple of the final pass's chunk and of 4 kv_heads (a slice
+// is then whole positions of every head, a multiple of 4 of them).
+int64_t alloc_slice(const Geometry& g) {
+  int64_t want = (g.n_bins + kAllocMaxSlices - 1) / kAllocMaxSlices;
+  if (want < 16384) want = 16384;
+  int64_t a = kAllocChunk, b = 4 * static_cast<int64_t>(g.kv_heads);
+  while (b) {
+    const int64_t t = a % b;
+    a = b;
+    b = t;
+  }
+  const int64_t al = kAllocChunk / a * (4 * static_cast<int64_t>(g.kv_heads));   // lcm
+  return (want + al - 1) / al * al;
+}
+
 void launch_allocate2(const Geometry& g, int64_t n_units, const float* var, int64_t var_stride,
                       int parts, float var_scale, uint8_t* bits_out, RecordView rec,
-                      uint32_t* plane_off, float* inv_gain, hipStream_t s, bool planes,
-                      float* var_out) {
-  hipLaunchKernelGGL(k_allocate2, dim3(static_cast<unsigned>(n_units)), dim3(kAllocThreads), 0, s,
-                     g, var, var_stride, bits_out, rec, plane_off, inv_gain, parts, var_scale,
-                     planes ? 1 : 0, var_out);
+                      uint32_t* plane_off, float* inv_gain, void* scratch, hipStream_t s,
+                      bool planes, float* var_out) {
+  AllocArgs a;
+  a.g = g;
+  a.var = var;
+  a.var_stride = var_stride;
+  a.parts = parts;
+  a.var_scale = var_scale;
+  a.planes = planes ? 1 : 0;
+  a.scratch = static_cast<uint8_t*>(scratch);
+  a.slice = alloc_slice(g);
+  a.bits_out = bits_out;
+  a.rec = rec;
+  a.plane_off = plane_off;
+  a.inv_gain = inv_gain;
+  a.var_out = var_out;
+  const dim3 grid(static_cast<unsigned>((g.n_bins + a.slice - 1) / a.slice),
+                  static_cast<unsigned>(n_units));
+  const dim3 block(kAllocThreads);
+  if (g.alloc_mode == TACT_ALLOC_WATERFILL && g.total_bits > 0) {
+    hipLaunchKernelGGL(k_alloc_clear, dim3(static_cast<unsigned>(n_units)), dim3(256), 0, s, a.scratch);
+    hipLaunchKernelGGL(k_alloc_hist<1>, grid, block, 0, s, a);
+    hipLaunchKernelGGL(k_alloc_hist<2>, grid, block, 0, s, a);
+    hipLaunchKernelGGL(k_alloc_hist<3>, grid, block, 0, s, a);
+  }
+  hipLaunchKernelGGL(k_alloc_count, grid, block, 0, s, a);
+  hipLaunchKernelGGL(k_alloc_write, grid, block, 0, s, a);
 }
 
 void launch_plane_offsets(const Geometry& g, int64_t n_units, RecordView rec, uint32_t* plane_off,

@@ -163,20 +163,22 @@ def test_stage_workspace_is_checked_first():
     L = lib()
     p = _params(rotation=0)
     need = L.tact_dbg_workspace_bytes(ctypes.byref(p), 2)
-    # tables, then per unit the volume, variances, 1/gain, first planes, a record
+    # tables, then per unit the volume, variances, 1/gain, first planes, the
+    # allocation's scratch, a record
     assert need >= 2 * (4 * 4 * 8 * 8 * 2 * 64)
     assert L.tact_dbg_workspace_bytes(ctypes.byref(p), 0) == 0
     assert L.tact_dbg_workspace_bytes(ctypes.byref(p), 65536) == 0
     ws = ctypes.c_void_p(1 << 30)
     for call in (lambda w, n: L.tact_dbg_dct3(ctypes.byref(p), 2, 0, fake, fake, w, n, None),
                  lambda w, n: L.tact_dbg_bin_variance(ctypes.byref(p), 2, fake, fake, w, n, None),
+                 lambda w, n: L.tact_dbg_allocate(ctypes.byref(p), 2, fake, fake, w, n, None),
                  lambda w, n: L.tact_dbg_quantize(ctypes.byref(p), 2, fake, fake, fake, w, n, None),
                  lambda w, n: L.tact_dbg_dequantize(ctypes.byref(p), 2, fake, fake, w, n, None)):
         assert call(None, need) == 3
         assert call(ws, need - 1) == 3
         assert call(ctypes.c_void_p((1 << 30) + 16), need) == 1      # not 256-byte aligned
     assert L.tact_dbg_dct3(ctypes.byref(p), 65536, 0, fake, fake, ws, 1 << 45, None) == 1
-    assert L.tact_dbg_allocate(ctypes.byref(p), 65536, fake, fake, None) == 1
+    assert L.tact_dbg_allocate(ctypes.byref(p), 65536, fake, fake, ws, 1 << 45, None) == 1
 
 
 def test_zero_units_is_a_noop():
