@@ -314,12 +314,15 @@ void compress_chunk(const Geometry& g, int64_t cn, const void* kv, int64_t kv_st
   const int64_t vs = var_stride(g);
   const float inv_d = 1.0f / static_cast<float>(g.head_dim);
   const StatsLayout sl = forward_stats(g, cn, kv, kv_stride, w, s);
-  launch_allocate2(g, cn, w.var, vs, sl.parts, inv_d, nullptr, view(g, recs), w.poff, w.invg,
-                   w.alloc, s, sl.planes);
   if (fused_path(g)) {
-    launch_quant(g, cn, w.coef, g.n_entries, w.invg, vs, view(g, recs), w.poff, s);
+    // the coding pass takes first planes and 1/gain from the record header
+    launch_allocate2(g, cn, w.var, vs, sl.parts, inv_d, nullptr, view(g, recs), nullptr, nullptr,
+                     w.alloc, s, sl.planes);
+    launch_quant(g, cn, w.coef, g.n_entries, view(g, recs), s);
     return;
   }
+  launch_allocate2(g, cn, w.var, vs, sl.parts, inv_d, nullptr, view(g, recs), w.poff, w.invg,
+                   w.alloc, s, sl.planes);
   int ax[3];
   const int m = forward_axes(g, ax);
   const int in_pro = g.dtype == TACT_BF16 ? AX_PRO_BF16 : AX_PRO_F32;
@@ -803,12 +806,11 @@ tact_status tact_dbg_quantize(const tact_params* p, int64_t n_units, const float
   if ((st = check_buffer(coef, "coef", 16)) != TACT_OK) return st;
   if ((st = check_buffer(var, "var", 4)) != TACT_OK) return st;
   if ((st = check_buffer(records, "records", 256)) != TACT_OK) return st;
-  // the allocation writes the header, the first planes and 1/gain (stride
-  // n_bins, which the workspace's per-unit stride covers), then the coding
-  // pass of the fused path
+  // the allocation writes the header, then the coding pass of the fused
+  // path (which takes first planes and 1/gain from the header)
   const RecordView rv = view(g, records);
-  launch_allocate2(g, n_units, var, g.n_bins, 1, 1.0f, nullptr, rv, w.poff, w.invg, w.alloc, stream);
-  launch_quant(g, n_units, coef, g.n_entries, w.invg, g.n_bins, rv, w.poff, stream);
+  launch_allocate2(g, n_units, var, g.n_bins, 1, 1.0f, nullptr, rv, nullptr, nullptr, w.alloc, stream);
+  launch_quant(g, n_units, coef, g.n_entries, rv, stream);
   return after_launch("tact_dbg_quantize");
 }
 

@@ -81,10 +81,10 @@ void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in,
 
 // Quantize + pack the final coefficients coef ([u][bin][head_dim], unit
 // stride ustride; already rotated when the geometry rotates) into the
-// records, given 1/gain and first planes (tact_quant.hip).
+// records, whose header (gains, bits, group index) the allocation has
+// written (tact_quant.hip).
 void launch_quant(const Geometry& g, int64_t n_units, const float* coef, int64_t ustride,
-                  const float* inv_gain, int64_t var_stride, RecordView rec,
-                  const uint32_t* plane_off, hipStream_t stream);
+                  RecordView rec, hipStream_t stream);
 
 // Per-bin first planes of n_units records (from each record's group index
 // and bit widths); with rec2, also those of n_units records of rec2 into

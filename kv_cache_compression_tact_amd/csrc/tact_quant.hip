@@ -39,10 +39,7 @@ struct QuantArgs {
   int64_t ustride;           // elements between units
   int64_t n_bins, total_bits;
   int max_bits;
-  const float* inv_gain;     // fp32 1/gain per bin (0 for gain 0)
-  int64_t var_stride;        // floats per unit in inv_gain
-  const uint32_t* plane_off; // first bit plane of each bin, [u][bin]
-  RecordView rec;
+  RecordView rec;            // header written by the allocation: gains, bits, group index
 };
 
 // Codes of one bin of B bits (B >= 1) for its WPP words of 64 channels:
@@ -96,17 +93,27 @@ __global__ __launch_bounds__(kWave * kQuantWaves) void k_quant(QuantArgs a) {
   if (b0 >= a.n_bins) return;
   constexpr int kHeadDim = 64 * WPP;
 
-  // side info of bin b0 + lane
-  int bj = 0, pj = 0;
+  // side info of bin b0 + lane, from the record's header: the wave's 64
+  // bins are one group of the index, so the first plane of bin b0 + lane is
+  // the group's entry plus the widths of the lanes below (a wave scan), and
+  // 1/gain is formed from the stored gain as the allocation forms it
+  const uint8_t* r = a.rec.base + u * a.rec.stride;
+  int bj = 0;
   float ij = 0.f;
   if (b0 + lane < a.n_bins) {
     const int64_t bin = b0 + lane;
-    const uint8_t* bits = a.rec.base + u * a.rec.stride + a.rec.off_bits;
-    bj = bits[bin];
-    pj = static_cast<int>(a.plane_off[u * a.n_bins + bin]);
-    ij = a.inv_gain[u * a.var_stride + bin];
-    if (bj > a.max_bits || static_cast<int64_t>(static_cast<uint32_t>(pj)) + bj > a.total_bits) bj = 0;
+    bj = r[a.rec.off_bits + bin];
+    const float gn = reinterpret_cast<const float*>(r + a.rec.off_gains)[bin];
+    ij = gn > 0.f ? 1.0f / gn : 0.f;
   }
+  int incl = bj;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  int pj = static_cast<int>(reinterpret_cast<const uint32_t*>(r + a.rec.off_groups)[b0 / kWave]) + incl - bj;
+  if (bj > a.max_bits || static_cast<int64_t>(static_cast<uint32_t>(pj)) + bj > a.total_bits) bj = 0;
 
   const float* cu = a.coef + u * a.ustride + b0 * kHeadDim + lane;
   uint64_t* words = reinterpret_cast<uint64_t*>(a.rec.base + u * a.rec.stride + a.rec.off_codes);
@@ -188,17 +195,13 @@ __global__ __launch_bounds__(kWave * kQuantWaves) void k_quant(QuantArgs a) {
 }  // namespace
 
 void launch_quant(const Geometry& g, int64_t n_units, const float* coef, int64_t ustride,
-                  const float* inv_gain, int64_t var_stride, RecordView rec,
-                  const uint32_t* plane_off, hipStream_t s) {
+                  RecordView rec, hipStream_t s) {
   QuantArgs a;
   a.coef = coef;
   a.ustride = ustride;
   a.n_bins = g.n_bins;
   a.total_bits = g.total_bits;
   a.max_bits = g.max_bits;
-  a.inv_gain = inv_gain;
-  a.var_stride = var_stride;
-  a.plane_off = plane_off;
   a.rec = rec;
   const int64_t per_block = static_cast<int64_t>(kWave) * kQuantWaves;
   const dim3 grid(static_cast<unsigned>((g.n_bins + per_block - 1) / per_block),
