@@ -211,6 +211,9 @@ def _var_cases(rng, nb):
     ((4, 8, 8, 2, 64), 1, 3), ((5, 7, 9, 3, 64), 2, 8), ((3, 14, 14, 1, 128), 1, 8),
     ((1, 1, 3, 1, 64), 1, 2), ((2, 5, 3, 2, 256), 4, 8), ((7, 3, 5, 1, 64), 0, 8),
     ((7, 3, 5, 1, 64), 8, 8), ((6, 6, 6, 4, 64), 3, 4),
+    # several allocation workgroups per unit (about 16K bins each): ties at the
+    # cut are then shared out across slices in bin order
+    ((16, 32, 32, 3, 64), 1, 8), ((32, 24, 24, 4, 128), 2, 5),
 ])
 def test_allocation_bit_exact(geo, budget, bmax):
     g = _geom(*geo, budget, bmax)
@@ -224,8 +227,9 @@ def test_allocation_bit_exact(geo, budget, bmax):
         assert np.array_equal(bits[u].astype(np.int64), ref), u
 
 
-def test_uniform_allocation():
-    g = _geom(3, 4, 5, 2, 64, 3, 8, alloc_mode=tact.ALLOC_UNIFORM)
+@pytest.mark.parametrize("geo", [(3, 4, 5, 2, 64), (32, 24, 24, 4, 128)])
+def test_uniform_allocation(geo):
+    g = _geom(*geo, 3, 8, alloc_mode=tact.ALLOC_UNIFORM)
     var = torch.rand((2,) + g.unit_shape[:-1]).cuda()
     bits = tact.dbg_allocate(var, g).cpu()
     assert torch.all(bits == 3)
