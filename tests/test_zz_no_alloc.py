@@ -75,3 +75,36 @@ def test_noalloc_matches_roundtrip_on_consecutive_calls():
         torch.cuda.synchronize()
         assert torch.equal(rec, ref_rec) and torch.equal(out, ref_out)
     say("noalloc: equal to tact_roundtrip on every call")
+
+
+@pytest.mark.gpu
+def test_noalloc_roundtrip_captured_in_a_graph():
+    # The callers this entry point serves include code under HIP graph
+    # capture: the captured call allocates nothing and records only kernel
+    # launches, so every replay (with the program's own work between them)
+    # gives the eager results.
+    import kv_cache_compression_tact_amd as tact
+    gen = torch.Generator(device="cpu").manual_seed(37)
+    x = torch.randn((3, 5, 7, 9, 3, 64), generator=gen).to(torch.bfloat16).cuda()
+    ref_out, ref_rec = tact.roundtrip(x, 2)
+    out = torch.empty_like(x)
+    rec = torch.empty_like(ref_rec)
+    tact.roundtrip_noalloc(x, 2, out=out, records=rec)      # eager: the array's address is known
+    torch.cuda.synchronize()
+    assert torch.equal(rec, ref_rec) and torch.equal(out, ref_out)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        tact.roundtrip_noalloc(x, 2, out=out, records=rec)
+    for replay in range(3):
+        out.zero_()
+        rec.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        say("noalloc graph replay", replay)
+        assert torch.equal(rec, ref_rec) and torch.equal(out, ref_out)
+    # eager calls between replays leave the captured call's results unchanged
+    y = torch.randn(tuple(x.shape), generator=gen).to(torch.bfloat16).cuda()
+    tact.roundtrip_noalloc(y, 1, out=torch.empty_like(y))
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(rec, ref_rec) and torch.equal(out, ref_out)
