@@ -83,6 +83,7 @@ __device__ __forceinline__ uint16_t bf16_rne_bits(float v) {
 // ---------------------------------------------------------------------------
 #include "tact_rotation.h"
 #include "tact_lane_ops.h"
+#include "tact_bitplanes.h"
 
 // Raw buffer access (descriptor word 3 of gfx9 raw buffers): loads past
 // the descriptor's byte range return 0 and stores past it are dropped, so
@@ -831,6 +832,16 @@ constexpr int kDecodeWaves = 12;
 // (one group: block b takes planes b, b + grid, ...).
 constexpr int kXcds = 8;
 
+// Decode staging of one plane row: bin kw takes 5 16-byte slots ({bits,
+// gain, first level-table entry, 0}, then its 64 code bytes, channel c at
+// byte c), and 12 more slots follow every 8 bins, so that the four bins
+// one W-stage read serves (kw, kw + 8, kw + 16, kw + 24) sit 52 slots
+// (208 words, 16 banks mod 64) apart: their 16-lane code reads fall in
+// distinct banks.
+__host__ __device__ constexpr int decode_stage_slot(int kw) { return kw * 5 + (kw >> 3) * 12; }
+// bytes of a row's staging for nk bins
+__host__ __device__ constexpr int decode_stage_bytes(int nk) { return (decode_stage_slot(nk - 1) + 5) * 16; }
+
 template <int GROUPS>
 // Plane indices fit in 32 bits: a launch covers at most one workspace chunk
 // of units (24 GiB of fp32 volume, under 2^28 planes of >= 64 entries), so
@@ -897,15 +908,9 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
   // byte strides of a slice: one w step, one h row; this lane's columns
   const int cbytes = static_cast<int>(a.C) * 4;
   const int row_bytes = W * cbytes;
-  // LDS row stride in 64-float positions: the decode pass stages the side
-  // info of NPW bins (80 bytes each, plus 112 bytes after every 8 bins) in a
-  // row's area, so short rows are padded
-  const int RW = MODE == MODE_DEQUANT ? max(W, (NPW * 80 + (NPW / 8 - 1) * 112 + 255) / 256) : W;
-  // 16-byte slot of bin kw's staging: 5 slots per bin and 7 more after every
-  // 8 bins, so that the four bins one read serves (kw, kw + 4, kw + 8,
-  // kw + 12 for kw % 8 < 4; 320 bytes apart without the gaps) start in
-  // distinct banks
-  auto stage_slot = [](int kw) { return kw * 5 + (kw >> 3) * 7; };
+  // LDS row stride in 64-float positions: the decode pass stages NPW bins
+  // in a row's area (decode_stage_bytes), so short rows are padded
+  const int RW = MODE == MODE_DEQUANT ? max(W, (decode_stage_bytes(NPW) + 255) / 256) : W;
   // bin of (s, kh, kw) of a plane's head
   auto bin_of3 = [&](const PlaneId& id, int kh, int kw) -> int64_t {
     return ((static_cast<int64_t>(id.s) * H + kh) * W + kw) * a.kv_heads + id.head;
@@ -1058,11 +1063,15 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
       p = pn;
     }
   } else {
-    // side info (bits, first plane, gain) and code words of this wave's kh
-    // rows, lane = kw; fetched one plane ahead
-    int bj[SLH], pjv[SLH];
-    float gjv[SLH];
-    uint2 wd[SLH][8];
+    // Side info (bits, first plane, gain) and code words of this wave's kh
+    // rows, fetched one plane ahead: lane (r, kw), r = lane / 32, holds bin
+    // (kh, kw) of the wave's row q = 2 ps + r in pass ps (two rows at once,
+    // so that a plane row of up to 32 bins keeps half the wave busy).
+    constexpr int kPass = (SLH + 1) / 2;
+    const int srow = lane / 32, skw = lane % 32;
+    int bj[kPass], pjv[kPass];
+    float gjv[kPass];
+    uint2 wd[kPass][8];
     // Record reads through buffer descriptors (32-bit offsets per lane).
     // Every call issues the same loads: lanes with nothing to read take an
     // offset past the buffer and read 0.  With fixed load and store counts
@@ -1075,14 +1084,15 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
       const __amdgpu_buffer_rsrc_t rg = make_rsrc(r + a.rec.off_gains, 4 * a.n_bins);
       const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.plane_off + id.u * a.n_bins, 4 * a.n_bins);
 #pragma unroll
-      for (int q = 0; q < SLH; ++q) {
+      for (int ps = 0; ps < kPass; ++ps) {
+        const int q = 2 * ps + srow;
         const int kh = wv + kWaves * q;
-        const bool ok = kh < H && lane < W;
-        const int bin = static_cast<int>(bin_of3(id, kh, lane));
+        const bool ok = q < SLH && kh < H && skw < W;
+        const int bin = static_cast<int>(bin_of3(id, ok ? kh : 0, ok ? skw : 0));
         const int vb = ok ? bin : kPastBuffer, vw = ok ? 4 * bin : kPastBuffer;
-        bj[q] = __builtin_amdgcn_raw_buffer_load_b8(rb, vb, 0, 0);
-        pjv[q] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(ro, vw, 0, 0));
-        gjv[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, vw, 0, 0));
+        bj[ps] = __builtin_amdgcn_raw_buffer_load_b8(rb, vb, 0, 0);
+        pjv[ps] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(ro, vw, 0, 0));
+        gjv[ps] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, vw, 0, 0));
       }
     };
     auto fetch_words = [&](int64_t p) {
@@ -1091,15 +1101,15 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
       const __amdgpu_buffer_rsrc_t rw =
           make_rsrc(a.rec.base + id.u * a.rec.stride + a.rec.off_codes, a.total_bits * wpp * 8);
 #pragma unroll
-      for (int q = 0; q < SLH; ++q) {
-        int b = bj[q];
-        const int64_t pj = static_cast<uint32_t>(pjv[q]);
+      for (int ps = 0; ps < kPass; ++ps) {
+        int b = bj[ps];
+        const int64_t pj = static_cast<uint32_t>(pjv[ps]);
         if (b > a.max_bits || pj + b > a.total_bits) b = 0;
-        bj[q] = b;
+        bj[ps] = b;
         const int base = 8 * (static_cast<int>(pj) * wpp + id.half);
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          wd[q][k] = __builtin_bit_cast(
+          wd[ps][k] = __builtin_bit_cast(
               uint2, __builtin_amdgcn_raw_buffer_load_b64(rw, k < b ? base + 8 * wpp * k : kPastBuffer, 0, 0));
       }
     };
@@ -1109,7 +1119,7 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
     auto gain_max = [&]() {
       float m = 0.f;
 #pragma unroll
-      for (int q = 0; q < SLH; ++q) m = fmaxf(m, bj[q] > 0 ? gjv[q] : 0.f);
+      for (int ps = 0; ps < kPass; ++ps) m = fmaxf(m, bj[ps] > 0 ? gjv[ps] : 0.f);
       return wave_max(m);
     };
     int64_t p = walk.at(k0);
@@ -1148,35 +1158,63 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
       const float gsc = ldexpf(1.0f, 2 - e);
       const float yscale = ldexpf(1.0f, e - 20);
       // ---- inverse W: decode into the B fragments, contract; a wave owns one
-      // kh row.  The row's LDS area first holds its bins' side info and code
-      // words, 80 bytes per bin: {bits, gain, first level-table entry, 0},
-      // the low 32-bit halves of the 8 plane words, then their high halves
-      // (planes at or above the bin's bit width are 0; bins without bits
-      // have gain 0).  Lane (t, g) then rebuilds the codes of its
-      // channels 4t..4t+3 for its K rows kw: it reads the 8 halves that hold
-      // its channels at once, and each plane gives a nibble, spread into one
-      // byte per channel.
+      // kh row.  The row's LDS area first holds its bins' staging, 80 bytes
+      // per bin (decode_stage_slot): {bits, gain, first level-table entry,
+      // 0}, then the bin's 64 codes, one byte per channel (planes at or above
+      // the bin's bit width are 0; bins without bits have gain 0).  The
+      // staging lane of a bin turns its bit planes into code bytes (two
+      // 32-channel plane transpositions, for as many planes as the wave's
+      // widest bin has), and lane (t, g) of the W stage reads the 4 code
+      // bytes of its channels 4t..4t+3 for each of its K rows kw.
       //   All rows are staged first.  The next plane's side info is then
       // fetched, and its code words at the end of this W stage: both before
       // this plane's stores.  Vector memory operations complete in issue
       // order, so waiting for those loads never waits for the stores, which
       // drain during the next W stage.
+      {
+        // planes to transpose: the widest bin of the wave, rounded up to 1,
+        // 2, 4 or 8 (narrower bins have zero planes there)
+        int bw = 0;
 #pragma unroll
-      for (int q = 0; q < SLH; ++q) {
-        const int kh = wv + kWaves * q;
-        if (kh >= H) break;
-        uint4* st = reinterpret_cast<uint4*>(plane + static_cast<int64_t>(kh) * RW * 64);
-        // lanes W..NPW-1 read nothing and stage an empty bin
-        if (lane < NPW) {
-          // {bits, gain (0 without bits), first level-table entry, 0}
-          const int b = bj[q];
-          const int sl = stage_slot(lane);
-          st[sl] = uint4{static_cast<uint32_t>(b), b > 0 ? __float_as_uint(gjv[q]) : 0u,
-                               b > 0 ? (1u << b) - 1u : 0u, 0u};
-          st[sl + 1] = uint4{wd[q][0].x, wd[q][1].x, wd[q][2].x, wd[q][3].x};
-          st[sl + 2] = uint4{wd[q][4].x, wd[q][5].x, wd[q][6].x, wd[q][7].x};
-          st[sl + 3] = uint4{wd[q][0].y, wd[q][1].y, wd[q][2].y, wd[q][3].y};
-          st[sl + 4] = uint4{wd[q][4].y, wd[q][5].y, wd[q][6].y, wd[q][7].y};
+        for (int ps = 0; ps < kPass; ++ps) bw = max(bw, bj[ps]);
+        const bool nb8 = __ballot(bw > 4) != 0;
+        const bool nb4 = __ballot(bw > 2) != 0;
+        const bool nb2 = __ballot(bw > 1) != 0;
+#pragma unroll
+        for (int ps = 0; ps < kPass; ++ps) {
+          uint32_t pl[8], ph[8], ql[8], qh[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            pl[k] = wd[ps][k].x;
+            ph[k] = wd[ps][k].y;
+          }
+          if (nb8) {
+            planes_to_codes<8>(pl, ql);
+            planes_to_codes<8>(ph, qh);
+          } else if (nb4) {
+            planes_to_codes<4>(pl, ql);
+            planes_to_codes<4>(ph, qh);
+          } else if (nb2) {
+            planes_to_codes<2>(pl, ql);
+            planes_to_codes<2>(ph, qh);
+          } else {
+            planes_to_codes<1>(pl, ql);
+            planes_to_codes<1>(ph, qh);
+          }
+          const int q = 2 * ps + srow;
+          const int kh = wv + kWaves * q;
+          // K rows W..NPW-1 are staged as empty bins (nothing was read)
+          if (q < SLH && kh < H && skw < NPW) {
+            uint4* st = reinterpret_cast<uint4*>(plane + static_cast<int64_t>(kh) * RW * 64);
+            const int b = bj[ps];
+            const int sl = decode_stage_slot(skw);
+            st[sl] = uint4{static_cast<uint32_t>(b), b > 0 ? __float_as_uint(gjv[ps]) : 0u,
+                           b > 0 ? (1u << b) - 1u : 0u, 0u};
+            st[sl + 1] = uint4{ql[0], ql[1], ql[2], ql[3]};
+            st[sl + 2] = uint4{ql[4], ql[5], ql[6], ql[7]};
+            st[sl + 3] = uint4{qh[0], qh[1], qh[2], qh[3]};
+            st[sl + 4] = uint4{qh[4], qh[5], qh[6], qh[7]};
+          }
         }
       }
       // (the last plane of the walk fetches itself again: same loads, unused)
@@ -1191,8 +1229,6 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
         if (kh >= H) break;
         float* row = plane + static_cast<int64_t>(kh) * RW * 64;
         const uint4* st = reinterpret_cast<const uint4*>(row);
-        const int nib_sh = (4 * t) & 31;
-        const int half = t >= 8 ? 3 : 1;     // the halves holding channels 4t..4t+3
         // B = the levels as (hi, lo) fp16 pairs; the gains go into A
         uint32_t bp[4][FW::KSTEPS][FW::KV];
         float gv[FW::KSTEPS][FW::KV];
@@ -1202,27 +1238,10 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
           for (int v = 0; v < FW::KV; ++v) {
             // (K rows kw >= W are staged as empty bins)
             const int kw = ks * FW::KPER + FW::KV * g + v;
-            const int sl = stage_slot(kw);
+            const int sl = decode_stage_slot(kw);
             const uint4 sb = st[sl];
-            const uint4 w03 = st[sl + half];
-            const uint4 w47 = st[sl + half + 1];
-            uint32_t wk[8] = {w03.x, w03.y, w03.z, w03.w, w47.x, w47.y, w47.z, w47.w};
-            // (all three reads issue here, not one word per plane below)
-            asm("" : "+v"(wk[0]), "+v"(wk[1]), "+v"(wk[2]), "+v"(wk[3]), "+v"(wk[4]), "+v"(wk[5]),
-                "+v"(wk[6]), "+v"(wk[7]));
-            int b = static_cast<int>(sb.x);
-            asm("" : "+v"(b));
-            // byte i of `codes` collects the bits of channel 4t + i (the
-            // spread is kept apart from the shift so that it stays a 24-bit
-            // multiply)
-            uint32_t codes = 0;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              if (__ballot(k < b) == 0) break;
-              uint32_t sp = __builtin_amdgcn_ubfe(wk[k], nib_sh, 4) * 0x204081u;
-              asm("" : "+v"(sp));
-              codes |= (sp & 0x01010101u) << k;
-            }
+            // byte i: the code of channel 4t + i
+            const uint32_t codes = reinterpret_cast<const uint32_t*>(st + sl + 1)[t];
             gv[ks][v] = __uint_as_float(sb.y);
             const int base = static_cast<int>(sb.z);           // s_lp[0] = 0
 #pragma unroll
@@ -2061,12 +2080,12 @@ void launch_plane(const Geometry& g, int64_t n_units, int mode, const float* in,
   const int waves = (mode == MODE_DEQUANT && span > 16 && span <= 24) ? kDecodeWaves : kPlaneWaves;
   const dim3 block(64 * waves);
   const bool h16 = g.H <= 16, w16 = g.W <= 16;
-  // the decode pass pads rows shorter than its staging (80 bytes per bin of
-  // the 16 or 32 K rows, plus 112 bytes after every 8 bins)
+  // the decode pass pads rows shorter than its staging of the 16 or 32 K
+  // rows (decode_stage_bytes)
   int rw = g.W;
   if (mode == MODE_DEQUANT) {
     const int nk = w16 ? 16 : 32;
-    const int need = (nk * 80 + (nk / 8 - 1) * 112 + 255) / 256;
+    const int need = (decode_stage_bytes(nk) + 255) / 256;
     if (rw < need) rw = need;
   }
   const size_t lds = static_cast<size_t>(g.H) * rw * 64 * sizeof(float);
