@@ -314,6 +314,24 @@ def test_decompress_from_oracle_records(geo, rot):
             assert _rel(out[u], exact) <= 1e-5
 
 
+@pytest.mark.parametrize("budget", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("geo", [(3, 20, 24, 2, 128), (2, 24, 12, 1, 64), (2, 28, 30, 1, 64)])
+def test_decode_every_bin_at_one_width(geo, budget):
+    # Uniform allocation gives every bin the same width, so each wave of the
+    # decoder turns bit planes into codes at one width: 1, 2, 4 and 8 planes
+    # (3 and 5 bits leave planes zero), on rows of 32 and 16 bins and with
+    # rows staged in two passes (8 waves of up to 4 rows)
+    g = _geom(*geo, budget, 8, dtype=torch.float32, alloc_mode=tact.ALLOC_UNIFORM)
+    say("decode at one width", geo, budget)
+    op = _oparams(g)
+    x = _units(g, 1, seed=21).float().cpu().numpy().astype(np.float64)
+    rec = O.compress(x[0], op, alloc="uniform", rotation=_orot(g))
+    assert np.all(O.unpack_record(rec, op)[2] == budget)     # every bin at the one width
+    out = tact.decompress(torch.from_numpy(rec[None]).cuda(), g).float().cpu().numpy()[0]
+    exact = O.decompress(rec, op, "f32", rotation=_orot(g))
+    assert _rel(out, exact) <= 1e-5
+
+
 def _check_bf16_decode(out, exact, what):
     """bf16 decoder output (as float) against the exact decoded values
     (fp64): equal to their bf16 rounding except where the exact value lies
