@@ -929,6 +929,9 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t s_wbuf[kWBufWords];
   // where a stage writes its output rows or columns past H or W (dropped)
   __shared__ __attribute__((aligned(16))) float s_sink[4 * kWave];
+  // statistics pass: a wave's row of partial sums (up to 32 bins), gathered
+  // so that the row goes out in one store
+  __shared__ float s_vsum[MODE == MODE_STATS ? kWaves * 32 : 1];
   FragLds<NPW>& s_fw = *reinterpret_cast<FragLds<NPW>*>(s_wbuf);
   float* s_aw = reinterpret_cast<float*>(s_wbuf);
   uint32_t* s_lp = s_wbuf + kAwFloats;
@@ -1052,11 +1055,16 @@ __global__ __launch_bounds__(64 * WV) void k_plane(PlaneArgs a) {
               for (int i = 0; i < 4; ++i) sq = fmaf(acc[i][m][rr], acc[i][m][rr], sq);
               sq = row_sum16(sq);
               const int kw = 16 * m + 4 * g + rr;
-              if (t == 0 && kw < W) vrow[kw] = sq;
+              if (t == 0) s_vsum[wv * 32 + kw] = sq;
               // columns past W take an offset past the buffer (dropped)
               buf_st4<2>(rcoef, kw < W ? vo : kPastBuffer, (16 * m + rr) * cbytes,
                          float4{acc[0][m][rr], acc[1][m][rr], acc[2][m][rr], acc[3][m][rr]});
             }
+          // the row's sums, lane kw (one store instead of one per sum)
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          if (lane < W) vrow[lane] = s_vsum[wv * 32 + lane];
         }
       }
       __syncthreads();                       // LDS free for the next plane
